@@ -1,0 +1,8 @@
+"""fp64 CPU oracle for piecewise block-sparse attention.
+
+Test infrastructure only: imported by the tests, by the smoke check and by the
+CPU-baseline leg of the benchmark, never by the product path.
+"""
+from .pisa_oracle import MODE_APPROX, MODE_DROP, attention, precompute, route
+
+__all__ = ["MODE_APPROX", "MODE_DROP", "attention", "precompute", "route"]

@@ -1,0 +1,199 @@
+"""Plain fp64 CPU oracle for piecewise block-sparse attention (PISA).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check in
+``__graft_entry__.smoke`` and the ``cpu_baseline`` leg of ``bench.py`` may import
+or call anything in this package.  The product path (the HIP library and its
+Python binding) never imports it, and this module imports nothing from the
+product: the two share no code, constants or helpers.
+
+What it computes, and where each step comes from
+-------------------------------------------------
+Sources (cited by page title and section; no line numbers):
+
+* PISA page -- "PISA: Piecewise Sparse Attention Is Wiser for Efficient
+  Diffusion Transformers", technical summary on gist.science (arXiv 2602.01077):
+  section 2 "Methodology", sub-parts "Core algorithm" (the output ratio
+  o_t = N_t / D_t and the numerator N_t), "Covariance-aware routing" (the block
+  score uses the attention score and M_j = ||H_j - Hbar||_2) and "Hardware
+  implementation" (the precompute of centroids, value sums and Hbar).
+* Block-sparse notes -- the block-sparse attention on multimodal DiT notes on
+  dpshk.com: section 3.3 (keep-or-drop block-sparse softmax,
+  O_i = softmax(Q_i K_{S_i}^T / sqrt(d)) V_{S_i}) and section 4.1 (blocks are
+  padded so no block is ragged).
+
+Functions, one per call of the C ABI:
+
+* ``precompute(K, V, B)`` -> block centroids, value sums, per-block H_j, Hbar, M_j
+* ``route(Q, centroid, M, k, lam, B, scale)`` -> per-query-block exact set S_i
+* ``attention(Q, K, V, idx, centroid, vsum, Hbar, mode, scale, B)`` -> O
+
+Readings where the pages are silent or ambiguous (each is also listed with the
+design notes of the repository):
+
+* Softmax scale: the PISA numerator is printed without a scale, the keep-or-drop
+  formula divides by sqrt(d).  Reading: every q_t is pre-multiplied by
+  ``scale`` (1/sqrt(d) by default), in the exact logits, in alpha and in the
+  first-order correction q_t Hbar.
+* Denominator D_t: the page only says it is made of the same three parts.
+  Reading, from the first-order block Taylor expansion
+  exp(q k) ~ exp(q kbar_j) (1 + q (k - kbar_j)): summing the weights over a
+  block gives B * alpha_{t,j} because the deviations k_{j,n} - kbar_j sum to
+  zero, so D_t = sum_{S_i} sum_n exp(q k) + B * sum_{U_i} alpha_{t,j} and the
+  first-order term contributes nothing to D_t.
+* Centroid = arithmetic mean of the block's B keys; value sum = plain sum.
+* H_j = sum_n (k_{j,n} - kbar_j)^T v_{j,n} is d_k x d_v; q Hbar is a row vector.
+* Hbar = mean of H_j over all blocks of the same (batch, head).
+* ||.||_2 of a matrix read as the Frobenius norm (entrywise 2-norm).
+* Routing score: scale * qbar_i . kbar_j + lam * M_j with qbar_i the mean query
+  of block i; the k largest are exact, ties go to the lower block index, and
+  the set is returned in ascending order.  One S_i serves the whole query block.
+* Keep-or-drop with an empty S_i gives o_t = 0.
+
+All arithmetic is float64.  Inputs of any float dtype are upcast exactly.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+MODE_APPROX = 0
+MODE_DROP = 1
+
+
+def _blocks(X: np.ndarray, B: int) -> np.ndarray:
+    """[b,h,L,d] -> [b,h,nb,B,d] in float64; L must be a multiple of B.
+
+    The block-sparse notes (section 4.1) pad each modality to a multiple of the
+    block size before splitting, so blocks are never ragged.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    b, h, L, d = X.shape
+    if L % B != 0:
+        raise ValueError(f"sequence length {L} is not a multiple of block size {B}")
+    return X.reshape(b, h, L // B, B, d)
+
+
+def precompute(K: np.ndarray, V: np.ndarray, B: int) -> dict:
+    """Block statistics of the PISA precompute stage.
+
+    PISA page, section 2, "Core algorithm": the zeroth-order term of block j
+    uses the block centroid kbar_j and the block value sum sum_n v_{j,n}; the
+    first-order term uses H_j = sum_n (k_{j,n} - kbar_j)^T v_{j,n} and the
+    global Hbar, the mean of H_j over all blocks.  "Covariance-aware routing":
+    M_j = ||H_j - Hbar||_2 (Frobenius reading).  "Hardware implementation":
+    these are computed before the attention stages.
+
+    Returns a dict of float64 arrays:
+      centroid [b,h,nb,d], vsum [b,h,nb,d], H [b,h,nb,d,d] (row = key dim,
+      column = value dim), Hbar [b,h,d,d], M [b,h,nb].
+    """
+    Kb = _blocks(K, B)
+    Vb = _blocks(V, B)
+    if Kb.shape != Vb.shape:
+        raise ValueError("K and V must have the same shape")
+    centroid = Kb.mean(axis=3)                      # kbar_j: mean of the block's keys
+    vsum = Vb.sum(axis=3)                           # sum_n v_{j,n}
+    dev = Kb - centroid[:, :, :, None, :]           # k_{j,n} - kbar_j
+    # H_j[a, c] = sum_n dev[n, a] * v[n, c]: a (d x B) @ (B x d) product per block
+    H = np.matmul(np.swapaxes(dev, -1, -2), Vb)
+    Hbar = H.mean(axis=2)                           # mean over the nb blocks of this (b, h)
+    diff = H - Hbar[:, :, None, :, :]
+    M = np.sqrt((diff * diff).sum(axis=(-2, -1)))   # Frobenius norm of H_j - Hbar
+    return {"centroid": centroid, "vsum": vsum, "H": H, "Hbar": Hbar, "M": M}
+
+
+def route(Q: np.ndarray, centroid: np.ndarray, M: np.ndarray, k: int, lam: float,
+          B: int, scale: float) -> np.ndarray:
+    """Covariance-aware top-k block selection (PISA page, section 2,
+    "Covariance-aware routing").
+
+    score_ij = scale * qbar_i . kbar_j + lam * M_j, where qbar_i is the mean of
+    the B queries of block i.  S_i = the k highest scores, ties broken towards
+    the lower block index; returned ascending as int32 [b,h,nqb,k].
+    """
+    Qb = _blocks(Q, B)
+    centroid = np.asarray(centroid, dtype=np.float64)
+    M = np.asarray(M, dtype=np.float64)
+    b, h, nqb, _, d = Qb.shape
+    nb = centroid.shape[2]
+    if not (1 <= k <= nb):
+        raise ValueError(f"k={k} must lie in [1, {nb}]")
+    qbar = Qb.mean(axis=3)                                          # [b,h,nqb,d]
+    idx = np.empty((b, h, nqb, k), dtype=np.int32)
+    order_key = np.arange(nb)
+    for bi in range(b):
+        for hi in range(h):
+            scores = scale * (qbar[bi, hi] @ centroid[bi, hi].T) + lam * M[bi, hi][None, :]
+            for i in range(nqb):
+                # sort by score descending, then block index ascending
+                order = np.lexsort((order_key, -scores[i]))
+                idx[bi, hi, i] = np.sort(order[:k])
+    return idx
+
+
+def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
+              centroid: np.ndarray, vsum: np.ndarray, Hbar: np.ndarray,
+              mode: int, scale: float, B: int, qblocks=None) -> np.ndarray:
+    """PISA exact-or-approximate attention, or keep-or-drop block-sparse attention.
+
+    PISA page, section 2, "Core algorithm": o_t = N_t / D_t with
+      N_t = sum_{j in S_i} sum_n e^{q k_{j,n}} v_{j,n}
+            + sum_{j in U_i} alpha_{t,j} sum_n v_{j,n}
+            + q_t Hbar sum_{j in U_i} alpha_{t,j},      alpha_{t,j} = e^{q kbar_j}
+    and (reading) D_t = sum_{S_i} sum_n e^{q k} + B sum_{U_i} alpha_{t,j}, where
+    q = scale * q_t.  U_i is every block not in S_i.
+
+    Block-sparse notes, section 3.3 (mode == MODE_DROP): only the S_i terms
+    remain, i.e. softmax over the selected blocks' keys; an empty S_i gives 0.
+
+    idx: int [b,h,nqb,kmax]; entries are block ids, -1 entries are padding.
+    qblocks: optional iterable of (b, h, i) triples; only those query blocks are
+      computed and every other output row is NaN.
+    Returns float64 [b,h,L,d].
+    """
+    Qb = _blocks(Q, B)
+    Kb = _blocks(K, B)
+    Vb = _blocks(V, B)
+    centroid = np.asarray(centroid, dtype=np.float64)
+    vsum = np.asarray(vsum, dtype=np.float64)
+    Hbar = np.asarray(Hbar, dtype=np.float64)
+    idx = np.asarray(idx)
+    if mode not in (MODE_APPROX, MODE_DROP):
+        raise ValueError(f"unknown mode {mode}")
+    b, h, nqb, _, d = Qb.shape
+    nb = Kb.shape[2]
+    dv = Vb.shape[-1]
+    out = np.full((b, h, nqb, B, dv), np.nan)
+    if qblocks is None:
+        qblocks = [(bi, hi, i) for bi in range(b) for hi in range(h) for i in range(nqb)]
+    for bi, hi, i in qblocks:
+        row = [int(j) for j in idx[bi, hi, i] if j >= 0]
+        if len(set(row)) != len(row) or any(j >= nb for j in row):
+            raise ValueError(f"idx row ({bi},{hi},{i}) has duplicates or out-of-range ids")
+        S = sorted(row)
+        chosen = set(S)
+        U = [j for j in range(nb) if j not in chosen]
+        q = scale * Qb[bi, hi, i]                                    # [B, d]
+        # exact logits over the selected blocks' keys
+        KS = Kb[bi, hi, S].reshape(-1, d)                            # [|S|*B, d]
+        VS = Vb[bi, hi, S].reshape(-1, dv)
+        ell = q @ KS.T                                               # [B, |S|*B]
+        if mode == MODE_DROP:
+            if len(S) == 0:
+                out[bi, hi, i] = 0.0
+                continue
+            m = ell.max(axis=1, keepdims=True)
+            w = np.exp(ell - m)
+            out[bi, hi, i] = (w @ VS) / w.sum(axis=1, keepdims=True)
+            continue
+        # zeroth-order block terms over U_i: alpha_{t,j} = e^{q . kbar_j}
+        c = q @ centroid[bi, hi, U].T                                # [B, |U|]
+        parts = [x for x in (ell, c) if x.size]
+        m = np.max(np.concatenate(parts, axis=1), axis=1, keepdims=True)
+        w = np.exp(ell - m)                                          # exact weights
+        a = np.exp(c - m)                                            # alpha, shifted by m
+        asum = a.sum(axis=1, keepdims=True)                          # sum_{U} alpha
+        N = w @ VS + a @ vsum[bi, hi, U] + (q @ Hbar[bi, hi]) * asum
+        D = w.sum(axis=1, keepdims=True) + B * asum
+        out[bi, hi, i] = N / D
+    return out.reshape(b, h, nqb * B, dv)
