@@ -1,0 +1,177 @@
+/*
+ * pisa.h -- C ABI of libpisa: piecewise block-sparse ("exact-or-approximate")
+ * attention for diffusion-transformer self-attention on AMD Instinct MI355X
+ * (gfx950), with keep-or-drop block-sparse attention as a mode flag.
+ *
+ * Method: "PISA: Piecewise Sparse Attention Is Wiser for Efficient Diffusion
+ * Transformers" (technical summary, gist.science), section 2 "Methodology":
+ * the KV blocks of query block i are split into an exact set S_i and the rest
+ * U_i; the output is o_t = N_t / D_t where the exact blocks contribute
+ * e^{q k} terms, every block of U_i contributes a zeroth-order block Taylor
+ * term alpha_{t,j} * sum_n v_{j,n} with alpha_{t,j} = e^{q kbar_j}, and one
+ * global first-order correction q_t Hbar sum_{j in U_i} alpha_{t,j} is added.
+ * Keep-or-drop: block-sparse attention notes (dpshk.com), section 3.3,
+ * O_i = softmax(Q_i K_{S_i}^T / sqrt(d)) V_{S_i}.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Tensors are dense, row-major and contiguous: Q, K, V, O are [b, h, L, d].
+ *   Q, K, V and O share one element type (pisa_shape.dtype).  Statistics are
+ *   always float32.
+ * - Sequences are split into blocks of `block` consecutive tokens; query blocks
+ *   and KV blocks have the same size.  L must be a multiple of `block` (pad on
+ *   the caller's side, per modality, as the block-sparse notes do in section
+ *   4.1); the library rejects ragged blocks rather than bias centroids with pad
+ *   tokens.  nb = L / block.
+ * - Supported: head_dim in {64, 128}; block in {64, 128}; nb <= 2048;
+ *   batch*heads*nb < 2^31.
+ * - Every pointer argument except `stream` is a DEVICE pointer owned by the
+ *   caller; the library never allocates, frees or retains device memory and
+ *   keeps no global mutable state.  `stream` is a hipStream_t (NULL = the
+ *   legacy default stream).  Calls are asynchronous on that stream: results are
+ *   valid once the stream reaches them.
+ * - Every call validates its arguments on the host first and returns an error
+ *   code without launching anything when they are wrong.  A failed launch
+ *   returns PISA_ERR_HIP; pisa_last_error() then names the HIP error.  No C++
+ *   exception crosses the ABI.
+ */
+#ifndef PISA_H_
+#define PISA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PISA_VERSION 100 /* major * 100 + minor */
+
+typedef enum {
+  PISA_OK = 0,
+  PISA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PISA_ERR_SHAPE = 2,       /* L % block != 0, unsupported head_dim/block, sizes <= 0 or too large */
+  PISA_ERR_ARG = 3,         /* k or kmax out of range, unknown mode, non-finite scale/lambda */
+  PISA_ERR_DTYPE = 4,       /* unknown element type */
+  PISA_ERR_WORKSPACE = 5,   /* workspace smaller than pisa_workspace_size() */
+  PISA_ERR_HIP = 6          /* a HIP launch or runtime call failed */
+} pisa_status;
+
+typedef enum {
+  PISA_DTYPE_BF16 = 0,      /* bfloat16 storage, float32 accumulation, bf16 MFMA */
+  PISA_DTYPE_FP32 = 1       /* float32 storage and arithmetic throughout */
+} pisa_dtype;
+
+typedef enum {
+  PISA_MODE_APPROX = 0,     /* PISA: exact S_i + zeroth-order U_i + global first-order correction */
+  PISA_MODE_DROP = 1        /* keep-or-drop block-sparse attention over S_i only */
+} pisa_mode;
+
+typedef struct {
+  int32_t batch;            /* b */
+  int32_t heads;            /* h */
+  int32_t seq_len;          /* L, multiple of block */
+  int32_t head_dim;         /* d: 64 or 128 (keys and values share it) */
+  int32_t block;            /* B: 64 or 128 */
+  int32_t dtype;            /* pisa_dtype of Q, K, V, O */
+} pisa_shape;
+
+/* Block statistics, all float32 device arrays owned by the caller. */
+typedef struct {
+  float* centroid;          /* [b,h,nb,d]   kbar_j = mean of block j's keys                  */
+  float* vsum;              /* [b,h,nb,d]   sigma_j = sum of block j's values                */
+  float* H;                 /* [b,h,nb,d,d] H_j = sum_n (k_{j,n} - kbar_j)^T v_{j,n}, row =
+                                            key dim, column = value dim.  NULLABLE: written
+                                            only when non-NULL                               */
+  float* Hbar;              /* [b,h,d,d]    mean of H_j over the nb blocks of (b,h)          */
+  float* M;                 /* [b,h,nb]     M_j = ||H_j - Hbar||_F                           */
+} pisa_stats;
+
+/* Version of the library (PISA_VERSION at build time). */
+int32_t pisa_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* pisa_status_string(int32_t status);
+
+/* Text of the most recent PISA_ERR_* raised on the calling thread (validation
+ * message or HIP error string); "" if none.  Thread-local, never NULL. */
+const char* pisa_last_error(void);
+
+/* Bytes of device workspace pisa_precompute needs for this shape (0 if the
+ * shape is invalid).  The workspace holds deterministic partial sums of H_j. */
+size_t pisa_workspace_size(const pisa_shape* shape);
+
+/*
+ * pisa_precompute -- block statistics (PISA summary, section 2: "Core
+ * algorithm" defines kbar_j, the value sums, H_j and Hbar; "Covariance-aware
+ * routing" defines M_j = ||H_j - Hbar||_2, read here as the Frobenius norm;
+ * "Hardware implementation" places this computation before the attention).
+ *
+ *   K, V       [b,h,L,d] of shape->dtype (device, read only)
+ *   out        centroid, vsum, Hbar, M required; H optional (see pisa_stats)
+ *   workspace  device scratch of at least pisa_workspace_size(shape) bytes,
+ *              caller-owned; contents on entry are ignored
+ *
+ * Two streaming passes over K and V (M_j needs the global Hbar); Hbar is
+ * reduced in a fixed order, so results are bitwise reproducible.
+ */
+pisa_status pisa_precompute(const pisa_shape* shape, const void* K, const void* V,
+                            const pisa_stats* out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * pisa_route -- covariance-aware top-k routing (PISA summary, section 2,
+ * "Covariance-aware routing": the block score combines the attention score
+ * with M_j).  Score of query block i and KV block j, computed in float64:
+ *
+ *     score_ij = scale * qbar_i . kbar_j + lambda * M_j,
+ *     qbar_i   = mean of the `block` queries of block i.
+ *
+ * S_i = the k highest scores; ties go to the lower j.
+ *
+ *   Q         [b,h,L,d] of shape->dtype (device)
+ *   centroid  [b,h,nb,d] float32, M [b,h,nb] float32 (from pisa_precompute)
+ *   k         1 <= k <= nb
+ *   scale     softmax scale (1/sqrt(d) for standard attention), finite
+ *   lambda    weight of M_j, finite
+ *   idx       out: int32 [b,h,nb,k], each row strictly ascending
+ */
+pisa_status pisa_route(const pisa_shape* shape, const void* Q, const float* centroid,
+                       const float* M, int32_t k, double scale, double lambda, int32_t* idx,
+                       void* stream);
+
+/*
+ * pisa_attention -- one fused kernel per query block (PISA summary, section 2,
+ * "Hardware implementation": stage 1 exact attention over the selected blocks,
+ * stage 2 zeroth-order sweep over the other blocks' centroids and value sums,
+ * stage 3 the global first-order correction, all inside one online softmax).
+ *
+ *   Q, K, V   [b,h,L,d] of shape->dtype (device)
+ *   idx       int32 [b,h,nb,kmax]: block ids of S_i; entries < 0 are padding
+ *             and are skipped wherever they appear.  Ids must be distinct and
+ *             < nb (ids >= nb are skipped, duplicates are counted twice; no
+ *             fault either way).  Rows may be fully padded (S_i empty).
+ *   kmax      row length of idx, 1 <= kmax <= nb
+ *   stats     centroid, vsum, Hbar read in APPROX mode (may be NULL in DROP
+ *             mode); H and M are not read
+ *   mode      pisa_mode
+ *   scale     softmax scale applied to every q_t (exact logits, alpha and the
+ *             correction), finite
+ *   O         out: [b,h,L,d] of shape->dtype (device)
+ *
+ * APPROX: o_t = N_t / D_t with, for q = scale * q_t,
+ *   N_t = sum_{S_i,n} e^{q k} v + sum_{U_i} e^{q kbar_j} sigma_j + (q Hbar) sum_{U_i} e^{q kbar_j}
+ *   D_t = sum_{S_i,n} e^{q k}   + block * sum_{U_i} e^{q kbar_j}
+ * (the first-order term adds nothing to D_t: block deviations sum to zero).
+ * DROP: softmax over the keys of S_i only; o_t = 0 when S_i is empty.
+ */
+pisa_status pisa_attention(const pisa_shape* shape, const void* Q, const void* K,
+                           const void* V, const int32_t* idx, int32_t kmax,
+                           const pisa_stats* stats, int32_t mode, float scale, void* O,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PISA_H_ */

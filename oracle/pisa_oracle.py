@@ -25,6 +25,7 @@ Functions, one per call of the C ABI:
 
 * ``precompute(K, V, B)`` -> block centroids, value sums, per-block H_j, Hbar, M_j
 * ``route(Q, centroid, M, k, lam, B, scale)`` -> per-query-block exact set S_i
+  (``route_scores`` exposes the float64 scores it ranks)
 * ``attention(Q, K, V, idx, centroid, vsum, Hbar, mode, scale, B)`` -> O
 
 Readings where the pages are silent or ambiguous (each is also listed with the
@@ -102,31 +103,37 @@ def precompute(K: np.ndarray, V: np.ndarray, B: int) -> dict:
     return {"centroid": centroid, "vsum": vsum, "H": H, "Hbar": Hbar, "M": M}
 
 
+def route_scores(Q: np.ndarray, centroid: np.ndarray, M: np.ndarray, lam: float,
+                 B: int, scale: float) -> np.ndarray:
+    """Routing scores (PISA page, section 2, "Covariance-aware routing"):
+    score_ij = scale * qbar_i . kbar_j + lam * M_j, with qbar_i the mean of the
+    B queries of block i.  Returns float64 [b,h,nqb,nb]."""
+    Qb = _blocks(Q, B)
+    centroid = np.asarray(centroid, dtype=np.float64)
+    M = np.asarray(M, dtype=np.float64)
+    qbar = Qb.mean(axis=3)                                          # [b,h,nqb,d]
+    return scale * np.matmul(qbar, np.swapaxes(centroid, -1, -2)) + lam * M[:, :, None, :]
+
+
 def route(Q: np.ndarray, centroid: np.ndarray, M: np.ndarray, k: int, lam: float,
           B: int, scale: float) -> np.ndarray:
     """Covariance-aware top-k block selection (PISA page, section 2,
     "Covariance-aware routing").
 
-    score_ij = scale * qbar_i . kbar_j + lam * M_j, where qbar_i is the mean of
-    the B queries of block i.  S_i = the k highest scores, ties broken towards
+    S_i = the k highest ``route_scores`` of query block i, ties broken towards
     the lower block index; returned ascending as int32 [b,h,nqb,k].
     """
-    Qb = _blocks(Q, B)
-    centroid = np.asarray(centroid, dtype=np.float64)
-    M = np.asarray(M, dtype=np.float64)
-    b, h, nqb, _, d = Qb.shape
-    nb = centroid.shape[2]
+    scores = route_scores(Q, centroid, M, lam, B, scale)
+    b, h, nqb, nb = scores.shape
     if not (1 <= k <= nb):
         raise ValueError(f"k={k} must lie in [1, {nb}]")
-    qbar = Qb.mean(axis=3)                                          # [b,h,nqb,d]
     idx = np.empty((b, h, nqb, k), dtype=np.int32)
     order_key = np.arange(nb)
     for bi in range(b):
         for hi in range(h):
-            scores = scale * (qbar[bi, hi] @ centroid[bi, hi].T) + lam * M[bi, hi][None, :]
             for i in range(nqb):
                 # sort by score descending, then block index ascending
-                order = np.lexsort((order_key, -scores[i]))
+                order = np.lexsort((order_key, -scores[bi, hi, i]))
                 idx[bi, hi, i] = np.sort(order[:k])
     return idx
 

@@ -1,0 +1,153 @@
+"""Piecewise block-sparse (PISA) attention for MI355X: Python binding of libpisa.
+
+Thin marshalling layer over the C ABI in include/pisa.h.  Torch supplies the
+device memory and the current HIP stream; every step of the computation runs
+in libpisa's gfx950 kernels.  If libpisa.so is missing the calls raise.
+
+    stats = precompute(K, V, block)                       # centroids, value sums, Hbar, M
+    idx = route(Q, stats, k, lam, block)                  # [b,h,nb,k] int32, ascending
+    O = attention(Q, K, V, idx, stats, block, mode="approx")
+
+Q, K, V: contiguous [b, h, L, d] CUDA tensors, bfloat16 or float32, L a
+multiple of `block`.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+from . import _lib
+
+__all__ = ["precompute", "route", "attention", "workspace_size", "version", "MODE_APPROX",
+           "MODE_DROP"]
+
+MODE_APPROX = _lib.MODE_APPROX
+MODE_DROP = _lib.MODE_DROP
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _shape(X, block: int) -> _lib.PisaShape:
+    torch = _torch()
+    if X.dim() != 4:
+        raise ValueError("expected a [b, h, L, d] tensor")
+    if X.dtype == torch.bfloat16:
+        dt = _lib.DTYPE_BF16
+    elif X.dtype == torch.float32:
+        dt = _lib.DTYPE_FP32
+    else:
+        raise TypeError(f"unsupported dtype {X.dtype}")
+    b, h, L, d = X.shape
+    return _lib.PisaShape(b, h, L, d, block, dt)
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("tensors must be contiguous device tensors")
+    return t.data_ptr()
+
+
+def _stream(t) -> int:
+    return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+def _expect(t, shape, dtype, name):
+    if t is None or tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        got = None if t is None else (tuple(t.shape), t.dtype)
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, got {got}")
+
+
+def _same(ref, *others):
+    for o in others:
+        if o.shape != ref.shape or o.dtype != ref.dtype or o.device != ref.device:
+            raise ValueError("Q, K, V (and O) must share shape, dtype and device")
+
+
+def version() -> int:
+    return _lib.load().pisa_version()
+
+
+def workspace_size(X, block: int) -> int:
+    return _lib.load().pisa_workspace_size(ctypes.byref(_shape(X, block)))
+
+
+def precompute(K, V, block: int, store_H: bool = False, workspace=None) -> dict:
+    """Block statistics (fp32): centroid, vsum, Hbar, M, and H when store_H."""
+    torch = _torch()
+    lib = _lib.load()
+    _same(K, V)
+    shp = _shape(K, block)
+    b, h, L, d = K.shape
+    nb = L // block if L % block == 0 else 0
+    f32 = dict(dtype=torch.float32, device=K.device)
+    out = {
+        "centroid": torch.empty((b, h, nb, d), **f32),
+        "vsum": torch.empty((b, h, nb, d), **f32),
+        "H": torch.empty((b, h, nb, d, d), **f32) if store_H else None,
+        "Hbar": torch.empty((b, h, d, d), **f32),
+        "M": torch.empty((b, h, nb), **f32),
+    }
+    need = lib.pisa_workspace_size(ctypes.byref(shp))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=K.device)
+    st = _lib.PisaStats(*(_ptr(out[n]) for n in ("centroid", "vsum", "H", "Hbar", "M")))
+    _lib.check("pisa_precompute", lib.pisa_precompute(
+        ctypes.byref(shp), _ptr(K), _ptr(V), ctypes.byref(st), _ptr(workspace),
+        workspace.numel(), _stream(K)))
+    return out
+
+
+def route(Q, stats: dict, k: int, lam: float, block: int, scale: float | None = None):
+    """Top-k exact blocks per query block, int32 [b, h, nb, k], rows ascending."""
+    torch = _torch()
+    lib = _lib.load()
+    shp = _shape(Q, block)
+    b, h, L, d = Q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    idx = torch.empty((b, h, max(L // block, 0), max(k, 0)), dtype=torch.int32, device=Q.device)
+    nb = L // block if L % block == 0 else 0
+    _expect(stats["centroid"], (b, h, nb, d), torch.float32, "stats['centroid']")
+    _expect(stats["M"], (b, h, nb), torch.float32, "stats['M']")
+    _lib.check("pisa_route", lib.pisa_route(
+        ctypes.byref(shp), _ptr(Q), _ptr(stats["centroid"]), _ptr(stats["M"]), int(k), scale,
+        float(lam), _ptr(idx), _stream(Q)))
+    return idx
+
+
+def attention(Q, K, V, idx, stats: dict | None, block: int, mode: int | str = "approx",
+              scale: float | None = None, out=None):
+    """PISA (mode "approx") or keep-or-drop (mode "drop") block-sparse attention."""
+    torch = _torch()
+    lib = _lib.load()
+    _same(Q, K, V)
+    if isinstance(mode, str):
+        mode = {"approx": MODE_APPROX, "drop": MODE_DROP}[mode]
+    shp = _shape(Q, block)
+    d = Q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    b, h, L, _ = Q.shape
+    nb = L // block if L % block == 0 else 0
+    if idx.dim() != 4:
+        raise ValueError("idx must be an int32 [b, h, nb, kmax] tensor")
+    _expect(idx, (b, h, nb, idx.shape[-1]), torch.int32, "idx")
+    O = torch.empty_like(Q) if out is None else out
+    _same(Q, O)
+    st = None
+    if mode == MODE_APPROX:
+        if stats is None:
+            raise ValueError("approx mode needs the block statistics")
+        _expect(stats["centroid"], (b, h, nb, d), torch.float32, "stats['centroid']")
+        _expect(stats["vsum"], (b, h, nb, d), torch.float32, "stats['vsum']")
+        _expect(stats["Hbar"], (b, h, d, d), torch.float32, "stats['Hbar']")
+    if stats is not None:
+        st = _lib.PisaStats(_ptr(stats["centroid"]), _ptr(stats["vsum"]), None,
+                            _ptr(stats["Hbar"]), None)
+    _lib.check("pisa_attention", lib.pisa_attention(
+        ctypes.byref(shp), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), int(idx.shape[-1]),
+        ctypes.byref(st) if st is not None else None, int(mode), scale, _ptr(O), _stream(Q)))
+    return O

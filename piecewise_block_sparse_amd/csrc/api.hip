@@ -1,0 +1,147 @@
+// C ABI of libpisa: argument validation on the host, then kernel launches on
+// the caller's stream.  Declared in include/pisa.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+#include "pisa.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+pisa_status fail(pisa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pisa_status fail(pisa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+pisa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PISA_OK;
+  return fail(PISA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shape rules shared by every call.  Returns PISA_OK and fills bh / nb.
+pisa_status check_shape(const pisa_shape* s, int* bh, int* nb) {
+  if (!s) return fail(PISA_ERR_NULL, "shape is NULL");
+  if (s->dtype != PISA_DTYPE_BF16 && s->dtype != PISA_DTYPE_FP32)
+    return fail(PISA_ERR_DTYPE, "unknown dtype %d", s->dtype);
+  if (s->batch <= 0 || s->heads <= 0 || s->seq_len <= 0)
+    return fail(PISA_ERR_SHAPE, "batch, heads and seq_len must be positive");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(PISA_ERR_SHAPE, "head_dim %d not in {64, 128}", s->head_dim);
+  if (s->block != 64 && s->block != 128)
+    return fail(PISA_ERR_SHAPE, "block %d not in {64, 128}", s->block);
+  if (s->seq_len % s->block != 0)
+    return fail(PISA_ERR_SHAPE, "seq_len %d is not a multiple of block %d (pad per modality)",
+                s->seq_len, s->block);
+  const long long n = (long long)s->seq_len / s->block;
+  if (n > pisa::kMaxBlocks)
+    return fail(PISA_ERR_SHAPE, "seq_len / block = %lld exceeds %d blocks", n, pisa::kMaxBlocks);
+  const long long b = (long long)s->batch * s->heads;
+  if (b * n >= (1LL << 31))
+    return fail(PISA_ERR_SHAPE, "batch * heads * blocks must stay below 2^31");
+  *bh = (int)b;
+  *nb = (int)n;
+  return PISA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pisa_version(void) { return PISA_VERSION; }
+
+const char* pisa_status_string(int32_t status) {
+  switch (status) {
+    case PISA_OK: return "ok";
+    case PISA_ERR_NULL: return "null pointer argument";
+    case PISA_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case PISA_ERR_ARG: return "invalid argument";
+    case PISA_ERR_DTYPE: return "unknown element type";
+    case PISA_ERR_WORKSPACE: return "workspace too small";
+    case PISA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* pisa_last_error(void) { return g_err; }
+
+size_t pisa_workspace_size(const pisa_shape* shape) {
+  int bh = 0, nb = 0;
+  if (check_shape(shape, &bh, &nb) != PISA_OK) return 0;
+  return shape->dtype == PISA_DTYPE_BF16 ? pisa::stats_workspace_bf16(bh, nb, shape->head_dim)
+                                         : pisa::stats_workspace_f32(bh, nb, shape->head_dim);
+}
+
+pisa_status pisa_precompute(const pisa_shape* shape, const void* K, const void* V,
+                            const pisa_stats* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  g_err[0] = 0;
+  int bh = 0, nb = 0;
+  pisa_status st = check_shape(shape, &bh, &nb);
+  if (st != PISA_OK) return st;
+  if (!K || !V || !out) return fail(PISA_ERR_NULL, "K, V and out are required");
+  if (!out->centroid || !out->vsum || !out->Hbar || !out->M)
+    return fail(PISA_ERR_NULL, "centroid, vsum, Hbar and M outputs are required");
+  const bool bf = shape->dtype == PISA_DTYPE_BF16;
+  const bool needs_ws = bf || out->H == nullptr;
+  if (needs_ws) {
+    const size_t need = pisa_workspace_size(shape);
+    if (!workspace) return fail(PISA_ERR_NULL, "workspace of %zu bytes is required", need);
+    if (workspace_bytes < need)
+      return fail(PISA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  }
+  pisa::StatsArgs a{K, V, out->centroid, out->vsum, out->H, out->Hbar, out->M, workspace,
+                    bh, nb, shape->head_dim, shape->block, (hipStream_t)stream};
+  return hip_status(bf ? pisa::launch_stats_bf16(a) : pisa::launch_stats_f32(a), "pisa_precompute");
+}
+
+pisa_status pisa_route(const pisa_shape* shape, const void* Q, const float* centroid,
+                       const float* M, int32_t k, double scale, double lambda, int32_t* idx,
+                       void* stream) {
+  g_err[0] = 0;
+  int bh = 0, nb = 0;
+  pisa_status st = check_shape(shape, &bh, &nb);
+  if (st != PISA_OK) return st;
+  if (!Q || !centroid || !M || !idx) return fail(PISA_ERR_NULL, "Q, centroid, M and idx are required");
+  if (k < 1 || k > nb) return fail(PISA_ERR_ARG, "k=%d outside [1, %d]", k, nb);
+  if (!std::isfinite(scale) || !std::isfinite(lambda))
+    return fail(PISA_ERR_ARG, "scale and lambda must be finite");
+  pisa::RouteArgs a{Q, centroid, M, k, scale, lambda, idx, bh, nb, shape->head_dim, shape->block,
+                    (hipStream_t)stream};
+  const bool bf = shape->dtype == PISA_DTYPE_BF16;
+  return hip_status(bf ? pisa::launch_route_bf16(a) : pisa::launch_route_f32(a), "pisa_route");
+}
+
+pisa_status pisa_attention(const pisa_shape* shape, const void* Q, const void* K,
+                           const void* V, const int32_t* idx, int32_t kmax,
+                           const pisa_stats* stats, int32_t mode, float scale, void* O,
+                           void* stream) {
+  g_err[0] = 0;
+  int bh = 0, nb = 0;
+  pisa_status st = check_shape(shape, &bh, &nb);
+  if (st != PISA_OK) return st;
+  if (!Q || !K || !V || !idx || !O) return fail(PISA_ERR_NULL, "Q, K, V, idx and O are required");
+  if (mode != PISA_MODE_APPROX && mode != PISA_MODE_DROP)
+    return fail(PISA_ERR_ARG, "unknown mode %d", mode);
+  if (kmax < 1 || kmax > nb) return fail(PISA_ERR_ARG, "kmax=%d outside [1, %d]", kmax, nb);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(PISA_ERR_ARG, "scale must be finite and positive");
+  const bool approx = mode == PISA_MODE_APPROX;
+  if (approx && (!stats || !stats->centroid || !stats->vsum || !stats->Hbar))
+    return fail(PISA_ERR_NULL, "APPROX mode needs stats centroid, vsum and Hbar");
+  pisa::AttnArgs a{Q, K, V, idx, kmax,
+                   approx ? stats->centroid : nullptr, approx ? stats->vsum : nullptr,
+                   approx ? stats->Hbar : nullptr, approx ? 1 : 0, scale, O, bh, nb,
+                   shape->head_dim, shape->block, (hipStream_t)stream};
+  const bool bf = shape->dtype == PISA_DTYPE_BF16;
+  return hip_status(bf ? pisa::launch_attn_bf16(a) : pisa::launch_attn_f32(a), "pisa_attention");
+}
+
+}  // extern "C"

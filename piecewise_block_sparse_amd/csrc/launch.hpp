@@ -1,0 +1,76 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pisa {
+
+struct AttnArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const int32_t* idx;
+  int kmax;
+  const float* centroid;
+  const float* vsum;
+  const float* hbar;
+  int approx;
+  float scale;
+  void* O;
+  int bh;   // batch * heads
+  int nb;   // blocks per sequence
+  int D;
+  int BLK;
+  hipStream_t stream;
+};
+
+struct StatsArgs {
+  const void* K;
+  const void* V;
+  float* centroid;
+  float* vsum;
+  float* H;      // nullable
+  float* hbar;
+  float* M;
+  void* ws;
+  int bh;
+  int nb;
+  int D;
+  int BLK;
+  hipStream_t stream;
+};
+
+struct RouteArgs {
+  const void* Q;
+  const float* centroid;
+  const float* M;
+  int k;
+  double scale;
+  double lam;
+  int32_t* idx;
+  int bh;
+  int nb;
+  int D;
+  int BLK;
+  hipStream_t stream;
+};
+
+// largest nb (= L / block) the kernels accept
+constexpr int kMaxBlocks = 2048;
+
+// blocks of one head handled by one statistics workgroup (bf16 path)
+constexpr int kStatsGroup = 8;
+
+size_t stats_workspace_bf16(int bh, int nb, int D);
+size_t stats_workspace_f32(int bh, int nb, int D);
+
+hipError_t launch_attn_bf16(const AttnArgs& a);
+hipError_t launch_attn_f32(const AttnArgs& a);
+hipError_t launch_stats_bf16(const StatsArgs& a);
+hipError_t launch_stats_f32(const StatsArgs& a);
+hipError_t launch_route_bf16(const RouteArgs& a);
+hipError_t launch_route_f32(const RouteArgs& a);
+
+}  // namespace pisa

@@ -1,0 +1,346 @@
+// Block statistics for PISA: centroids, value sums, H_j, Hbar and M_j.
+//
+// PISA summary (gist.science), section 2: "Core algorithm" (centroid kbar_j,
+// value sum, H_j = sum_n (k_{j,n} - kbar_j)^T v_{j,n}, Hbar = mean of H_j),
+// "Covariance-aware routing" (M_j = ||H_j - Hbar||_2, Frobenius reading) and
+// "Hardware implementation" (computed before the attention stages).
+//
+// bf16 path: H_j = K_j^T V_j - kbar_j^T sigma_j, with K_j^T V_j on bf16 MFMA
+// (products of bf16 values are exact in the fp32 accumulator).  Pass 1 streams
+// K and V once and writes one fp32 partial sum of H_j per group of
+// kStatsGroup blocks; a fixed-order fp64 reduction gives Hbar; pass 2 streams K
+// and V again, recomputes each H_j and writes M_j (and H_j when asked).  No
+// atomics: results are bitwise reproducible.
+//
+// fp32 path: plain fp32 VALU arithmetic with centred keys; H_j is kept in a
+// buffer, reduced to Hbar, then M_j is read off the buffer.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace pisa {
+namespace {
+
+template <int D, int BLK>
+struct SCfg {
+  static constexpr int NT = 256;
+  static constexpr int ROW = BLK + 8;                 // LDS row (tokens) of K^T / V^T, padded
+  static constexpr int SUB = (BLK / 8) * (D / 8);     // 8x8 sub-tiles per tensor
+  static constexpr int PER_T = (2 * SUB + NT - 1) / NT;
+  static constexpr int TM = (D == 128) ? 2 : 1;       // 32x32 output tiles per wave, per dim
+  static_assert(2 * D <= NT, "column sums use one thread per column");
+};
+
+template <int D, int BLK, bool PASS2>
+__global__ __launch_bounds__(256) void stats_bf16_kernel(
+    const bf16* __restrict__ K, const bf16* __restrict__ V, int nb, float* __restrict__ centroid,
+    float* __restrict__ vsum, float* __restrict__ partial, const float* __restrict__ hbar,
+    float* __restrict__ M, float* __restrict__ Hout) {
+  using C = SCfg<D, BLK>;
+  __shared__ __attribute__((aligned(16))) bf16 Kt[D * C::ROW];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[D * C::ROW];
+  __shared__ float s_k[D];
+  __shared__ float s_v[D];
+  __shared__ float s_red[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int q32 = lane & 31, hh = lane >> 5;
+  const int ngrp = (nb + kStatsGroup - 1) / kStatsGroup;
+  const int bh = blockIdx.x / ngrp, grp = blockIdx.x - bh * ngrp;
+  const int j0 = grp * kStatsGroup;
+  const int j1 = min(nb, j0 + kStatsGroup);
+  const size_t L = (size_t)nb * BLK;
+  const bf16* Kh = K + (size_t)bh * L * D;
+  const bf16* Vh = V + (size_t)bh * L * D;
+  const int mt0 = (w >> 1) * C::TM, nt0 = (w & 1) * C::TM;
+
+  f32x16 acc[C::TM][C::TM];
+#pragma unroll
+  for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+    for (int b = 0; b < C::TM; ++b) acc[a][b] = f32x16{};
+
+  float hb[C::TM][C::TM][16];
+  if (PASS2) {
+    const float* hbh = hbar + (size_t)bh * D * D;
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+      for (int b = 0; b < C::TM; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          hb[a][b][r] = hbh[(32 * (mt0 + a) + 8 * (r / 4) + 4 * hh + (r % 4)) * D + 32 * (nt0 + b) + q32];
+  }
+
+  u32x4 regs[C::PER_T][8];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int u = 0; u < C::PER_T; ++u) {
+      const int p = tid + u * C::NT;
+      if (p < 2 * C::SUB) {
+        const bf16* X = ((p < C::SUB) ? Kh : Vh) + (size_t)j * BLK * D;
+        const int q = p % C::SUB;
+        const int g = q % (BLK / 8), c = q / (BLK / 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) regs[u][e] = ld16(X + (8 * g + e) * D + 8 * c);
+      }
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int u = 0; u < C::PER_T; ++u) {
+      const int p = tid + u * C::NT;
+      if (p < 2 * C::SUB) {
+        bf16* Xt = (p < C::SUB) ? Kt : Vt;
+        const int q = p % C::SUB;
+        const int g = q % (BLK / 8), c = q / (BLK / 8);
+        u32x4 col[8];
+        transpose8x8(regs[u], col);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st16(Xt + (8 * c + i) * C::ROW + 8 * g, col[i]);
+      }
+    }
+  };
+
+  gload(j0);
+  for (int j = j0; j < j1; ++j) {
+    __syncthreads();
+    lstore();
+    __syncthreads();
+    if (j + 1 < j1) gload(j + 1);
+
+    // centroid (mean of keys) and value sum, one thread per column
+    if (tid < 2 * D) {
+      const bf16* rp = (tid < D) ? (Kt + tid * C::ROW) : (Vt + (tid - D) * C::ROW);
+      float s = 0.f;
+#pragma unroll
+      for (int c8 = 0; c8 < BLK / 8; ++c8) {
+        const bf16x8 v = as_bf16x8(ld16(rp + 8 * c8));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += (float)v[e];
+      }
+      if (tid < D) {
+        s_k[tid] = s * (1.f / BLK);
+        if (!PASS2) centroid[((size_t)bh * nb + j) * D + tid] = s * (1.f / BLK);
+      } else {
+        s_v[tid - D] = s;
+        if (!PASS2) vsum[((size_t)bh * nb + j) * D + (tid - D)] = s;
+      }
+    }
+
+    // K_j^T V_j on MFMA: A = K^T rows (key dim), B = V^T rows (value dim), k = tokens
+    if (PASS2) {
+#pragma unroll
+      for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TM; ++b) acc[a][b] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < BLK / 16; ++ks) {
+      bf16x8 A[C::TM], Bv[C::TM];
+#pragma unroll
+      for (int a = 0; a < C::TM; ++a)
+        A[a] = as_bf16x8(ld16(Kt + (32 * (mt0 + a) + q32) * C::ROW + 16 * ks + 8 * hh));
+#pragma unroll
+      for (int b = 0; b < C::TM; ++b)
+        Bv[b] = as_bf16x8(ld16(Vt + (32 * (nt0 + b) + q32) * C::ROW + 16 * ks + 8 * hh));
+#pragma unroll
+      for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma32(A[a], Bv[b], acc[a][b]);
+    }
+    __syncthreads();
+
+    // H_j = K_j^T V_j - kbar_j^T sigma_j
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+      for (int b = 0; b < C::TM; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ra = 32 * (mt0 + a) + 8 * (r / 4) + 4 * hh + (r % 4);
+          const int cb = 32 * (nt0 + b) + q32;
+          acc[a][b][r] -= s_k[ra] * s_v[cb];
+        }
+
+    if (PASS2) {
+      float sq = 0.f;
+      float* Hj = Hout ? Hout + ((size_t)bh * nb + j) * D * D : nullptr;
+#pragma unroll
+      for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+        for (int b = 0; b < C::TM; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float x = acc[a][b][r];
+            const float dlt = x - hb[a][b][r];
+            sq += dlt * dlt;
+            if (Hj) Hj[(32 * (mt0 + a) + 8 * (r / 4) + 4 * hh + (r % 4)) * D + 32 * (nt0 + b) + q32] = x;
+          }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+      if (lane == 0) s_red[w] = sq;
+      __syncthreads();
+      if (tid == 0) M[(size_t)bh * nb + j] = sqrtf(s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+    }
+  }
+
+  if (!PASS2) {
+    float* P = partial + ((size_t)bh * ngrp + grp) * D * D;
+#pragma unroll
+    for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+      for (int b = 0; b < C::TM; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          P[(32 * (mt0 + a) + 8 * (r / 4) + 4 * hh + (r % 4)) * D + 32 * (nt0 + b) + q32] = acc[a][b][r];
+  }
+}
+
+// Hbar[bh][e] = (1/nb) sum_g parts[bh][g][e], summed in fp64 in group order.
+__global__ __launch_bounds__(256) void hbar_reduce_kernel(const float* __restrict__ parts, int ngrp,
+                                                          int nb, int DD, int total,
+                                                          float* __restrict__ hbar) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;
+  const int bh = t / DD, e = t - bh * DD;
+  const float* p = parts + (size_t)bh * ngrp * DD + e;
+  double s = 0.0;
+  for (int g = 0; g < ngrp; ++g) s += (double)p[(size_t)g * DD];
+  hbar[t] = (float)(s / nb);
+}
+
+// ---------------------------------------------------------------- fp32 path
+
+// one workgroup per (bh, block j): centroid, value sum and H_j with centred keys
+template <int D>
+__global__ __launch_bounds__(256) void stats_f32_block_kernel(
+    const float* __restrict__ K, const float* __restrict__ V, int nb, int BLK,
+    float* __restrict__ centroid, float* __restrict__ vsum, float* __restrict__ Hbuf) {
+  constexpr int NT = 256, CH = 32, PER = D * D / NT;
+  __shared__ float kc[CH][D];
+  __shared__ float vc[CH][D];
+  __shared__ float s_k[D];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x / nb, j = blockIdx.x - bh * nb;
+  const float* Kb = K + ((size_t)bh * nb + j) * BLK * D;
+  const float* Vb = V + ((size_t)bh * nb + j) * BLK * D;
+  if (tid < D) {
+    float sk = 0.f, sv = 0.f;
+    for (int n = 0; n < BLK; ++n) {
+      sk += Kb[(size_t)n * D + tid];
+      sv += Vb[(size_t)n * D + tid];
+    }
+    s_k[tid] = sk / BLK;
+    centroid[((size_t)bh * nb + j) * D + tid] = sk / BLK;
+    vsum[((size_t)bh * nb + j) * D + tid] = sv;
+  }
+  __syncthreads();
+  float acc[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) acc[u] = 0.f;
+  for (int n0 = 0; n0 < BLK; n0 += CH) {
+    for (int q = tid; q < CH * D; q += NT) {
+      const int n = q / D, c = q % D;
+      kc[n][c] = Kb[(size_t)(n0 + n) * D + c] - s_k[c];
+      vc[n][c] = Vb[(size_t)(n0 + n) * D + c];
+    }
+    __syncthreads();
+    for (int n = 0; n < CH; ++n)
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int e = tid + u * NT;
+        acc[u] += kc[n][e / D] * vc[n][e % D];
+      }
+    __syncthreads();
+  }
+  float* Hj = Hbuf + ((size_t)bh * nb + j) * D * D;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) Hj[tid + u * NT] = acc[u];
+}
+
+// M_j = ||H_j - Hbar||_F, one workgroup per (bh, j), fixed reduction order
+template <int D>
+__global__ __launch_bounds__(256) void frob_kernel(const float* __restrict__ Hbuf,
+                                                   const float* __restrict__ hbar, int nb,
+                                                   float* __restrict__ M) {
+  __shared__ float s_red[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int bh = blockIdx.x / nb;
+  const float* Hj = Hbuf + (size_t)blockIdx.x * D * D;
+  const float* hb = hbar + (size_t)bh * D * D;
+  float sq = 0.f;
+  for (int e = tid; e < D * D; e += 256) {
+    const float dlt = Hj[e] - hb[e];
+    sq += dlt * dlt;
+  }
+  for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+  if (lane == 0) s_red[w] = sq;
+  __syncthreads();
+  if (tid == 0) M[blockIdx.x] = sqrtf(s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+}
+
+template <int D, int BLK>
+hipError_t stats_bf16_t(const StatsArgs& a) {
+  const int ngrp = (a.nb + kStatsGroup - 1) / kStatsGroup;
+  float* parts = static_cast<float*>(a.ws);
+  const int grid = a.bh * ngrp;
+  hipLaunchKernelGGL((stats_bf16_kernel<D, BLK, false>), dim3(grid), dim3(256), 0, a.stream,
+                     (const bf16*)a.K, (const bf16*)a.V, a.nb, a.centroid, a.vsum, parts,
+                     (const float*)nullptr, (float*)nullptr, (float*)nullptr);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int total = a.bh * D * D;
+  hipLaunchKernelGGL(hbar_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, a.stream,
+                     (const float*)parts, ngrp, a.nb, D * D, total, a.hbar);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((stats_bf16_kernel<D, BLK, true>), dim3(grid), dim3(256), 0, a.stream,
+                     (const bf16*)a.K, (const bf16*)a.V, a.nb, (float*)nullptr, (float*)nullptr,
+                     (float*)nullptr, (const float*)a.hbar, a.M, a.H);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t stats_f32_t(const StatsArgs& a) {
+  float* Hbuf = a.H ? a.H : static_cast<float*>(a.ws);
+  const int grid = a.bh * a.nb;
+  hipLaunchKernelGGL((stats_f32_block_kernel<D>), dim3(grid), dim3(256), 0, a.stream,
+                     (const float*)a.K, (const float*)a.V, a.nb, a.BLK, a.centroid, a.vsum, Hbuf);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int total = a.bh * D * D;
+  hipLaunchKernelGGL(hbar_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, a.stream,
+                     (const float*)Hbuf, a.nb, a.nb, D * D, total, a.hbar);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((frob_kernel<D>), dim3(grid), dim3(256), 0, a.stream, (const float*)Hbuf,
+                     (const float*)a.hbar, a.nb, a.M);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t stats_workspace_bf16(int bh, int nb, int D) {
+  const size_t ngrp = (size_t)(nb + kStatsGroup - 1) / kStatsGroup;
+  return (size_t)bh * ngrp * D * D * sizeof(float);
+}
+
+size_t stats_workspace_f32(int bh, int nb, int D) {
+  return (size_t)bh * nb * D * D * sizeof(float);
+}
+
+hipError_t launch_stats_bf16(const StatsArgs& a) {
+  if (a.D == 128 && a.BLK == 64) return stats_bf16_t<128, 64>(a);
+  if (a.D == 128 && a.BLK == 128) return stats_bf16_t<128, 128>(a);
+  if (a.D == 64 && a.BLK == 64) return stats_bf16_t<64, 64>(a);
+  if (a.D == 64 && a.BLK == 128) return stats_bf16_t<64, 128>(a);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_stats_f32(const StatsArgs& a) {
+  if (a.D == 128) return stats_f32_t<128>(a);
+  if (a.D == 64) return stats_f32_t<64>(a);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pisa

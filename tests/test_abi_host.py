@@ -1,0 +1,111 @@
+"""Host-only checks of libpisa's C ABI: the library loads, exports every symbol
+include/pisa.h declares, and rejects bad arguments before touching the GPU.
+
+Every call here fails validation, which happens on the host before any HIP
+call, so no device is needed.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from piecewise_block_sparse_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)       # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libpisa.so is not built (run python -m piecewise_block_sparse_amd.build)")
+    return _lib.load()
+
+
+def shape(b=1, h=2, L=1024, d=128, B=64, dtype=_lib.DTYPE_BF16):
+    return _lib.PisaShape(b, h, L, d, B, dtype)
+
+
+def stats(full=True):
+    p = FAKE.value
+    return _lib.PisaStats(p, p, None, p, p) if full else _lib.PisaStats(None, p, None, p, p)
+
+
+def test_exports_every_declared_symbol(lib):
+    header = open(os.path.join(ROOT, "include", "pisa.h")).read()
+    declared = set(re.findall(r"\b(pisa_\w+)\s*\(", header))
+    assert declared == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.pisa_version() == 100
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.pisa_status_string(code)
+    assert lib.pisa_status_string(99) == b"unknown status"
+
+
+def pre(lib, shp, out=None, ws=FAKE, wsb=1 << 40):
+    out = stats() if out is None else out
+    return lib.pisa_precompute(ctypes.byref(shp) if shp else None, FAKE, FAKE,
+                               ctypes.byref(out), ws, wsb, None)
+
+
+def rte(lib, shp, k=4, scale=0.1, lam=0.1, Q=FAKE):
+    return lib.pisa_route(ctypes.byref(shp), Q, FAKE, FAKE, k, scale, lam, FAKE, None)
+
+
+def att(lib, shp, kmax=4, mode=0, scale=0.1, st=None, O=FAKE):
+    st = stats() if st is None else st
+    return lib.pisa_attention(ctypes.byref(shp), FAKE, FAKE, FAKE, FAKE, kmax, ctypes.byref(st),
+                              mode, scale, O, None)
+
+
+def test_shape_rules(lib):
+    assert pre(lib, None) == 1
+    assert pre(lib, shape(dtype=7)) == 4
+    assert pre(lib, shape(L=1000)) == 2              # ragged last block
+    assert pre(lib, shape(d=96)) == 2
+    assert pre(lib, shape(B=32)) == 2
+    assert pre(lib, shape(L=64 * 4096)) == 2         # more than 2048 blocks
+    assert pre(lib, shape(b=0)) == 2
+    assert pre(lib, shape(h=-1)) == 2
+    assert rte(lib, shape(L=1000)) == 2
+    assert att(lib, shape(L=1000)) == 2
+    assert lib.pisa_workspace_size(ctypes.byref(shape(L=1000))) == 0
+
+
+def test_precompute_arguments(lib):
+    s = shape()
+    assert pre(lib, s, out=stats(full=False)) == 1                 # missing centroid
+    need = lib.pisa_workspace_size(ctypes.byref(s))
+    assert need == 2 * (16 // 8) * 128 * 128 * 4                  # one fp32 d x d partial per 8 blocks
+    assert pre(lib, s, ws=None) == 1
+    assert pre(lib, s, wsb=need - 1) == 5
+    assert b"needs" in lib.pisa_last_error()
+    f = shape(dtype=_lib.DTYPE_FP32, d=64)
+    assert lib.pisa_workspace_size(ctypes.byref(f)) == 2 * 16 * 64 * 64 * 4
+
+
+def test_route_arguments(lib):
+    s = shape()                                                     # nb = 16
+    assert rte(lib, s, k=0) == 3
+    assert rte(lib, s, k=17) == 3
+    assert rte(lib, s, scale=float("nan")) == 3
+    assert rte(lib, s, lam=float("inf")) == 3
+    assert rte(lib, s, Q=None) == 1
+
+
+def test_attention_arguments(lib):
+    s = shape()
+    assert att(lib, s, kmax=0) == 3
+    assert att(lib, s, kmax=17) == 3
+    assert att(lib, s, mode=2) == 3
+    assert att(lib, s, scale=float("nan")) == 3
+    assert att(lib, s, scale=-0.5) == 3
+    assert att(lib, s, O=None) == 1
+    assert att(lib, s, st=stats(full=False)) == 1                  # APPROX needs centroids
+    assert b"APPROX" in lib.pisa_last_error()
