@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the PISA hot path on one MI355X.
+
+One step = pisa_precompute + pisa_route + pisa_attention (exact-or-approximate
+mode) over one batch of seeded synthetic inputs already resident in HBM, on
+the video-DiT-L workload (batch 1, 40 heads, L = 32768 on a 16x32x64 latent
+grid, head dim 128, block 128, top-k 32 of 256 blocks = 12.5% density, bf16).
+
+Prints ONE JSON line.  `value` is the algorithmic TFLOP/s of the whole step;
+`ms_per_step` its latency; `roofline` describes the fused attention kernel
+(the dominant one) against the bf16 MFMA peak; `phases` splits the step by
+kernel (HIP events on the launch stream); `dense` is the same kernel run with
+every block exact; `cpu_baseline` is the fp64 oracle on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4|3]
+                    [--no-cpu-baseline] [--no-dense] [--copy-calibration]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0               # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def flops(w, k):
+    """Algorithmic FLOPs of one step's calls (2 per multiply-add)."""
+    bh, L, d, B, nb = w.batch * w.heads, w.seq_len, w.head_dim, w.block, w.nb
+    exact = bh * nb * 4 * B * (k * B) * d                 # QK^T and PV over k exact blocks
+    approx = bh * L * (4 * d * (nb - k) + 2 * d * d)      # centroid logits + sigma sums + q Hbar
+    stats = 2 * bh * nb * 2 * B * d * d                   # K_j^T V_j, two passes
+    route = bh * nb * nb * 2 * d                          # pooled-q . kbar (fp64)
+    return {"exact": exact, "approx": approx, "attention": exact + approx, "stats": stats,
+            "route": route, "step": exact + approx + stats + route}
+
+
+def bytes_moved(w):
+    """Algorithmic HBM bytes of the streaming kernels."""
+    bh, L, d, nb = w.batch * w.heads, w.seq_len, w.head_dim, w.nb
+    e = 2
+    kv = bh * L * d * e * 2
+    stats_out = bh * (2 * nb * d + d * d + nb) * 4
+    return {"stats": 2 * kv + stats_out, "route": bh * L * d * e + bh * nb * (d + 1) * 4}
+
+
+def timed_phases(pisa, torch, Qd, Kd, Vd, w, k, steps, warmup, mode="approx"):
+    """Run `steps` full steps; return total wall ms and per-phase event ms."""
+    stream = torch.cuda.current_stream()
+    ws = torch.empty(pisa.workspace_size(Kd, w.block), dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        st = pisa.precompute(Kd, Vd, w.block, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        idx = pisa.route(Qd, st, k, w.lam, w.block)
+        if ev is not None:
+            ev[2].record(stream)
+        out = pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode=mode)
+        if ev is not None:
+            ev[3].record(stream)
+        return st, idx, out
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        st, idx, out = step(evs[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ph = {"precompute": 0.0, "route": 0.0, "attention": 0.0}
+    for e in evs:
+        ph["precompute"] += e[0].elapsed_time(e[1])
+        ph["route"] += e[1].elapsed_time(e[2])
+        ph["attention"] += e[2].elapsed_time(e[3])
+    return wall_ms, {n: v / steps for n, v in ph.items()}, (st, idx, out)
+
+
+def time_attention(pisa, torch, Qd, Kd, Vd, idx, st, w, mode, reps):
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode=mode)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode=mode)
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The fp64 oracle on whole heads of the same workload, until ~budget_s."""
+    import numpy as np
+    import oracle
+    from piecewise_block_sparse_amd import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    done, spent, fl = 0, 0.0, 0.0
+    per_head = flops(wl.WORKLOADS[w.wid], w.k)
+    for h in range(w.heads):
+        Q, K, V = wl.make_inputs(w, heads=[h])
+        t0 = time.perf_counter()
+        st = oracle.precompute(K, V, w.block)
+        idx = oracle.route(Q, st["centroid"], st["M"], w.k, w.lam, w.block, w.scale)
+        oracle.attention(Q, K, V, idx, st["centroid"], st["vsum"], st["Hbar"], oracle.MODE_APPROX,
+                         w.scale, w.block)
+        spent += time.perf_counter() - t0
+        done += 1
+        fl += per_head["step"] / w.heads
+        if spent >= budget_s:
+            break
+    return {"value": fl / spent / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {w.heads} heads, full precompute+route+attention each, "
+                      f"{spent:.1f} s of fp64 numpy",
+            "seconds_per_step_extrapolated": spent * w.heads / done}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4, choices=[3, 4])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              f"(the path shards by heads with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import piecewise_block_sparse_amd as pisa
+    from piecewise_block_sparse_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    pisa._lib.load()
+
+    if args.copy_calibration:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+
+    def run(wid, steps, warmup, with_dense):
+        w = wl.WORKLOADS[wid]
+        log(f"{w.name}: generating inputs")
+        Q, K, V = wl.make_inputs(w)
+        Qd, Kd, Vd = (torch.from_numpy(a).to("cuda", torch.bfloat16) for a in (Q, K, V))
+        del Q, K, V
+        log(f"{w.name}: timing {steps} steps")
+        wall_ms, ph, (st, idx, _) = timed_phases(pisa, torch, Qd, Kd, Vd, w, w.k, steps, warmup)
+        f, by = flops(w, w.k), bytes_moved(w)
+        res = {"wall_ms_per_step": wall_ms / steps, "phases_ms": ph}
+        t_drop = time_attention(pisa, torch, Qd, Kd, Vd, idx, st, w, "drop", max(5, steps // 2))
+        res["exact_phase_ms"] = t_drop
+        res["approx_phase_ms"] = ph["attention"] - t_drop
+        res["tflops"] = {
+            "step": f["step"] / (wall_ms / steps) / 1e9,
+            "attention": f["attention"] / ph["attention"] / 1e9,
+            "exact_phase": f["exact"] / t_drop / 1e9,
+        }
+        res["gbs"] = {"precompute": by["stats"] / ph["precompute"] / 1e6,
+                      "route": by["route"] / ph["route"] / 1e6}
+        res["gflop"] = {n: v / 1e9 for n, v in f.items()}
+        if with_dense:
+            log(f"{w.name}: dense comparator")
+            nb = w.nb
+            dense_idx = torch.arange(nb, dtype=torch.int32, device="cuda").expand(
+                w.batch, w.heads, nb, nb).contiguous()
+            t_dense = time_attention(pisa, torch, Qd, Kd, Vd, dense_idx, st, w, "drop", 3)
+            fd = flops(w, nb)["exact"]
+            res["dense"] = {"ms": t_dense, "tflops": fd / t_dense / 1e9,
+                            "speedup_of_pisa_attention": t_dense / ph["attention"]}
+        del Qd, Kd, Vd, st, idx
+        torch.cuda.empty_cache()
+        return w, res
+
+    w, main_res = run(args.workload, args.steps, args.warmup, not args.no_dense)
+    f = flops(w, w.k)
+    ms = main_res["wall_ms_per_step"]
+    t_attn = main_res["phases_ms"]["attention"]
+    achieved = f["attention"] / t_attn / 1e9
+    line = {
+        "metric": "PISA attention latency (ms) & TFLOP/s at L=32K d=128 12.5% density; MFMA util",
+        "value": f["step"] / ms / 1e9,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; smooth latent-grid field + N(0,1) noise)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
+                   "head_dim": w.head_dim, "block": w.block, "k": w.k,
+                   "density": w.k / w.nb, "lambda": w.lam, "mode": "approx"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None, "kernel": "attn_bf16_kernel<128,128>",
+                     "avg_launch_ms": t_attn},
+        "phases": main_res,
+    }
+    if not args.no_secondary:
+        other = 3 if args.workload == 4 else 4
+        _, res2 = run(other, max(5, args.steps // 2), 2, False)
+        line["secondary"] = {wl.WORKLOADS[other].name: res2}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -85,6 +85,13 @@ typedef struct {
                                             only when non-NULL                               */
   float* Hbar;              /* [b,h,d,d]    mean of H_j over the nb blocks of (b,h)          */
   float* M;                 /* [b,h,nb]     M_j = ||H_j - Hbar||_F                           */
+  void* packed;             /* NULLABLE, bf16 inputs only: pisa_packed_size() bytes holding
+                               bfloat16 copies that the attention kernel streams:
+                                 centroid [b,h,nbp,d] | vsum [b,h,nbp,d] | Hbar^T [b,h,d,d]
+                               (nbp = nb rounded up to a multiple of block, padding rows 0;
+                               Hbar^T row = value dim).  Written by pisa_precompute when
+                               non-NULL; read by pisa_attention (PISA mode) when non-NULL,
+                               which otherwise converts the fp32 statistics itself.         */
 } pisa_stats;
 
 /* Version of the library (PISA_VERSION at build time). */
@@ -101,6 +108,10 @@ const char* pisa_last_error(void);
  * shape is invalid).  The workspace holds deterministic partial sums of H_j. */
 size_t pisa_workspace_size(const pisa_shape* shape);
 
+/* Bytes of the optional bf16 statistics pack (pisa_stats.packed) for this
+ * shape: b*h*(2*nbp*d + d*d)*2 for bf16 inputs, 0 for fp32 or invalid shapes. */
+size_t pisa_packed_size(const pisa_shape* shape);
+
 /*
  * pisa_precompute -- block statistics (PISA summary, section 2: "Core
  * algorithm" defines kbar_j, the value sums, H_j and Hbar; "Covariance-aware
@@ -108,7 +119,7 @@ size_t pisa_workspace_size(const pisa_shape* shape);
  * "Hardware implementation" places this computation before the attention).
  *
  *   K, V       [b,h,L,d] of shape->dtype (device, read only)
- *   out        centroid, vsum, Hbar, M required; H optional (see pisa_stats)
+ *   out        centroid, vsum, Hbar, M required; H and packed optional (see pisa_stats)
  *   workspace  device scratch of at least pisa_workspace_size(shape) bytes,
  *              caller-owned; contents on entry are ignored
  *
@@ -152,8 +163,8 @@ pisa_status pisa_route(const pisa_shape* shape, const void* Q, const float* cent
  *             < nb (ids >= nb are skipped, duplicates are counted twice; no
  *             fault either way).  Rows may be fully padded (S_i empty).
  *   kmax      row length of idx, 1 <= kmax <= nb
- *   stats     centroid, vsum, Hbar read in APPROX mode (may be NULL in DROP
- *             mode); H and M are not read
+ *   stats     centroid, vsum, Hbar (and packed, when non-NULL) read in APPROX
+ *             mode (may be NULL in DROP mode); H and M are not read
  *   mode      pisa_mode
  *   scale     softmax scale applied to every q_t (exact logits, alpha and the
  *             correction), finite

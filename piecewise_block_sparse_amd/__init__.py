@@ -76,8 +76,11 @@ def workspace_size(X, block: int) -> int:
     return _lib.load().pisa_workspace_size(ctypes.byref(_shape(X, block)))
 
 
-def precompute(K, V, block: int, store_H: bool = False, workspace=None) -> dict:
-    """Block statistics (fp32): centroid, vsum, Hbar, M, and H when store_H."""
+def precompute(K, V, block: int, store_H: bool = False, workspace=None, packed: bool = True) -> dict:
+    """Block statistics (fp32): centroid, vsum, Hbar, M, and H when store_H.
+
+    For bf16 inputs (and packed=True) also the bf16 pack that the attention
+    kernel streams in PISA mode (key "packed")."""
     torch = _torch()
     lib = _lib.load()
     _same(K, V)
@@ -91,11 +94,15 @@ def precompute(K, V, block: int, store_H: bool = False, workspace=None) -> dict:
         "H": torch.empty((b, h, nb, d, d), **f32) if store_H else None,
         "Hbar": torch.empty((b, h, d, d), **f32),
         "M": torch.empty((b, h, nb), **f32),
+        "packed": None,
     }
+    npk = lib.pisa_packed_size(ctypes.byref(shp)) if packed else 0
+    if npk:
+        out["packed"] = torch.empty(npk, dtype=torch.uint8, device=K.device)
     need = lib.pisa_workspace_size(ctypes.byref(shp))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=K.device)
-    st = _lib.PisaStats(*(_ptr(out[n]) for n in ("centroid", "vsum", "H", "Hbar", "M")))
+    st = _lib.PisaStats(*(_ptr(out[n]) for n in ("centroid", "vsum", "H", "Hbar", "M", "packed")))
     _lib.check("pisa_precompute", lib.pisa_precompute(
         ctypes.byref(shp), _ptr(K), _ptr(V), ctypes.byref(st), _ptr(workspace),
         workspace.numel(), _stream(K)))
@@ -145,8 +152,11 @@ def attention(Q, K, V, idx, stats: dict | None, block: int, mode: int | str = "a
         _expect(stats["vsum"], (b, h, nb, d), torch.float32, "stats['vsum']")
         _expect(stats["Hbar"], (b, h, d, d), torch.float32, "stats['Hbar']")
     if stats is not None:
+        pk = stats.get("packed")
+        if pk is not None and pk.numel() != lib.pisa_packed_size(ctypes.byref(shp)):
+            raise ValueError("stats['packed'] does not match this shape")
         st = _lib.PisaStats(_ptr(stats["centroid"]), _ptr(stats["vsum"]), None,
-                            _ptr(stats["Hbar"]), None)
+                            _ptr(stats["Hbar"]), None, _ptr(pk))
     _lib.check("pisa_attention", lib.pisa_attention(
         ctypes.byref(shp), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), int(idx.shape[-1]),
         ctypes.byref(st) if st is not None else None, int(mode), scale, _ptr(O), _stream(Q)))

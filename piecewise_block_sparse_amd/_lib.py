@@ -20,7 +20,7 @@ MODE_DROP = 1
 
 # every symbol the header declares
 EXPORTS = ("pisa_version", "pisa_status_string", "pisa_last_error", "pisa_workspace_size",
-           "pisa_precompute", "pisa_route", "pisa_attention")
+           "pisa_packed_size", "pisa_precompute", "pisa_route", "pisa_attention")
 
 
 class PisaShape(ctypes.Structure):
@@ -30,7 +30,7 @@ class PisaShape(ctypes.Structure):
 
 class PisaStats(ctypes.Structure):
     _fields_ = [("centroid", ctypes.c_void_p), ("vsum", ctypes.c_void_p), ("H", ctypes.c_void_p),
-                ("Hbar", ctypes.c_void_p), ("M", ctypes.c_void_p)]
+                ("Hbar", ctypes.c_void_p), ("M", ctypes.c_void_p), ("packed", ctypes.c_void_p)]
 
 
 class PisaError(RuntimeError):
@@ -60,6 +60,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_last_error.argtypes = []
     lib.pisa_workspace_size.restype = sz
     lib.pisa_workspace_size.argtypes = [sp]
+    lib.pisa_packed_size.restype = sz
+    lib.pisa_packed_size.argtypes = [sp]
     lib.pisa_precompute.restype = i32
     lib.pisa_precompute.argtypes = [sp, vp, vp, stp, vp, sz, vp]
     lib.pisa_route.restype = i32

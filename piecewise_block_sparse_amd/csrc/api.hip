@@ -79,6 +79,12 @@ size_t pisa_workspace_size(const pisa_shape* shape) {
                                          : pisa::stats_workspace_f32(bh, nb, shape->head_dim);
 }
 
+size_t pisa_packed_size(const pisa_shape* shape) {
+  int bh = 0, nb = 0;
+  if (check_shape(shape, &bh, &nb) != PISA_OK || shape->dtype != PISA_DTYPE_BF16) return 0;
+  return pisa::stats_packed_bytes(bh, nb, shape->head_dim, shape->block);
+}
+
 pisa_status pisa_precompute(const pisa_shape* shape, const void* K, const void* V,
                             const pisa_stats* out, void* workspace, size_t workspace_bytes,
                             void* stream) {
@@ -97,8 +103,9 @@ pisa_status pisa_precompute(const pisa_shape* shape, const void* K, const void* 
     if (workspace_bytes < need)
       return fail(PISA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   }
-  pisa::StatsArgs a{K, V, out->centroid, out->vsum, out->H, out->Hbar, out->M, workspace,
-                    bh, nb, shape->head_dim, shape->block, (hipStream_t)stream};
+  pisa::StatsArgs a{K, V, out->centroid, out->vsum, out->H, out->Hbar, out->M,
+                    bf ? out->packed : nullptr, workspace, bh, nb, shape->head_dim, shape->block,
+                    (hipStream_t)stream};
   return hip_status(bf ? pisa::launch_stats_bf16(a) : pisa::launch_stats_f32(a), "pisa_precompute");
 }
 
@@ -136,11 +143,12 @@ pisa_status pisa_attention(const pisa_shape* shape, const void* Q, const void* K
   const bool approx = mode == PISA_MODE_APPROX;
   if (approx && (!stats || !stats->centroid || !stats->vsum || !stats->Hbar))
     return fail(PISA_ERR_NULL, "APPROX mode needs stats centroid, vsum and Hbar");
+  const bool bf = shape->dtype == PISA_DTYPE_BF16;
   pisa::AttnArgs a{Q, K, V, idx, kmax,
                    approx ? stats->centroid : nullptr, approx ? stats->vsum : nullptr,
-                   approx ? stats->Hbar : nullptr, approx ? 1 : 0, scale, O, bh, nb,
-                   shape->head_dim, shape->block, (hipStream_t)stream};
-  const bool bf = shape->dtype == PISA_DTYPE_BF16;
+                   approx ? stats->Hbar : nullptr, (approx && bf) ? stats->packed : nullptr,
+                   approx ? 1 : 0, scale, O, bh, nb, shape->head_dim, shape->block,
+                   (hipStream_t)stream};
   return hip_status(bf ? pisa::launch_attn_bf16(a) : pisa::launch_attn_f32(a), "pisa_attention");
 }
 

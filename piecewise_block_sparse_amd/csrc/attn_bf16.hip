@@ -168,10 +168,37 @@ struct RowState {
   float a;      // this lane's share of sum over U_i of alpha (same scaling as acc)
 };
 
+// The running max is only raised when a row's new maximum exceeds it by more
+// than kTau (log2 units); until then the weights exp2(x - m) stay below 2^kTau.
+// Any m gives the same N / D, so this only saves rescales of acc.
+constexpr float kTau = 8.f;
+
+// exp2 weights of one 64-key chunk -> bf16 MFMA B operands (pf) and the sum of
+// the same bf16-rounded weights.  Each pair is packed into its own 32-bit value
+// and summed from that value with v_dot2 against (1, 1) before the four pairs
+// of a slab are assembled into the 128-bit operand.
+__device__ __forceinline__ float weights_bf16(const f32x16 (&s)[2], float c2, float nm,
+                                              u32x4 (&pf)[4]) {
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+  float sum = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float p0 = fast_exp2(fmaf(s[kt][2 * q], c2, nm));
+      const float p1 = fast_exp2(fmaf(s[kt][2 * q + 1], c2, nm));
+      const bf16x2 pr = {(bf16)p0, (bf16)p1};
+      sum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, sum, false);
+      pf[2 * kt + q / 4][q % 4] = __builtin_bit_cast(unsigned, pr);
+    }
+  return sum;
+}
+
 // One 64-key chunk of the LDS tile: S^T, softmax update, O^T += V^T P^T.
 // STAGE2: the keys are block centroids (values = block value sums); entries
 // whose block is in S_i or past nb are masked, and each weight counts `block`
-// times in the denominator.
+// times in the denominator.  The denominator sums the same bf16-rounded
+// weights that the MFMA multiplies into the numerator.
 template <int D, int BLK, bool STAGE2>
 __device__ __forceinline__ void chunk(RowState<D>& st, const bf16x8 (&qf)[D / 16], const bf16* Ks,
                                       const bf16* Vt, int ch, float c2, int q32, int hh,
@@ -185,47 +212,45 @@ __device__ __forceinline__ void chunk(RowState<D>& st, const bf16x8 (&qf)[D / 16
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) s[kt] = mfma32(as_bf16x8(ld16(krow + 16 * ks)), qf[ks], s[kt]);
   }
+  if (STAGE2) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = jbase + 64 * ch + 32 * kt + 8 * (r / 4) + 4 * hh + (r % 4);
+        const bool masked = (j >= nb) || ((bits[j >> 5] >> (j & 31)) & 1u);
+        s[kt][r] = masked ? -INFINITY : s[kt][r];
+      }
+  }
   float mx = -INFINITY;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = s[kt][r] * c2;
-      if (STAGE2) {
-        const int j = jbase + 64 * ch + 32 * kt + 8 * (r / 4) + 4 * hh + (r % 4);
-        const bool masked = (j >= nb) || ((bits[j >> 5] >> (j & 31)) & 1u);
-        x = masked ? -INFINITY : x;
-      }
-      s[kt][r] = x;
-      mx = fmaxf(mx, x);
-    }
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mnew = fmaxf(st.m, mx);
-  const float corr = fast_exp2(st.m - mnew);
-  st.m = mnew;
-  float ps = 0.f;
-  bf16x8 pf[4];
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
+  if (__any(mx > st.m + kTau)) {
+    const float mnew = fmaxf(st.m, mx);
+    const float corr = fast_exp2(st.m - mnew);
+    st.m = mnew;
+    st.l *= corr;
+    st.a *= corr;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(s[kt][r] - mnew);
-      ps += p;
-      pf[2 * kt + r / 8][r % 8] = (bf16)p;
-    }
-  if (STAGE2) {
-    st.l = st.l * corr + (float)BLK * ps;
-    st.a = st.a * corr + ps;
-  } else {
-    st.l = st.l * corr + ps;
+    for (int mt = 0; mt < C::MT; ++mt) st.acc[mt] *= corr;
   }
-#pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt) st.acc[mt] *= corr;
+  u32x4 pf[4];
+  const float ps = weights_bf16(s, c2, -st.m, pf);
+  if (STAGE2) {
+    st.l += (float)BLK * ps;
+    st.a += ps;
+  } else {
+    st.l += ps;
+  }
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) {
     const bf16* vrow = Vt + (32 * mt + q32) * C::VROW + 64 * ch + 8 * hh;
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) st.acc[mt] = mfma32(as_bf16x8(ld16(vrow + 16 * sl)), pf[sl], st.acc[mt]);
+    for (int sl = 0; sl < 4; ++sl)
+      st.acc[mt] = mfma32(as_bf16x8(ld16(vrow + 16 * sl)), as_bf16x8(pf[sl]), st.acc[mt]);
   }
 }
 
@@ -238,12 +263,26 @@ __device__ __forceinline__ int next_valid(const int32_t* row, int e, int kmax, i
   return e;
 }
 
+// Kernel arguments: fp32 statistics, plus (optionally) their bf16 packs written
+// by the statistics pass: centroids and value sums [nbp][D] per head (nbp = nb
+// rounded up to BLK, padding rows zero) and Hbar^T [D][D] per head.
+struct AttnPtrs {
+  const bf16* Q;
+  const bf16* K;
+  const bf16* V;
+  const int32_t* idx;
+  const float* centroid;
+  const float* vsum;
+  const float* hbar;
+  const bf16* pk_cen;
+  const bf16* pk_vsum;
+  const bf16* pk_hbart;
+  bf16* O;
+};
+
 template <int D, int BLK>
-__global__ __launch_bounds__(2 * BLK) void attn_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const int32_t* __restrict__ idx, int kmax, const float* __restrict__ centroid,
-    const float* __restrict__ vsum, const float* __restrict__ hbar, int approx, float scale,
-    bf16* __restrict__ O, int nb) {
+__global__ __launch_bounds__(2 * BLK) void attn_bf16_kernel(AttnPtrs p, int kmax, int approx,
+                                                            float scale, int nb) {
   using C = Cfg<D, BLK>;
   __shared__ __attribute__((aligned(16))) bf16 lds[C::LDS_ELEMS];
   __shared__ unsigned bits[kMaxBlocks / 32];
@@ -255,9 +294,11 @@ __global__ __launch_bounds__(2 * BLK) void attn_bf16_kernel(
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = logical / nb, i = logical - bh * nb;
   const size_t L = (size_t)nb * BLK;
-  const bf16* Kh = K + (size_t)bh * L * D;
-  const bf16* Vh = V + (size_t)bh * L * D;
-  const int32_t* row = idx + ((size_t)bh * nb + i) * kmax;
+  const int nbp = (nb + BLK - 1) / BLK * BLK;
+  const bf16* Kh = p.K + (size_t)bh * L * D;
+  const bf16* Vh = p.V + (size_t)bh * L * D;
+  const int32_t* row = p.idx + ((size_t)bh * nb + i) * kmax;
+  const bool packed = approx && p.pk_cen != nullptr;
 
   if (approx) {
     for (int e = tid; e < (nb + 31) / 32; e += C::NT) bits[e] = 0u;
@@ -271,7 +312,7 @@ __global__ __launch_bounds__(2 * BLK) void attn_bf16_kernel(
   // this lane's query row as 16-byte B-operand fragments (d = 16 ks + 8 hh + 0..7)
   bf16x8 qf[C::KS];
   {
-    const bf16* qrow = Q + ((size_t)bh * L + (size_t)i * BLK + 32 * w + q32) * D + 8 * hh;
+    const bf16* qrow = p.Q + ((size_t)bh * L + (size_t)i * BLK + 32 * w + q32) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_bf16x8(ld16(qrow + 16 * ks));
   }
@@ -283,67 +324,116 @@ __global__ __launch_bounds__(2 * BLK) void attn_bf16_kernel(
   st.a = 0.f;
   const float c2 = scale * kLog2e;
 
-  // ---- stage 1: exact attention over the selected blocks (register-prefetched)
+  // ---- stages 1 and 2 as one register-prefetched stream of tiles: the exact
+  // blocks of S_i, then (PISA mode, packed statistics) the centroid / value-sum
+  // tiles, which have exactly the layout of a K / V block.
+  const int ntile = packed ? nbp / BLK : 0;
+  int e = next_valid(row, 0, kmax, nb), t = 0;
+  auto next_tile = [&](int& kind, int& id) {
+    if (e < kmax) {
+      kind = 0;
+      id = row[e];
+      e = next_valid(row, e + 1, kmax, nb);
+    } else if (t < ntile) {
+      kind = 1;
+      id = t++;
+    } else {
+      kind = -1;
+    }
+  };
   TileRegs<D, BLK> regs;
-  int e = next_valid(row, 0, kmax, nb);
-  if (e < kmax) {
-    const int j = row[e];
-    load_kv<D, BLK>(regs, Kh + (size_t)j * BLK * D, Vh + (size_t)j * BLK * D, tid);
-  }
-  while (e < kmax) {
+  auto load = [&](int kind, int id) {
+    if (kind == 0)
+      load_kv<D, BLK>(regs, Kh + (size_t)id * BLK * D, Vh + (size_t)id * BLK * D, tid);
+    else
+      load_kv<D, BLK>(regs, p.pk_cen + ((size_t)bh * nbp + (size_t)id * BLK) * D,
+                      p.pk_vsum + ((size_t)bh * nbp + (size_t)id * BLK) * D, tid);
+  };
+  int kind, id;
+  next_tile(kind, id);
+  if (kind >= 0) load(kind, id);
+  while (kind >= 0) {
     __syncthreads();
     store_kv<D, BLK>(regs, Ks, Vt, tid);
     __syncthreads();
-    const int en = next_valid(row, e + 1, kmax, nb);
-    if (en < kmax) {
-      const int j = row[en];
-      load_kv<D, BLK>(regs, Kh + (size_t)j * BLK * D, Vh + (size_t)j * BLK * D, tid);
-    }
+    int kind_n, id_n;
+    next_tile(kind_n, id_n);
+    if (kind_n >= 0) load(kind_n, id_n);
+    if (kind == 0) {
 #pragma unroll
-    for (int ch = 0; ch < BLK / 64; ++ch)
-      chunk<D, BLK, false>(st, qf, Ks, Vt, ch, c2, q32, hh, bits, 0, nb);
-    e = en;
+      for (int ch = 0; ch < BLK / 64; ++ch)
+        chunk<D, BLK, false>(st, qf, Ks, Vt, ch, c2, q32, hh, bits, 0, nb);
+    } else {
+#pragma unroll
+      for (int ch = 0; ch < BLK / 64; ++ch)
+        chunk<D, BLK, true>(st, qf, Ks, Vt, ch, c2, q32, hh, bits, id * BLK, nb);
+    }
+    kind = kind_n;
+    id = id_n;
   }
 
   if (approx) {
-    // ---- stage 2: zeroth-order sweep over every block's centroid / value sum
-    const float* cen = centroid + (size_t)bh * nb * D;
-    const float* vs = vsum + (size_t)bh * nb * D;
-    for (int j0 = 0; j0 < nb; j0 += BLK) {
-      __syncthreads();
-      stage_centroids<D, BLK>(cen, vs, j0, nb, Ks, Vt, tid);
-      __syncthreads();
+    if (!packed) {
+      // ---- stage 2 from the fp32 statistics (converted while staging)
+      const float* cen = p.centroid + (size_t)bh * nb * D;
+      const float* vs = p.vsum + (size_t)bh * nb * D;
+      for (int j0 = 0; j0 < nb; j0 += BLK) {
+        __syncthreads();
+        stage_centroids<D, BLK>(cen, vs, j0, nb, Ks, Vt, tid);
+        __syncthreads();
 #pragma unroll
-      for (int ch = 0; ch < BLK / 64; ++ch)
-        chunk<D, BLK, true>(st, qf, Ks, Vt, ch, c2, q32, hh, bits, j0, nb);
+        for (int ch = 0; ch < BLK / 64; ++ch)
+          chunk<D, BLK, true>(st, qf, Ks, Vt, ch, c2, q32, hh, bits, j0, nb);
+      }
     }
     // ---- stage 3: global first-order correction, acc += scale * (q Hbar) * sum alpha
-    __syncthreads();
-    stage_hbar_t<D, BLK>(hbar + (size_t)bh * D * D, lds, tid);
-    __syncthreads();
     const float atot = st.a + __shfl_xor(st.a, 32);
     const float f = scale * atot;
+    if (packed) {
+      // A operand (Hbar^T rows) straight from the bf16 pack, two d-tiles at a time
+      const bf16* hb = p.pk_hbart + ((size_t)bh * D + q32) * D + 8 * hh;
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) {
-      f32x16 hq = f32x16{};
-      const bf16* hrow = lds + (32 * mt + q32) * C::KROW + 8 * hh;
+      for (int m0 = 0; m0 < C::MT; m0 += 2) {
+        constexpr int NM = (C::MT >= 2) ? 2 : 1;
+        u32x4 ha[NM][C::KS];
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) hq = mfma32(as_bf16x8(ld16(hrow + 16 * ks)), qf[ks], hq);
-      st.acc[mt] += f * hq;
+        for (int u = 0; u < NM; ++u)
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) ha[u][ks] = ld16(hb + (size_t)(32 * (m0 + u)) * D + 16 * ks);
+#pragma unroll
+        for (int u = 0; u < NM; ++u) {
+          f32x16 hq = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) hq = mfma32(as_bf16x8(ha[u][ks]), qf[ks], hq);
+          st.acc[m0 + u] += f * hq;
+        }
+      }
+    } else {
+      __syncthreads();
+      stage_hbar_t<D, BLK>(p.hbar + (size_t)bh * D * D, lds, tid);
+      __syncthreads();
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+        f32x16 hq = f32x16{};
+        const bf16* hrow = lds + (32 * mt + q32) * C::KROW + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) hq = mfma32(as_bf16x8(ld16(hrow + 16 * ks)), qf[ks], hq);
+        st.acc[mt] += f * hq;
+      }
     }
   }
 
   // ---- epilogue: o = N / D (0 when nothing was attended in keep-or-drop)
   const float ltot = st.l + __shfl_xor(st.l, 32);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  bf16* orow = O + ((size_t)bh * L + (size_t)i * BLK + 32 * w + q32) * D;
+  bf16* orow = p.O + ((size_t)bh * L + (size_t)i * BLK + 32 * w + q32) * D;
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const f32x16& a = st.acc[mt];
-      u32x2 p = {pack2(a[4 * g4] * inv, a[4 * g4 + 1] * inv), pack2(a[4 * g4 + 2] * inv, a[4 * g4 + 3] * inv)};
-      st8(orow + 32 * mt + 8 * g4 + 4 * hh, p);
+      u32x2 pk = {pack2(a[4 * g4] * inv, a[4 * g4 + 1] * inv), pack2(a[4 * g4 + 2] * inv, a[4 * g4 + 3] * inv)};
+      st8(orow + 32 * mt + 8 * g4 + 4 * hh, pk);
     }
 }
 
@@ -351,9 +441,13 @@ template <int D, int BLK>
 hipError_t launch_t(const AttnArgs& a) {
   using C = Cfg<D, BLK>;
   const int grid = a.bh * a.nb;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, BLK>), dim3(grid), dim3(C::NT), 0, a.stream,
-                     (const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.idx, a.kmax,
-                     a.centroid, a.vsum, a.hbar, a.approx, a.scale, (bf16*)a.O, a.nb);
+  const int nbp = (a.nb + BLK - 1) / BLK * BLK;
+  const bf16* pk = static_cast<const bf16*>(a.packed);
+  AttnPtrs p{(const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.idx, a.centroid, a.vsum,
+             a.hbar, pk, pk ? pk + (size_t)a.bh * nbp * D : nullptr,
+             pk ? pk + (size_t)2 * a.bh * nbp * D : nullptr, (bf16*)a.O};
+  hipLaunchKernelGGL((attn_bf16_kernel<D, BLK>), dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax,
+                     a.approx, a.scale, a.nb);
   return hipGetLastError();
 }
 

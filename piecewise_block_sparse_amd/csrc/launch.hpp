@@ -16,6 +16,7 @@ struct AttnArgs {
   const float* centroid;
   const float* vsum;
   const float* hbar;
+  const void* packed;   // nullable bf16 pack of the statistics
   int approx;
   float scale;
   void* O;
@@ -34,6 +35,7 @@ struct StatsArgs {
   float* H;      // nullable
   float* hbar;
   float* M;
+  void* packed;  // nullable bf16 pack of the statistics
   void* ws;
   int bh;
   int nb;
@@ -65,6 +67,7 @@ constexpr int kStatsGroup = 8;
 
 size_t stats_workspace_bf16(int bh, int nb, int D);
 size_t stats_workspace_f32(int bh, int nb, int D);
+size_t stats_packed_bytes(int bh, int nb, int D, int BLK);
 
 hipError_t launch_attn_bf16(const AttnArgs& a);
 hipError_t launch_attn_f32(const AttnArgs& a);

@@ -34,7 +34,8 @@ template <int D, int BLK, bool PASS2>
 __global__ __launch_bounds__(256) void stats_bf16_kernel(
     const bf16* __restrict__ K, const bf16* __restrict__ V, int nb, float* __restrict__ centroid,
     float* __restrict__ vsum, float* __restrict__ partial, const float* __restrict__ hbar,
-    float* __restrict__ M, float* __restrict__ Hout) {
+    float* __restrict__ M, float* __restrict__ Hout, bf16* __restrict__ pk_cen,
+    bf16* __restrict__ pk_vsum) {
   using C = SCfg<D, BLK>;
   __shared__ __attribute__((aligned(16))) bf16 Kt[D * C::ROW];
   __shared__ __attribute__((aligned(16))) bf16 Vt[D * C::ROW];
@@ -118,12 +119,19 @@ __global__ __launch_bounds__(256) void stats_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) s += (float)v[e];
       }
+      const size_t prow = ((size_t)bh * ((nb + BLK - 1) / BLK * BLK) + j) * D;
       if (tid < D) {
         s_k[tid] = s * (1.f / BLK);
-        if (!PASS2) centroid[((size_t)bh * nb + j) * D + tid] = s * (1.f / BLK);
+        if (!PASS2) {
+          centroid[((size_t)bh * nb + j) * D + tid] = s * (1.f / BLK);
+          if (pk_cen) pk_cen[prow + tid] = (bf16)(s * (1.f / BLK));
+        }
       } else {
         s_v[tid - D] = s;
-        if (!PASS2) vsum[((size_t)bh * nb + j) * D + (tid - D)] = s;
+        if (!PASS2) {
+          vsum[((size_t)bh * nb + j) * D + (tid - D)] = s;
+          if (pk_vsum) pk_vsum[prow + (tid - D)] = (bf16)s;
+        }
       }
     }
 
@@ -197,16 +205,38 @@ __global__ __launch_bounds__(256) void stats_bf16_kernel(
 }
 
 // Hbar[bh][e] = (1/nb) sum_g parts[bh][g][e], summed in fp64 in group order.
+// With a bf16 pack: also writes Hbar^T in bf16 and zeroes the padding rows
+// (nb .. nbp) of the packed centroids and value sums.
 __global__ __launch_bounds__(256) void hbar_reduce_kernel(const float* __restrict__ parts, int ngrp,
-                                                          int nb, int DD, int total,
-                                                          float* __restrict__ hbar) {
+                                                          int nb, int D, int total,
+                                                          float* __restrict__ hbar,
+                                                          bf16* __restrict__ pk_hbart,
+                                                          bf16* __restrict__ pk_cen,
+                                                          bf16* __restrict__ pk_vsum, int nbp) {
   const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= total) return;
-  const int bh = t / DD, e = t - bh * DD;
-  const float* p = parts + (size_t)bh * ngrp * DD + e;
-  double s = 0.0;
-  for (int g = 0; g < ngrp; ++g) s += (double)p[(size_t)g * DD];
-  hbar[t] = (float)(s / nb);
+  const int DD = D * D;
+  if (t < total) {
+    const int bh = t / DD, e = t - bh * DD;
+    const float* p = parts + (size_t)bh * ngrp * DD + e;
+    double s = 0.0;
+    for (int g = 0; g < ngrp; ++g) s += (double)p[(size_t)g * DD];
+    const float v = (float)(s / nb);
+    hbar[t] = v;
+    if (pk_hbart) {
+      const int a = e / D, c = e - a * D;
+      pk_hbart[(size_t)bh * DD + (size_t)c * D + a] = (bf16)v;
+    }
+  }
+  if (pk_cen && nbp > nb) {
+    const int per = (nbp - nb) * D;
+    const int npad = (total / DD) * per;
+    for (int u = t; u < npad; u += gridDim.x * 256) {
+      const int bh = u / per, r = u - bh * per;
+      const size_t o = ((size_t)bh * nbp + nb) * D + r;
+      pk_cen[o] = (bf16)0.f;
+      pk_vsum[o] = (bf16)0.f;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -282,21 +312,28 @@ __global__ __launch_bounds__(256) void frob_kernel(const float* __restrict__ Hbu
 template <int D, int BLK>
 hipError_t stats_bf16_t(const StatsArgs& a) {
   const int ngrp = (a.nb + kStatsGroup - 1) / kStatsGroup;
+  const int nbp = (a.nb + BLK - 1) / BLK * BLK;
   float* parts = static_cast<float*>(a.ws);
+  bf16* pk = static_cast<bf16*>(a.packed);
+  bf16* pk_cen = pk;
+  bf16* pk_vsum = pk ? pk + (size_t)a.bh * nbp * D : nullptr;
+  bf16* pk_hbart = pk ? pk + (size_t)2 * a.bh * nbp * D : nullptr;
   const int grid = a.bh * ngrp;
   hipLaunchKernelGGL((stats_bf16_kernel<D, BLK, false>), dim3(grid), dim3(256), 0, a.stream,
                      (const bf16*)a.K, (const bf16*)a.V, a.nb, a.centroid, a.vsum, parts,
-                     (const float*)nullptr, (float*)nullptr, (float*)nullptr);
+                     (const float*)nullptr, (float*)nullptr, (float*)nullptr, pk_cen, pk_vsum);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int total = a.bh * D * D;
   hipLaunchKernelGGL(hbar_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, a.stream,
-                     (const float*)parts, ngrp, a.nb, D * D, total, a.hbar);
+                     (const float*)parts, ngrp, a.nb, D, total, a.hbar, pk_hbart, pk_cen, pk_vsum,
+                     nbp);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((stats_bf16_kernel<D, BLK, true>), dim3(grid), dim3(256), 0, a.stream,
                      (const bf16*)a.K, (const bf16*)a.V, a.nb, (float*)nullptr, (float*)nullptr,
-                     (float*)nullptr, (const float*)a.hbar, a.M, a.H);
+                     (float*)nullptr, (const float*)a.hbar, a.M, a.H, (bf16*)nullptr,
+                     (bf16*)nullptr);
   return hipGetLastError();
 }
 
@@ -310,7 +347,8 @@ hipError_t stats_f32_t(const StatsArgs& a) {
   if (err != hipSuccess) return err;
   const int total = a.bh * D * D;
   hipLaunchKernelGGL(hbar_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, a.stream,
-                     (const float*)Hbuf, a.nb, a.nb, D * D, total, a.hbar);
+                     (const float*)Hbuf, a.nb, a.nb, D, total, a.hbar, (bf16*)nullptr,
+                     (bf16*)nullptr, (bf16*)nullptr, a.nb);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((frob_kernel<D>), dim3(grid), dim3(256), 0, a.stream, (const float*)Hbuf,
@@ -323,6 +361,11 @@ hipError_t stats_f32_t(const StatsArgs& a) {
 size_t stats_workspace_bf16(int bh, int nb, int D) {
   const size_t ngrp = (size_t)(nb + kStatsGroup - 1) / kStatsGroup;
   return (size_t)bh * ngrp * D * D * sizeof(float);
+}
+
+size_t stats_packed_bytes(int bh, int nb, int D, int BLK) {
+  const size_t nbp = (size_t)(nb + BLK - 1) / BLK * BLK;
+  return (size_t)bh * (2 * nbp * D + (size_t)D * D) * sizeof(bf16);
 }
 
 size_t stats_workspace_f32(int bh, int nb, int D) {

@@ -30,7 +30,7 @@ def shape(b=1, h=2, L=1024, d=128, B=64, dtype=_lib.DTYPE_BF16):
 
 def stats(full=True):
     p = FAKE.value
-    return _lib.PisaStats(p, p, None, p, p) if full else _lib.PisaStats(None, p, None, p, p)
+    return _lib.PisaStats(p, p, None, p, p, None) if full else _lib.PisaStats(None, p, None, p, p, None)
 
 
 def test_exports_every_declared_symbol(lib):
@@ -88,6 +88,9 @@ def test_precompute_arguments(lib):
     assert b"needs" in lib.pisa_last_error()
     f = shape(dtype=_lib.DTYPE_FP32, d=64)
     assert lib.pisa_workspace_size(ctypes.byref(f)) == 2 * 16 * 64 * 64 * 4
+    assert lib.pisa_packed_size(ctypes.byref(s)) == 2 * (2 * 64 * 128 + 128 * 128) * 2   # nbp = 64
+    assert lib.pisa_packed_size(ctypes.byref(shape(L=72 * 64))) == 2 * (2 * 128 * 128 + 128 * 128) * 2
+    assert lib.pisa_packed_size(ctypes.byref(f)) == 0
 
 
 def test_route_arguments(lib):

@@ -234,3 +234,31 @@ def test_end_to_end_routing_diagnostic(torch):
     agree = float(np.mean(np.all(idx == ref, axis=-1)))
     print(f"{w.name}: {agree:.4f} of rows identical with independent statistics")
     assert agree > 0.9
+
+
+def test_route_max_blocks(torch):
+    """nb = 2048 (the largest supported block count): routing still matches."""
+    pisa = pisa_mod()
+    B, L, d, k = 64, 2048 * 64, 128, 200
+    Q, K, V = (_rand(torch, (1, 1, L, d), "bf16", s) for s in (11, 12, 13))
+    Qd, Kd, Vd = (to_dev(x, "bf16") for x in (Q, K, V))
+    st = pisa.precompute(Kd, Vd, B)
+    idx = pisa.route(Qd, st, k, 0.02, B)
+    torch.cuda.synchronize()
+    scores = oracle.route_scores(Q, to_np(st["centroid"]), to_np(st["M"]), 0.02, B, 1 / math.sqrt(d))
+    check_route(idx.cpu().numpy(), scores, k, name="nb2048")
+
+
+@pytest.mark.parametrize("wid", [2, 5])
+def test_packed_and_fp32_statistics_paths_agree(torch, wid):
+    """PISA mode reads the bf16 statistics pack when present and converts the
+    fp32 statistics itself otherwise; both feed identical bf16 operands."""
+    pisa = pisa_mod()
+    w, Q, K, V, Qd, Kd, Vd = inputs(wid)
+    st = pisa.precompute(Kd, Vd, w.block)
+    assert st["packed"] is not None
+    idx = _idx_for(pisa, w, Qd, st)
+    a = pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode="approx")
+    b = pisa.attention(Qd, Kd, Vd, idx, dict(st, packed=None), w.block, mode="approx")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
