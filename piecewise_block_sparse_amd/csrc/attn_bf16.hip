@@ -11,153 +11,76 @@
 // Work decomposition: one workgroup per (batch*head, query block); BLK/32
 // waves, each owning 32 query rows.  Everything is computed transposed so
 // that a lane owns one query row:
-//   S^T[key][query]  = K_tile . Q^T      (A = K rows from LDS, B = Q fragments in VGPRs)
-//   O^T[d][query]   += V_tile^T . P^T    (A = V^T rows from LDS, B = P straight from S^T)
+//   S^T[key][query]  = K_chunk . Q^T      (A = K rows from LDS, B = Q fragments in VGPRs)
+//   O^T[d][query]   += V_chunk^T . P^T    (A = V read transposed from LDS, B = P from S^T)
 // The 32x32x16 result layout gives lane l the 16 keys {8(r/4) + 4(l/32) + r%4}
 // of query l%32, so the row max needs one cross-lane step (lane l ^ 32) and the
-// rescale of O^T is lane-local.  The V tile is stored transposed in LDS with
-// each 16-key slab permuted (keys 0-3, 8-11, 4-7, 12-15) so that a lane's P
-// registers feed the next MFMA's B operand without any shuffle.
+// rescale of O^T is lane-local.
+//
+// Memory pipeline: keys and values stream in chunks of CK tokens through a
+// ring of two LDS stages.  Each chunk is copied global -> LDS by the waves'
+// global_load_lds_dwordx4 (no registers, no staging ALU), row-major, with the
+// 16-byte slots of row r XOR-swizzled by swz(r) so that the K reads (16 rows,
+// one column each) and the transposing V reads (ds_read_b64_tr_b16: 4 rows x
+// 32 columns) are both free of bank conflicts.  The V read of each 4-key group
+// picks the keys that the lane's P registers hold, so P feeds the MFMA as is.
+// PISA's zeroth-order sweep streams the bf16 centroid / value-sum pack through
+// the same ring (a centroid chunk has the layout of a K / V chunk).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace pisa {
 namespace {
 
-template <int D, int BLK>
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+typedef __attribute__((address_space(3))) s16x4 ls16x4;
+
+template <int D_, int BLK_, int CK_>
 struct Cfg {
-  static constexpr int NW = BLK / 32;          // waves per workgroup
-  static constexpr int NT = 64 * NW;           // threads
-  static constexpr int KS = D / 16;            // MFMA k-steps over the head dim
-  static constexpr int MT = D / 32;            // 32-row tiles of O^T
-  static constexpr int KROW = D + 8;           // LDS row (elements) of the K tile, padded
-  static constexpr int VROW = BLK + 8;         // LDS row of the V^T tile, padded
-  static constexpr int K_ELEMS = BLK * KROW;
-  static constexpr int V_ELEMS = D * VROW;
-  static constexpr int LDS_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int K_PER_T = BLK * D / 8 / NT;        // 16-byte K chunks per thread
-  static constexpr int VSUB = (BLK / 8) * (D / 8);        // 8x8 sub-tiles of V
-  static_assert(BLK * D / 8 % NT == 0, "K tile split");
-  static_assert(VSUB <= NT, "one V sub-tile per thread");
-  static_assert(D * KROW <= LDS_ELEMS, "Hbar^T fits in the tile buffers");
+  static constexpr int D = D_, BLK = BLK_, CK = CK_;
+  static constexpr int NW = BLK / 32;            // waves per workgroup
+  static constexpr int NT = 64 * NW;             // threads
+  static constexpr int RB = 2 * D;               // bytes per row
+  static constexpr int CPR = D / 8;              // 16-byte slots per row
+  static constexpr int SUBB = CK * RB;           // bytes of one K (or V) chunk
+  static constexpr int STB = 2 * SUBB;           // bytes of one stage: K chunk, then V chunk
+  static constexpr int LDSB = 2 * STB;           // two stages (separate arrays)
+  static constexpr int KS = D / 16;              // MFMA k-steps over the head dim
+  static constexpr int MT = D / 32;              // 32-row tiles of O^T
+  static constexpr int NKT = CK / 32;            // S^T tiles per chunk
+  static constexpr int NSL = CK / 16;            // 16-key slabs per chunk
+  static constexpr int NDMA = STB / 1024;        // 1 KB wave copies per stage
+  static constexpr int DPW = NDMA / NW;          // ... per wave
+  static constexpr int RPD = 1024 / RB;          // rows per 1 KB copy
+  static_assert(NDMA % NW == 0, "copies split evenly over waves");
+  static_assert(D * RB <= LDSB && (D / 2) * RB <= STB, "Hbar^T (fallback) halves fit the stages");
+  static_assert(BLK % CK == 0 && CK % 32 == 0, "chunking");
 };
 
-// physical slot (0..15) inside a 16-key slab of V^T holding logical key e of
-// a thread's 8-key group h2: groups are {4 h2 + 0..3, 8 + 4 h2 + 0..3}
-__device__ __forceinline__ int slab_key(int h2, int e) {
-  return (e < 4) ? (4 * h2 + e) : (8 + 4 * h2 + (e - 4));
+// 16-byte slot of logical column chunk c in row r is c ^ swz(r).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return (D == 128) ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
 }
 
-template <int D, int BLK>
-struct TileRegs {
-  u32x4 k[Cfg<D, BLK>::K_PER_T];
-  u32x4 v[8];
-};
-
-// global -> registers: one KV block (BLK tokens) of one head
-template <int D, int BLK>
-__device__ __forceinline__ void load_kv(TileRegs<D, BLK>& t, const bf16* Kb, const bf16* Vb, int tid) {
-  using C = Cfg<D, BLK>;
+// Copy one CK-row K chunk and V chunk (row stride D) into a stage.
+template <class C>
+__device__ __forceinline__ void dma_stage(const bf16* gK, const bf16* gV, char* stage, int w,
+                                          int lane) {
 #pragma unroll
-  for (int u = 0; u < C::K_PER_T; ++u) {
-    const int q = tid + u * C::NT;
-    const int r = q / (D / 8), c = q % (D / 8);
-    t.k[u] = ld16(Kb + r * D + c * 8);
-  }
-  if (tid < C::VSUB) {
-    const int g = tid % (BLK / 8), c = tid / (BLK / 8);
-    const int s = g >> 1, h2 = g & 1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t.v[e] = ld16(Vb + (16 * s + slab_key(h2, e)) * D + c * 8);
+  for (int u = 0; u < C::DPW; ++u) {
+    const int n = w + C::NW * u;                           // 1 KB block of the stage
+    const bool isv = n >= C::NDMA / 2;
+    const int r = (isv ? n - C::NDMA / 2 : n) * C::RPD + lane / C::CPR;
+    const int c = (lane % C::CPR) ^ swz<C::D>(r);
+    const bf16* src = (isv ? gV : gK) + r * C::D + 8 * c;
+    __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(stage + n * 1024), 16, 0, 0);
   }
 }
 
-// registers -> LDS: K row-major, V transposed with permuted slabs
-template <int D, int BLK>
-__device__ __forceinline__ void store_kv(const TileRegs<D, BLK>& t, bf16* Ks, bf16* Vt, int tid) {
-  using C = Cfg<D, BLK>;
-#pragma unroll
-  for (int u = 0; u < C::K_PER_T; ++u) {
-    const int q = tid + u * C::NT;
-    const int r = q / (D / 8), c = q % (D / 8);
-    st16(Ks + r * C::KROW + c * 8, t.k[u]);
-  }
-  if (tid < C::VSUB) {
-    const int g = tid % (BLK / 8), c = tid / (BLK / 8);
-    const int s = g >> 1, h2 = g & 1;
-    u32x4 col[8];
-    transpose8x8(t.v, col);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st16(Vt + (8 * c + i) * C::VROW + 16 * s + 8 * h2, col[i]);
-  }
-}
-
-// fp32 centroid / value-sum tile (BLK consecutive blocks starting at j0) ->
-// bf16 LDS in the same layouts as a KV tile; rows past nb are zero.
-template <int D, int BLK>
-__device__ __forceinline__ void stage_centroids(const float* cen, const float* vs, int j0, int nb,
-                                                bf16* Ks, bf16* Vt, int tid) {
-  using C = Cfg<D, BLK>;
-  for (int q = tid; q < BLK * (D / 4); q += C::NT) {
-    const int r = q / (D / 4), c4 = q % (D / 4);
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (j0 + r < nb) v = *reinterpret_cast<const f32x4*>(cen + (size_t)(j0 + r) * D + c4 * 4);
-    u32x2 p = {pack2(v[0], v[1]), pack2(v[2], v[3])};
-    st8(Ks + r * C::KROW + c4 * 4, p);
-  }
-  for (int p = tid; p < C::VSUB; p += C::NT) {
-    const int g = p % (BLK / 8), c = p / (BLK / 8);
-    const int s = g >> 1, h2 = g & 1;
-    f32x4 lo[8], hi[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int r = j0 + 16 * s + slab_key(h2, e);
-      if (r < nb) {
-        lo[e] = *reinterpret_cast<const f32x4*>(vs + (size_t)r * D + 8 * c);
-        hi[e] = *reinterpret_cast<const f32x4*>(vs + (size_t)r * D + 8 * c + 4);
-      } else {
-        lo[e] = hi[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x4 col;
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        const float a = (i < 4) ? lo[2 * q2][i] : hi[2 * q2][i - 4];
-        const float b = (i < 4) ? lo[2 * q2 + 1][i] : hi[2 * q2 + 1][i - 4];
-        col[q2] = pack2(a, b);
-      }
-      st16(Vt + (8 * c + i) * C::VROW + 16 * s + 8 * h2, col);
-    }
-  }
-}
-
-// Hbar [d_k][d_v] fp32 -> LDS Hbar^T [d_v][d_k] bf16, row stride KROW
-template <int D, int BLK>
-__device__ __forceinline__ void stage_hbar_t(const float* hb, bf16* Ht, int tid) {
-  using C = Cfg<D, BLK>;
-  for (int p = tid; p < (D / 8) * (D / 8); p += C::NT) {
-    const int g = p % (D / 8), c = p / (D / 8);   // rows 8g.., cols 8c..
-    f32x4 lo[8], hi[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lo[e] = *reinterpret_cast<const f32x4*>(hb + (size_t)(8 * g + e) * D + 8 * c);
-      hi[e] = *reinterpret_cast<const f32x4*>(hb + (size_t)(8 * g + e) * D + 8 * c + 4);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x4 col;
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        const float a = (i < 4) ? lo[2 * q2][i] : hi[2 * q2][i - 4];
-        const float b = (i < 4) ? lo[2 * q2 + 1][i] : hi[2 * q2 + 1][i - 4];
-        col[q2] = pack2(a, b);
-      }
-      st16(Ht + (8 * c + i) * C::KROW + 8 * g, col);
-    }
-  }
-}
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Online-softmax state of one lane (one query row, half of each key tile).
 template <int D>
@@ -173,16 +96,44 @@ struct RowState {
 // Any m gives the same N / D, so this only saves rescales of acc.
 constexpr float kTau = 8.f;
 
-// exp2 weights of one 64-key chunk -> bf16 MFMA B operands (pf) and the sum of
-// the same bf16-rounded weights.  Each pair is packed into its own 32-bit value
-// and summed from that value with v_dot2 against (1, 1) before the four pairs
-// of a slab are assembled into the 128-bit operand.
-__device__ __forceinline__ float weights_bf16(const f32x16 (&s)[2], float c2, float nm,
-                                              u32x4 (&pf)[4]) {
+// Per-lane LDS byte offsets, fixed for the whole kernel:
+//   koff[ks]       K row 32 kt + q32 (kt added as an immediate), columns 16 ks + 8 hh ..
+//   voff[mt][h]    transposing V read of 4 keys (slab base added as an immediate)
+template <class C>
+struct Offsets {
+  int koff[C::KS];
+  int voff[C::MT][2];
+};
+
+template <class C>
+__device__ __forceinline__ Offsets<C> make_offsets(int lane) {
+  Offsets<C> o;
+  const int q32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+    o.koff[ks] = q32 * C::RB + (((2 * ks + hh) ^ swz<C::D>(q32)) << 4);
+  const int j = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 4 * hh + 8 * h + (j >> 2);
+      const int chunk = (32 * mt + 16 * (g & 1)) / 8 + ((j & 3) >> 1);
+      o.voff[mt][h] = row * C::RB + ((chunk ^ swz<C::D>(row)) << 4) + 8 * (j & 1);
+    }
+  return o;
+}
+
+// exp2 weights -> bf16 MFMA B operands, and the sum of the same bf16 weights.
+// Each pair is packed into its own 32-bit value and summed from that value
+// with v_dot2 against (1, 1).
+template <int NKT>
+__device__ __forceinline__ float weights_bf16(const f32x16 (&s)[NKT], float c2, float nm,
+                                              u32x4 (&pf)[2 * NKT]) {
   const bf16x2 one = {(bf16)1.f, (bf16)1.f};
   float sum = 0.f;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+  for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const float p0 = fast_exp2(fmaf(s[kt][2 * q], c2, nm));
@@ -194,37 +145,34 @@ __device__ __forceinline__ float weights_bf16(const f32x16 (&s)[2], float c2, fl
   return sum;
 }
 
-// One 64-key chunk of the LDS tile: S^T, softmax update, O^T += V^T P^T.
+// One CK-key chunk from a stage: S^T, softmax update, O^T += V^T P^T.
 // STAGE2: the keys are block centroids (values = block value sums); entries
-// whose block is in S_i or past nb are masked, and each weight counts `block`
-// times in the denominator.  The denominator sums the same bf16-rounded
-// weights that the MFMA multiplies into the numerator.
-template <int D, int BLK, bool STAGE2>
-__device__ __forceinline__ void chunk(RowState<D>& st, const bf16x8 (&qf)[D / 16], const bf16* Ks,
-                                      const bf16* Vt, int ch, float c2, int q32, int hh,
-                                      const unsigned* bits, int jbase, int nb) {
-  using C = Cfg<D, BLK>;
-  f32x16 s[2];
+// whose block is in S_i or is padding (bit set in `bits`) are masked, and each
+// weight counts BLK times in the denominator.
+template <class C, bool STAGE2>
+__device__ __forceinline__ void chunk(RowState<C::D>& st, const bf16x8 (&qf)[C::KS],
+                                      const char* stage, const Offsets<C>& off, float c2, int hh,
+                                      const unsigned* bits, int jbase) {
+  f32x16 s[C::NKT];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < C::NKT; ++kt) {
     s[kt] = f32x16{};
-    const bf16* krow = Ks + (64 * ch + 32 * kt + q32) * C::KROW + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) s[kt] = mfma32(as_bf16x8(ld16(krow + 16 * ks)), qf[ks], s[kt]);
+    for (int ks = 0; ks < C::KS; ++ks)
+      s[kt] = mfma32(as_bf16x8(ld16(stage + kt * 32 * C::RB + off.koff[ks])), qf[ks], s[kt]);
   }
   if (STAGE2) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < C::NKT; ++kt) {
+      const unsigned wbits = bits[(jbase >> 5) + kt] >> (4 * hh);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = jbase + 64 * ch + 32 * kt + 8 * (r / 4) + 4 * hh + (r % 4);
-        const bool masked = (j >= nb) || ((bits[j >> 5] >> (j & 31)) & 1u);
-        s[kt][r] = masked ? -INFINITY : s[kt][r];
-      }
+      for (int r = 0; r < 16; ++r)
+        if ((wbits >> (8 * (r / 4) + (r % 4))) & 1u) s[kt][r] = -INFINITY;
+    }
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+  for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
   mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
@@ -237,21 +185,27 @@ __device__ __forceinline__ void chunk(RowState<D>& st, const bf16x8 (&qf)[D / 16
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt) st.acc[mt] *= corr;
   }
-  u32x4 pf[4];
-  const float ps = weights_bf16(s, c2, -st.m, pf);
+  u32x4 pf[C::NSL];
+  const float ps = weights_bf16<C::NKT>(s, c2, -st.m, pf);
   if (STAGE2) {
-    st.l += (float)BLK * ps;
+    st.l += (float)C::BLK * ps;
     st.a += ps;
   } else {
     st.l += ps;
   }
+  const char* vst = stage + C::SUBB;
 #pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt) {
-    const bf16* vrow = Vt + (32 * mt + q32) * C::VROW + 64 * ch + 8 * hh;
+  for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl)
-      st.acc[mt] = mfma32(as_bf16x8(ld16(vrow + 16 * sl)), as_bf16x8(pf[sl]), st.acc[mt]);
-  }
+    for (int sl = 0; sl < C::NSL; ++sl) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (ls16x4*)(vst + sl * 16 * C::RB + off.voff[mt][0]));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (ls16x4*)(vst + sl * 16 * C::RB + off.voff[mt][1]));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
+      st.acc[mt] = mfma32(as_bf16x8(a), as_bf16x8(pf[sl]), st.acc[mt]);
+    }
 }
 
 __device__ __forceinline__ int next_valid(const int32_t* row, int e, int kmax, int nb) {
@@ -261,6 +215,42 @@ __device__ __forceinline__ int next_valid(const int32_t* row, int e, int kmax, i
     ++e;
   }
   return e;
+}
+
+// fp32 statistics -> bf16 chunk of CK centroids / value sums in the stage
+// layout (used when no bf16 pack was supplied); rows past nb are zero.
+template <class C>
+__device__ __forceinline__ void stage_centroids(const float* cen, const float* vs, int j0, int nb,
+                                                char* stage, int tid) {
+  for (int q = tid; q < 2 * C::CK * C::CPR; q += C::NT) {
+    const bool isv = q >= C::CK * C::CPR;
+    const int qq = isv ? q - C::CK * C::CPR : q;
+    const int r = qq / C::CPR, c = qq % C::CPR;
+    const float* src = (isv ? vs : cen) + (size_t)(j0 + r) * C::D + 8 * c;
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
+    if (j0 + r < nb) {
+      lo = *reinterpret_cast<const f32x4*>(src);
+      hi = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+    const u32x4 v = {pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(hi[0], hi[1]), pack2(hi[2], hi[3])};
+    st16(stage + (isv ? C::SUBB : 0) + r * C::RB + ((c ^ swz<C::D>(r)) << 4), v);
+  }
+}
+
+// fp32 Hbar [d_k][d_v] -> bf16 Hbar^T [d_v][d_k] rows in the K layout; rows
+// below D/2 go to stage 0, the others to stage 1
+template <class C>
+__device__ __forceinline__ void stage_hbar_t(const float* hb, char* s0, char* s1, int tid) {
+  for (int q = tid; q < C::D * C::CPR; q += C::NT) {
+    const int r = q / C::CPR, c = q % C::CPR;   // row = d_v, columns d_k = 8c .. 8c+7
+    unsigned w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = pack2(hb[(size_t)(8 * c + 2 * e) * C::D + r], hb[(size_t)(8 * c + 2 * e + 1) * C::D + r]);
+    const u32x4 v = {w[0], w[1], w[2], w[3]};
+    char* dst = (r < C::D / 2) ? s0 + r * C::RB : s1 + (r - C::D / 2) * C::RB;
+    st16(dst + ((c ^ swz<C::D>(r)) << 4), v);
+  }
 }
 
 // Kernel arguments: fp32 statistics, plus (optionally) their bf16 packs written
@@ -280,14 +270,17 @@ struct AttnPtrs {
   bf16* O;
 };
 
-template <int D, int BLK>
-__global__ __launch_bounds__(2 * BLK) void attn_bf16_kernel(AttnPtrs p, int kmax, int approx,
-                                                            float scale, int nb) {
-  using C = Cfg<D, BLK>;
-  __shared__ __attribute__((aligned(16))) bf16 lds[C::LDS_ELEMS];
-  __shared__ unsigned bits[kMaxBlocks / 32];
-  bf16* Ks = lds;
-  bf16* Vt = lds + C::K_ELEMS;
+constexpr int kBitWords = (kMaxBlocks + 128) / 32;
+
+template <class C>
+__global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kmax, int approx,
+                                                             float scale, int nb) {
+  constexpr int D = C::D, BLK = C::BLK, CK = C::CK;
+  // the two ring stages are separate objects, so the compiler can tell a copy
+  // into one stage from reads of the other and does not wait on the copy
+  __shared__ __attribute__((aligned(1024))) char stg0[C::STB];
+  __shared__ __attribute__((aligned(1024))) char stg1[C::STB];
+  __shared__ unsigned bits[kBitWords];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q32 = lane & 31, hh = lane >> 5;
@@ -301,12 +294,19 @@ __global__ __launch_bounds__(2 * BLK) void attn_bf16_kernel(AttnPtrs p, int kmax
   const bool packed = approx && p.pk_cen != nullptr;
 
   if (approx) {
-    for (int e = tid; e < (nb + 31) / 32; e += C::NT) bits[e] = 0u;
+    // bit j set: block j is exact (in S_i) or padding (j >= nb)
+    for (int e = tid; e < nbp / 32; e += C::NT) {
+      const int lo = 32 * e;
+      unsigned pad = 0u;
+      if (lo + 32 > nb) pad = (lo >= nb) ? ~0u : (~0u << (nb - lo));
+      bits[e] = pad;
+    }
     __syncthreads();
     for (int e = tid; e < kmax; e += C::NT) {
       const int j = row[e];
       if (j >= 0 && j < nb) atomicOr(&bits[j >> 5], 1u << (j & 31));
     }
+    __syncthreads();
   }
 
   // this lane's query row as 16-byte B-operand fragments (d = 16 ks + 8 hh + 0..7)
@@ -316,6 +316,7 @@ __global__ __launch_bounds__(2 * BLK) void attn_bf16_kernel(AttnPtrs p, int kmax
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_bf16x8(ld16(qrow + 16 * ks));
   }
+  const Offsets<C> off = make_offsets<C>(lane);
   RowState<D> st;
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) st.acc[mt] = f32x16{};
@@ -324,52 +325,65 @@ __global__ __launch_bounds__(2 * BLK) void attn_bf16_kernel(AttnPtrs p, int kmax
   st.a = 0.f;
   const float c2 = scale * kLog2e;
 
-  // ---- stages 1 and 2 as one register-prefetched stream of tiles: the exact
-  // blocks of S_i, then (PISA mode, packed statistics) the centroid / value-sum
-  // tiles, which have exactly the layout of a K / V block.
-  const int ntile = packed ? nbp / BLK : 0;
-  int e = next_valid(row, 0, kmax, nb), t = 0;
-  auto next_tile = [&](int& kind, int& id) {
+  // ---- the chunk stream: CK-token chunks of the exact blocks of S_i, then (PISA
+  // mode with a pack) the chunks of CK centroids that hold any unselected block.
+  const int nctile = packed ? nbp / CK : 0;
+  int e = next_valid(row, 0, kmax, nb), sub = 0, tc = 0;
+  auto next_chunk = [&](int& kind, const bf16*& gk, const bf16*& gv, int& jbase) {
     if (e < kmax) {
+      const int j = row[e];
       kind = 0;
-      id = row[e];
-      e = next_valid(row, e + 1, kmax, nb);
-    } else if (t < ntile) {
+      gk = Kh + ((size_t)j * BLK + (size_t)sub * CK) * D;
+      gv = Vh + ((size_t)j * BLK + (size_t)sub * CK) * D;
+      if (++sub == BLK / CK) {
+        sub = 0;
+        e = next_valid(row, e + 1, kmax, nb);
+      }
+      return;
+    }
+    while (tc < nctile) {
+      bool all = true;
+#pragma unroll
+      for (int u = 0; u < CK / 32; ++u) all = all && (bits[tc * (CK / 32) + u] == ~0u);
+      if (!all) break;
+      ++tc;
+    }
+    if (tc < nctile) {
       kind = 1;
-      id = t++;
-    } else {
-      kind = -1;
+      jbase = tc * CK;
+      gk = p.pk_cen + ((size_t)bh * nbp + jbase) * D;
+      gv = p.pk_vsum + ((size_t)bh * nbp + jbase) * D;
+      ++tc;
+      return;
     }
+    kind = -1;
   };
-  TileRegs<D, BLK> regs;
-  auto load = [&](int kind, int id) {
-    if (kind == 0)
-      load_kv<D, BLK>(regs, Kh + (size_t)id * BLK * D, Vh + (size_t)id * BLK * D, tid);
-    else
-      load_kv<D, BLK>(regs, p.pk_cen + ((size_t)bh * nbp + (size_t)id * BLK) * D,
-                      p.pk_vsum + ((size_t)bh * nbp + (size_t)id * BLK) * D, tid);
-  };
-  int kind, id;
-  next_tile(kind, id);
-  if (kind >= 0) load(kind, id);
+
+  int kind, jb = 0;
+  const bf16 *gk, *gv;
+  next_chunk(kind, gk, gv, jb);
+  if (kind >= 0) dma_stage<C>(gk, gv, stg0, w, lane);
+  // ring of two stages, unrolled so every LDS access names its stage statically
   while (kind >= 0) {
-    __syncthreads();
-    store_kv<D, BLK>(regs, Ks, Vt, tid);
-    __syncthreads();
-    int kind_n, id_n;
-    next_tile(kind_n, id_n);
-    if (kind_n >= 0) load(kind_n, id_n);
-    if (kind == 0) {
 #pragma unroll
-      for (int ch = 0; ch < BLK / 64; ++ch)
-        chunk<D, BLK, false>(st, qf, Ks, Vt, ch, c2, q32, hh, bits, 0, nb);
-    } else {
-#pragma unroll
-      for (int ch = 0; ch < BLK / 64; ++ch)
-        chunk<D, BLK, true>(st, qf, Ks, Vt, ch, c2, q32, hh, bits, id * BLK, nb);
+    for (int sidx = 0; sidx < 2; ++sidx) {
+      if (kind >= 0) {
+        char* cur = sidx ? stg1 : stg0;
+        char* nxt = sidx ? stg0 : stg1;
+        wait_vm0();
+        __syncthreads();
+        int kind_n, jb_n = 0;
+        const bf16 *gk_n, *gv_n;
+        next_chunk(kind_n, gk_n, gv_n, jb_n);
+        if (kind_n >= 0) dma_stage<C>(gk_n, gv_n, nxt, w, lane);
+        if (kind == 0)
+          chunk<C, false>(st, qf, cur, off, c2, hh, bits, 0);
+        else
+          chunk<C, true>(st, qf, cur, off, c2, hh, bits, jb);
+        kind = kind_n;
+        jb = jb_n;
+      }
     }
-    kind = kind_n;
-    id = id_n;
   }
 
   if (approx) {
@@ -377,13 +391,11 @@ __global__ __launch_bounds__(2 * BLK) void attn_bf16_kernel(AttnPtrs p, int kmax
       // ---- stage 2 from the fp32 statistics (converted while staging)
       const float* cen = p.centroid + (size_t)bh * nb * D;
       const float* vs = p.vsum + (size_t)bh * nb * D;
-      for (int j0 = 0; j0 < nb; j0 += BLK) {
+      for (int j0 = 0; j0 < nbp; j0 += CK) {
         __syncthreads();
-        stage_centroids<D, BLK>(cen, vs, j0, nb, Ks, Vt, tid);
+        stage_centroids<C>(cen, vs, j0, nb, stg0, tid);
         __syncthreads();
-#pragma unroll
-        for (int ch = 0; ch < BLK / 64; ++ch)
-          chunk<D, BLK, true>(st, qf, Ks, Vt, ch, c2, q32, hh, bits, j0, nb);
+        chunk<C, true>(st, qf, stg0, off, c2, hh, bits, j0);
       }
     }
     // ---- stage 3: global first-order correction, acc += scale * (q Hbar) * sum alpha
@@ -394,14 +406,13 @@ __global__ __launch_bounds__(2 * BLK) void attn_bf16_kernel(AttnPtrs p, int kmax
       const bf16* hb = p.pk_hbart + ((size_t)bh * D + q32) * D + 8 * hh;
 #pragma unroll
       for (int m0 = 0; m0 < C::MT; m0 += 2) {
-        constexpr int NM = (C::MT >= 2) ? 2 : 1;
-        u32x4 ha[NM][C::KS];
+        u32x4 ha[2][C::KS];
 #pragma unroll
-        for (int u = 0; u < NM; ++u)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int ks = 0; ks < C::KS; ++ks) ha[u][ks] = ld16(hb + (size_t)(32 * (m0 + u)) * D + 16 * ks);
 #pragma unroll
-        for (int u = 0; u < NM; ++u) {
+        for (int u = 0; u < 2; ++u) {
           f32x16 hq = f32x16{};
 #pragma unroll
           for (int ks = 0; ks < C::KS; ++ks) hq = mfma32(as_bf16x8(ha[u][ks]), qf[ks], hq);
@@ -410,14 +421,14 @@ __global__ __launch_bounds__(2 * BLK) void attn_bf16_kernel(AttnPtrs p, int kmax
       }
     } else {
       __syncthreads();
-      stage_hbar_t<D, BLK>(p.hbar + (size_t)bh * D * D, lds, tid);
+      stage_hbar_t<C>(p.hbar + (size_t)bh * D * D, stg0, stg1, tid);
       __syncthreads();
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) {
         f32x16 hq = f32x16{};
-        const bf16* hrow = lds + (32 * mt + q32) * C::KROW + 8 * hh;
+        const char* base = (mt < C::MT / 2) ? stg0 + 32 * mt * C::RB : stg1 + 32 * (mt - C::MT / 2) * C::RB;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) hq = mfma32(as_bf16x8(ld16(hrow + 16 * ks)), qf[ks], hq);
+        for (int ks = 0; ks < C::KS; ++ks) hq = mfma32(as_bf16x8(ld16(base + off.koff[ks])), qf[ks], hq);
         st.acc[mt] += f * hq;
       }
     }
@@ -437,16 +448,15 @@ __global__ __launch_bounds__(2 * BLK) void attn_bf16_kernel(AttnPtrs p, int kmax
     }
 }
 
-template <int D, int BLK>
+template <class C>
 hipError_t launch_t(const AttnArgs& a) {
-  using C = Cfg<D, BLK>;
   const int grid = a.bh * a.nb;
-  const int nbp = (a.nb + BLK - 1) / BLK * BLK;
+  const int nbp = (a.nb + C::BLK - 1) / C::BLK * C::BLK;
   const bf16* pk = static_cast<const bf16*>(a.packed);
   AttnPtrs p{(const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.idx, a.centroid, a.vsum,
-             a.hbar, pk, pk ? pk + (size_t)a.bh * nbp * D : nullptr,
-             pk ? pk + (size_t)2 * a.bh * nbp * D : nullptr, (bf16*)a.O};
-  hipLaunchKernelGGL((attn_bf16_kernel<D, BLK>), dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax,
+             a.hbar, pk, pk ? pk + (size_t)a.bh * nbp * C::D : nullptr,
+             pk ? pk + (size_t)2 * a.bh * nbp * C::D : nullptr, (bf16*)a.O};
+  hipLaunchKernelGGL((attn_bf16_kernel<C>), dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax,
                      a.approx, a.scale, a.nb);
   return hipGetLastError();
 }
@@ -454,10 +464,10 @@ hipError_t launch_t(const AttnArgs& a) {
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a) {
-  if (a.D == 128 && a.BLK == 64) return launch_t<128, 64>(a);
-  if (a.D == 128 && a.BLK == 128) return launch_t<128, 128>(a);
-  if (a.D == 64 && a.BLK == 64) return launch_t<64, 64>(a);
-  if (a.D == 64 && a.BLK == 128) return launch_t<64, 128>(a);
+  if (a.D == 128 && a.BLK == 64) return launch_t<Cfg<128, 64, 32>>(a);
+  if (a.D == 128 && a.BLK == 128) return launch_t<Cfg<128, 128, 64>>(a);
+  if (a.D == 64 && a.BLK == 64) return launch_t<Cfg<64, 64, 32>>(a);
+  if (a.D == 64 && a.BLK == 128) return launch_t<Cfg<64, 128, 64>>(a);
   return hipErrorInvalidValue;
 }
 
