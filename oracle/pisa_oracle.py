@@ -28,8 +28,7 @@ Functions, one per call of the C ABI:
   (``route_scores`` exposes the float64 scores it ranks)
 * ``attention(Q, K, V, idx, centroid, vsum, Hbar, mode, scale, B)`` -> O
 
-Readings where the pages are silent or ambiguous (each is also listed with the
-design notes of the repository):
+Readings where the pages are silent or ambiguous:
 
 * Softmax scale: the PISA numerator is printed without a scale, the keep-or-drop
   formula divides by sqrt(d).  Reading: every q_t is pre-multiplied by
