@@ -46,7 +46,7 @@ struct Cfg {
   static constexpr int CPR = D / 8;              // 16-byte slots per row
   static constexpr int SUBB = CK * RB;           // bytes of one K (or V) chunk
   static constexpr int STB = 2 * SUBB;           // bytes of one stage: K chunk, then V chunk
-  static constexpr int LDSB = 2 * STB;           // two stages (separate arrays)
+  static constexpr int LDSB = 2 * STB;           // two stages
   static constexpr int KS = D / 16;              // MFMA k-steps over the head dim
   static constexpr int MT = D / 32;              // 32-row tiles of O^T
   static constexpr int NKT = CK / 32;            // S^T tiles per chunk
@@ -55,6 +55,9 @@ struct Cfg {
   static constexpr int DPW = NDMA / NW;          // ... per wave
   static constexpr int RPD = 1024 / RB;          // rows per 1 KB copy
   static_assert(NDMA % NW == 0, "copies split evenly over waves");
+  static constexpr int NPH = ((NW * RPD) % 16 == 0) ? 1 : 16 / (NW * RPD);  // swizzle phases
+  static_assert(DPW % 2 == 0 && (NW * RPD * NPH) % 16 == 0 && (DPW / 2) % NPH == 0,
+                "per-wave copies: half K, half V, whole swizzle periods");
   static_assert(D * RB <= LDSB && (D / 2) * RB <= STB, "Hbar^T (fallback) halves fit the stages");
   static_assert(BLK % CK == 0 && CK % 32 == 0, "chunking");
 };
@@ -65,18 +68,54 @@ __device__ __forceinline__ int swz(int r) {
   return (D == 128) ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
 }
 
-// Copy one CK-row K chunk and V chunk (row stride D) into a stage.
+// One global_load_lds_dwordx4: lane l copies 16 bytes from src into LDS at
+// lds_dst + 16 l (lds_dst is wave-uniform, passed in M0).  Issued from asm so
+// the compiler does not track the copy: it neither orders later LDS reads of
+// the other ring stage behind it nor waits on it; every use of a stage is
+// preceded by wait_vm0() and a workgroup barrier instead.  The instruction has
+// no register result.
+__device__ __forceinline__ void dma16(const void* src, char* lds_dst) {
+  const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lvoid*)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0v), "v"(src)
+               : "memory", "m0");
+}
+
+// Copy one CK-row K chunk and V chunk (row stride D) into a stage.  Copy n
+// (wave w issues n = w, w + NW, ...) fills LDS bytes [1024 n, 1024 n + 1024) of
+// the stage: rows RPD n .. RPD n + RPD - 1 of the K chunk (n < NDMA/2) or of the
+// V chunk, lane l writing slot l % CPR of row RPD n + l / CPR.  The slot holds
+// logical column chunk (l % CPR) ^ swz(row).  swz has period 16 in the row, so a
+// lane's source offset within a copy takes only NPH values over its copies
+// (kept in registers); copy u adds a constant.
+template <class C>
+struct DmaOff {
+  int v[C::NPH];
+};
+
+template <class C>
+__device__ __forceinline__ DmaOff<C> dma_lane_offsets(int w, int lane) {
+  DmaOff<C> o;
+#pragma unroll
+  for (int ph = 0; ph < C::NPH; ++ph) {
+    const int r = (w + C::NW * ph) * C::RPD + lane / C::CPR;
+    o.v[ph] = (lane / C::CPR) * C::D + 8 * ((lane % C::CPR) ^ swz<C::D>(r));
+  }
+  return o;
+}
+
 template <class C>
 __device__ __forceinline__ void dma_stage(const bf16* gK, const bf16* gV, char* stage, int w,
-                                          int lane) {
+                                          const DmaOff<C>& loff) {
+  constexpr int half = C::DPW / 2;                       // copies of the K chunk per wave
 #pragma unroll
   for (int u = 0; u < C::DPW; ++u) {
-    const int n = w + C::NW * u;                           // 1 KB block of the stage
-    const bool isv = n >= C::NDMA / 2;
-    const int r = (isv ? n - C::NDMA / 2 : n) * C::RPD + lane / C::CPR;
-    const int c = (lane % C::CPR) ^ swz<C::D>(r);
-    const bf16* src = (isv ? gV : gK) + r * C::D + 8 * c;
-    __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(stage + n * 1024), 16, 0, 0);
+    const bool isv = u >= half;
+    const int uu = isv ? u - half : u;
+    const int n = w + C::NW * u;
+    const bf16* src = (isv ? gV : gK) + (w + C::NW * uu) * C::RPD * C::D + loff.v[uu % C::NPH];
+    dma16(src, stage + n * 1024);
   }
 }
 
@@ -276,10 +315,7 @@ template <class C>
 __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kmax, int approx,
                                                              float scale, int nb) {
   constexpr int D = C::D, BLK = C::BLK, CK = C::CK;
-  // the two ring stages are separate objects, so the compiler can tell a copy
-  // into one stage from reads of the other and does not wait on the copy
-  __shared__ __attribute__((aligned(1024))) char stg0[C::STB];
-  __shared__ __attribute__((aligned(1024))) char stg1[C::STB];
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDSB];
   __shared__ unsigned bits[kBitWords];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -317,6 +353,7 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
     for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_bf16x8(ld16(qrow + 16 * ks));
   }
   const Offsets<C> off = make_offsets<C>(lane);
+  const DmaOff<C> loff = dma_lane_offsets<C>(w, lane);
   RowState<D> st;
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) st.acc[mt] = f32x16{};
@@ -359,31 +396,34 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
     kind = -1;
   };
 
-  int kind, jb = 0;
+  // two-stage ring: chunk t lives in stage t & 1; the copy of chunk t + 1 is
+  // issued right after the barrier that publishes chunk t
+  int kind, jb = 0, t = 0;
   const bf16 *gk, *gv;
   next_chunk(kind, gk, gv, jb);
-  if (kind >= 0) dma_stage<C>(gk, gv, stg0, w, lane);
-  // ring of two stages, unrolled so every LDS access names its stage statically
-  while (kind >= 0) {
-#pragma unroll
-    for (int sidx = 0; sidx < 2; ++sidx) {
-      if (kind >= 0) {
-        char* cur = sidx ? stg1 : stg0;
-        char* nxt = sidx ? stg0 : stg1;
-        wait_vm0();
-        __syncthreads();
-        int kind_n, jb_n = 0;
-        const bf16 *gk_n, *gv_n;
-        next_chunk(kind_n, gk_n, gv_n, jb_n);
-        if (kind_n >= 0) dma_stage<C>(gk_n, gv_n, nxt, w, lane);
-        if (kind == 0)
-          chunk<C, false>(st, qf, cur, off, c2, hh, bits, 0);
-        else
-          chunk<C, true>(st, qf, cur, off, c2, hh, bits, jb);
-        kind = kind_n;
-        jb = jb_n;
-      }
-    }
+  if (kind >= 0) dma_stage<C>(gk, gv, lds, w, loff);
+  auto advance = [&](char* cur) {
+    wait_vm0();
+    __syncthreads();
+    int kind_n, jb_n = 0;
+    const bf16 *gk_n, *gv_n;
+    next_chunk(kind_n, gk_n, gv_n, jb_n);
+    if (kind_n >= 0) dma_stage<C>(gk_n, gv_n, lds + ((t + 1) & 1) * C::STB, w, loff);
+    const int jcur = jb;
+    kind = kind_n;
+    jb = jb_n;
+    ++t;
+    return jcur;
+  };
+  while (kind == 0) {                       // stage 1: exact blocks
+    char* cur = lds + (t & 1) * C::STB;
+    advance(cur);
+    chunk<C, false>(st, qf, cur, off, c2, hh, bits, 0);
+  }
+  while (kind == 1) {                       // stage 2: centroid / value-sum chunks
+    char* cur = lds + (t & 1) * C::STB;
+    const int jcur = advance(cur);
+    chunk<C, true>(st, qf, cur, off, c2, hh, bits, jcur);
   }
 
   if (approx) {
@@ -393,9 +433,9 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
       const float* vs = p.vsum + (size_t)bh * nb * D;
       for (int j0 = 0; j0 < nbp; j0 += CK) {
         __syncthreads();
-        stage_centroids<C>(cen, vs, j0, nb, stg0, tid);
+        stage_centroids<C>(cen, vs, j0, nb, lds, tid);
         __syncthreads();
-        chunk<C, true>(st, qf, stg0, off, c2, hh, bits, j0);
+        chunk<C, true>(st, qf, lds, off, c2, hh, bits, j0);
       }
     }
     // ---- stage 3: global first-order correction, acc += scale * (q Hbar) * sum alpha
@@ -421,12 +461,12 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
       }
     } else {
       __syncthreads();
-      stage_hbar_t<C>(p.hbar + (size_t)bh * D * D, stg0, stg1, tid);
+      stage_hbar_t<C>(p.hbar + (size_t)bh * D * D, lds, lds + C::STB, tid);
       __syncthreads();
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) {
         f32x16 hq = f32x16{};
-        const char* base = (mt < C::MT / 2) ? stg0 + 32 * mt * C::RB : stg1 + 32 * (mt - C::MT / 2) * C::RB;
+        const char* base = (mt < C::MT / 2) ? lds + 32 * mt * C::RB : lds + C::STB + 32 * (mt - C::MT / 2) * C::RB;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) hq = mfma32(as_bf16x8(ld16(base + off.koff[ks])), qf[ks], hq);
         st.acc[mt] += f * hq;
