@@ -68,17 +68,16 @@ __device__ __forceinline__ int swz(int r) {
   return (D == 128) ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
 }
 
-// One global_load_lds_dwordx4: lane l copies 16 bytes from src into LDS at
-// lds_dst + 16 l (lds_dst is wave-uniform, passed in M0).  Issued from asm so
-// the compiler does not track the copy: it neither orders later LDS reads of
-// the other ring stage behind it nor waits on it; every use of a stage is
-// preceded by wait_vm0() and a workgroup barrier instead.  The instruction has
-// no register result.
-__device__ __forceinline__ void dma16(const void* src, char* lds_dst) {
-  const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lvoid*)lds_dst);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+// One global_load_lds_dwordx4: lane l copies 16 bytes from gbase + voff(l)
+// into LDS at m0 + 16 l (gbase and m0 wave-uniform).  Issued from asm so the
+// compiler does not track the copy: it neither orders later LDS reads of the
+// other ring stage behind it nor waits on it; every use of a stage is preceded
+// by wait_vm0() and a workgroup barrier instead.  The instruction has no
+// register result.
+__device__ __forceinline__ void dma16(const void* gbase, unsigned voff, unsigned m0v) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(m0v), "v"(src)
+               : "s"(m0v), "v"(voff), "s"(gbase)
                : "memory", "m0");
 }
 
@@ -87,11 +86,11 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_dst) {
 // the stage: rows RPD n .. RPD n + RPD - 1 of the K chunk (n < NDMA/2) or of the
 // V chunk, lane l writing slot l % CPR of row RPD n + l / CPR.  The slot holds
 // logical column chunk (l % CPR) ^ swz(row).  swz has period 16 in the row, so a
-// lane's source offset within a copy takes only NPH values over its copies
-// (kept in registers); copy u adds a constant.
+// lane's byte offset within a copy takes only NPH values over its copies (kept
+// in registers); copy u adds a wave-uniform constant to the base.
 template <class C>
 struct DmaOff {
-  int v[C::NPH];
+  unsigned v[C::NPH];
 };
 
 template <class C>
@@ -100,22 +99,22 @@ __device__ __forceinline__ DmaOff<C> dma_lane_offsets(int w, int lane) {
 #pragma unroll
   for (int ph = 0; ph < C::NPH; ++ph) {
     const int r = (w + C::NW * ph) * C::RPD + lane / C::CPR;
-    o.v[ph] = (lane / C::CPR) * C::D + 8 * ((lane % C::CPR) ^ swz<C::D>(r));
+    o.v[ph] = 2u * ((lane / C::CPR) * C::D + 8 * ((lane % C::CPR) ^ swz<C::D>(r)));
   }
   return o;
 }
 
+// gK, gV: first byte of the K and V chunk; stage_m0: LDS address of the stage
 template <class C>
-__device__ __forceinline__ void dma_stage(const bf16* gK, const bf16* gV, char* stage, int w,
-                                          const DmaOff<C>& loff) {
+__device__ __forceinline__ void dma_stage(const char* gK, const char* gV, unsigned stage_m0,
+                                          int w, const DmaOff<C>& loff) {
   constexpr int half = C::DPW / 2;                       // copies of the K chunk per wave
 #pragma unroll
   for (int u = 0; u < C::DPW; ++u) {
     const bool isv = u >= half;
     const int uu = isv ? u - half : u;
-    const int n = w + C::NW * u;
-    const bf16* src = (isv ? gV : gK) + (w + C::NW * uu) * C::RPD * C::D + loff.v[uu % C::NPH];
-    dma16(src, stage + n * 1024);
+    const char* base = (isv ? gV : gK) + (w + C::NW * uu) * C::RPD * C::RB;
+    dma16(base, loff.v[uu % C::NPH], stage_m0 + (w + C::NW * u) * 1024);
   }
 }
 
@@ -247,15 +246,6 @@ __device__ __forceinline__ void chunk(RowState<C::D>& st, const bf16x8 (&qf)[C::
     }
 }
 
-__device__ __forceinline__ int next_valid(const int32_t* row, int e, int kmax, int nb) {
-  while (e < kmax) {
-    const int j = row[e];
-    if (j >= 0 && j < nb) break;
-    ++e;
-  }
-  return e;
-}
-
 // fp32 statistics -> bf16 chunk of CK centroids / value sums in the stage
 // layout (used when no bf16 pack was supplied); rows past nb are zero.
 template <class C>
@@ -317,6 +307,9 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
   constexpr int D = C::D, BLK = C::BLK, CK = C::CK;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDSB];
   __shared__ unsigned bits[kBitWords];
+  __shared__ short s_list[kMaxBlocks];                 // exact block ids of S_i, in order
+  __shared__ short s_clist[kBitWords];                 // centroid chunks to sweep
+  __shared__ int s_cnt[2];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q32 = lane & 31, hh = lane >> 5;
@@ -362,68 +355,71 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
   st.a = 0.f;
   const float c2 = scale * kLog2e;
 
-  // ---- the chunk stream: CK-token chunks of the exact blocks of S_i, then (PISA
-  // mode with a pack) the chunks of CK centroids that hold any unselected block.
+  // ---- the chunk stream: CK-token chunks of the exact blocks of S_i (in idx
+  // order), then (PISA mode with a pack) the chunks of CK centroids that hold
+  // any unselected block.  Both lists are compacted into LDS once, in order.
+  constexpr int SPB = BLK / CK;                          // chunks per KV block
   const int nctile = packed ? nbp / CK : 0;
-  int e = next_valid(row, 0, kmax, nb), sub = 0, tc = 0;
-  auto next_chunk = [&](int& kind, const bf16*& gk, const bf16*& gv, int& jbase) {
-    if (e < kmax) {
-      const int j = row[e];
-      kind = 0;
-      gk = Kh + ((size_t)j * BLK + (size_t)sub * CK) * D;
-      gv = Vh + ((size_t)j * BLK + (size_t)sub * CK) * D;
-      if (++sub == BLK / CK) {
-        sub = 0;
-        e = next_valid(row, e + 1, kmax, nb);
-      }
-      return;
+  if (w == 0) {
+    int cnt = 0;
+    for (int e0 = 0; e0 < kmax; e0 += 64) {
+      const int e = e0 + lane;
+      const int j = (e < kmax) ? row[e] : -1;
+      const bool ok = j >= 0 && j < nb;
+      const unsigned long long m = __ballot(ok);
+      if (ok) s_list[cnt + __popcll(m & ((1ull << lane) - 1))] = (short)j;
+      cnt += __popcll(m);
     }
-    while (tc < nctile) {
-      bool all = true;
-#pragma unroll
-      for (int u = 0; u < CK / 32; ++u) all = all && (bits[tc * (CK / 32) + u] == ~0u);
-      if (!all) break;
-      ++tc;
+    int ccnt = 0;
+    for (int c0 = 0; c0 < nctile; c0 += 64) {
+      const int tcv = c0 + lane;
+      bool need = false;
+      if (tcv < nctile)
+        for (int u = 0; u < CK / 32; ++u) need = need || (bits[tcv * (CK / 32) + u] != ~0u);
+      const unsigned long long m = __ballot(need);
+      if (need) s_clist[ccnt + __popcll(m & ((1ull << lane) - 1))] = (short)tcv;
+      ccnt += __popcll(m);
     }
-    if (tc < nctile) {
-      kind = 1;
-      jbase = tc * CK;
-      gk = p.pk_cen + ((size_t)bh * nbp + jbase) * D;
-      gv = p.pk_vsum + ((size_t)bh * nbp + jbase) * D;
-      ++tc;
-      return;
+    if (lane == 0) {
+      s_cnt[0] = cnt;
+      s_cnt[1] = ccnt;
     }
-    kind = -1;
+  }
+  __syncthreads();
+  const int nex = s_cnt[0] * SPB, ntot = nex + s_cnt[1];
+  const int ws = __builtin_amdgcn_readfirstlane(w);
+  const unsigned lds_m0 = (unsigned)(uintptr_t)(lvoid*)lds;
+  const char* Kb = reinterpret_cast<const char*>(Kh);
+  const char* Vb = reinterpret_cast<const char*>(Vh);
+  const char* Cb = packed ? reinterpret_cast<const char*>(p.pk_cen + (size_t)bh * nbp * D) : nullptr;
+  const char* Sb = packed ? reinterpret_cast<const char*>(p.pk_vsum + (size_t)bh * nbp * D) : nullptr;
+  // copy chunk t into stage t & 1
+  auto issue = [&](int t) {
+    const unsigned m0 = lds_m0 + (unsigned)((t & 1) * C::STB);
+    if (t < nex) {
+      const int j = __builtin_amdgcn_readfirstlane((int)s_list[t / SPB]);
+      const size_t off = ((size_t)j * BLK + (size_t)(t % SPB) * CK) * C::RB;
+      dma_stage<C>(Kb + off, Vb + off, m0, ws, loff);
+    } else {
+      const int tcv = __builtin_amdgcn_readfirstlane((int)s_clist[t - nex]);
+      const size_t off = (size_t)tcv * CK * C::RB;
+      dma_stage<C>(Cb + off, Sb + off, m0, ws, loff);
+    }
   };
-
-  // two-stage ring: chunk t lives in stage t & 1; the copy of chunk t + 1 is
-  // issued right after the barrier that publishes chunk t
-  int kind, jb = 0, t = 0;
-  const bf16 *gk, *gv;
-  next_chunk(kind, gk, gv, jb);
-  if (kind >= 0) dma_stage<C>(gk, gv, lds, w, loff);
-  auto advance = [&](char* cur) {
+  if (ntot > 0) issue(0);
+  int t = 0;
+  for (; t < nex; ++t) {                    // stage 1: exact blocks
     wait_vm0();
     __syncthreads();
-    int kind_n, jb_n = 0;
-    const bf16 *gk_n, *gv_n;
-    next_chunk(kind_n, gk_n, gv_n, jb_n);
-    if (kind_n >= 0) dma_stage<C>(gk_n, gv_n, lds + ((t + 1) & 1) * C::STB, w, loff);
-    const int jcur = jb;
-    kind = kind_n;
-    jb = jb_n;
-    ++t;
-    return jcur;
-  };
-  while (kind == 0) {                       // stage 1: exact blocks
-    char* cur = lds + (t & 1) * C::STB;
-    advance(cur);
-    chunk<C, false>(st, qf, cur, off, c2, hh, bits, 0);
+    if (t + 1 < ntot) issue(t + 1);
+    chunk<C, false>(st, qf, lds + (t & 1) * C::STB, off, c2, hh, bits, 0);
   }
-  while (kind == 1) {                       // stage 2: centroid / value-sum chunks
-    char* cur = lds + (t & 1) * C::STB;
-    const int jcur = advance(cur);
-    chunk<C, true>(st, qf, cur, off, c2, hh, bits, jcur);
+  for (; t < ntot; ++t) {                   // stage 2: centroid / value-sum chunks
+    wait_vm0();
+    __syncthreads();
+    if (t + 1 < ntot) issue(t + 1);
+    const int jbase = (int)s_clist[t - nex] * CK;
+    chunk<C, true>(st, qf, lds + (t & 1) * C::STB, off, c2, hh, bits, jbase);
   }
 
   if (approx) {
