@@ -10,11 +10,12 @@
 // j, written in ascending order.
 //
 // One workgroup = 4 waves = 4 query blocks of one head.  Each wave pools its
-// block's queries with fully unrolled 16-byte loads (the HBM-bound part), the
-// workgroup stages 32-centroid tiles through LDS for the scores, and each
-// wave sorts its row's block ids with a bitonic network in LDS (score
-// descending, id ascending; padding last).  LDS is sized to the padded block
-// count, so small nb keeps many workgroups resident.
+// block's queries with fully unrolled 16-byte loads (the HBM-bound part); for
+// the scores each thread owns one centroid and forms its dot products with all
+// four pooled queries (broadcast LDS reads); each wave then selects its row's
+// top k with a radix select over order-preserving 64-bit keys (ties at the
+// threshold resolved to the lower block ids).  LDS is sized to the padded
+// block count, so small nb keeps many workgroups resident.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -22,7 +23,6 @@ namespace pisa {
 namespace {
 
 constexpr int kRows = 4;       // query blocks per workgroup (one wave each)
-constexpr int kCT = 32;        // centroids per LDS tile
 
 template <typename T>
 struct Chunk8;
@@ -51,19 +51,19 @@ struct Chunk8<float> {
   }
 };
 
-__device__ __forceinline__ bool before(int ia, int ib, const double* sc, int nb) {
-  if (ia >= nb) return (ib >= nb) && (ia < ib);
-  if (ib >= nb) return true;
-  const double a = sc[ia], b = sc[ib];
-  return (a > b) || (a == b && ia < ib);
-}
-
-// dynamic LDS layout (bytes): q[kRows][D] f64 | c[kCT][D+1] f32 | sc[kRows][nbp] f64 |
-// ord[kRows][nbp] i16 | sel[kRows][nbp/32] u32
+// dynamic LDS layout (bytes): q[kRows][D] f64 | sc[kRows][nbp] f64 |
+// hist[kRows][256] u32 | sel[kRows][nbp/32] u32
 template <int D>
 __host__ __device__ constexpr size_t route_lds_bytes(int nbp) {
-  return (size_t)kRows * D * 8 + (size_t)kCT * (D + 1) * 4 + (size_t)kRows * nbp * 8 +
-         (size_t)kRows * nbp * 2 + (size_t)kRows * (nbp / 32) * 4;
+  return (size_t)kRows * D * 8 + (size_t)kRows * nbp * 8 + (size_t)kRows * 256 * 4 +
+         (size_t)kRows * (nbp / 32) * 4;
+}
+
+// fp64 score -> unsigned key with the same order (larger score, larger key);
+// -0.0 becomes +0.0 first so that equal scores give equal keys
+__device__ __forceinline__ unsigned long long order_key(double x) {
+  const unsigned long long b = __builtin_bit_cast(unsigned long long, x + 0.0);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
 template <int D, int BLK, typename T>
@@ -74,10 +74,9 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
                                                             double lam, int32_t* __restrict__ idx) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   double* s_q = reinterpret_cast<double*>(smem);
-  float* s_c = reinterpret_cast<float*>(s_q + kRows * D);
-  double* s_sc = reinterpret_cast<double*>(s_c + kCT * (D + 1));
-  short* s_ord = reinterpret_cast<short*>(s_sc + kRows * nbp);
-  unsigned* s_sel = reinterpret_cast<unsigned*>(s_ord + kRows * nbp);
+  double* s_sc = s_q + kRows * D;
+  unsigned* s_hist = reinterpret_cast<unsigned*>(s_sc + kRows * nbp);
+  unsigned* s_sel = s_hist + kRows * 256;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nrb = (nb + kRows - 1) / kRows;
@@ -115,64 +114,120 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
       for (int e = 0; e < 8; ++e) s_q[w * D + 8 * c + e] = x[e] * (1.0 / BLK);
   }
 
-  // ---- scores against every block centroid
+  // ---- scores against every block centroid: thread t owns centroid j0 + t
+  // and all kRows pooled queries (read as LDS broadcasts), fp64 FMAs
+  __syncthreads();
   const float* cen = centroid + (size_t)bh * nb * D;
   const float* Mh = M + (size_t)bh * nb;
-  double* sc = s_sc + w * nbp;
-  for (int j0 = 0; j0 < nb; j0 += kCT) {
-    __syncthreads();
-    for (int q = tid; q < kCT * (D / 4); q += 64 * kRows) {
-      const int r = q / (D / 4), c4 = q % (D / 4);
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (j0 + r < nb) v = *reinterpret_cast<const f32x4*>(cen + (size_t)(j0 + r) * D + 4 * c4);
+  for (int j0 = 0; j0 < nb; j0 += 64 * kRows) {
+    const int j = j0 + tid;
+    if (j < nb) {
+      const float* cj = cen + (size_t)j * D;
+      double acc[kRows];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s_c[r * (D + 1) + 4 * c4 + e] = v[e];
-    }
-    __syncthreads();
-    const int jj = lane % kCT, half = lane / kCT;    // two lanes per centroid, half the dims each
-    const double* qv = s_q + w * D + half * (D / 2);
-    const float* cv = s_c + jj * (D + 1) + half * (D / 2);
-    double d0 = 0.0, d1 = 0.0;
+      for (int r = 0; r < kRows; ++r) acc[r] = 0.0;
+#pragma unroll 4
+      for (int a = 0; a < D; a += 4) {
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(cj + a);
 #pragma unroll
-    for (int a = 0; a < D / 2; a += 2) {
-      d0 = fma(qv[a], (double)cv[a], d0);
-      d1 = fma(qv[a + 1], (double)cv[a + 1], d1);
+        for (int r = 0; r < kRows; ++r) {
+          const double* q = s_q + r * D + a;
+          acc[r] = fma(q[0], (double)kv[0], acc[r]);
+          acc[r] = fma(q[1], (double)kv[1], acc[r]);
+          acc[r] = fma(q[2], (double)kv[2], acc[r]);
+          acc[r] = fma(q[3], (double)kv[3], acc[r]);
+        }
+      }
+      const double mj = lam * (double)Mh[j];
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) s_sc[r * nbp + j] = scale * acc[r] + mj;
     }
-    double dot = d0 + d1;
-    dot += __shfl_xor(dot, kCT);
-    const int j = j0 + jj;
-    if (half == 0 && j < nb) sc[j] = scale * dot + lam * (double)Mh[j];
   }
-  short* ord = s_ord + w * nbp;
+  double* sc = s_sc + w * nbp;
+  unsigned* hist = s_hist + w * 256;
   unsigned* sel = s_sel + w * (nbp / 32);
-  for (int t = lane; t < nbp; t += 64) ord[t] = (short)t;
   for (int t = lane; t < nbp / 32; t += 64) sel[t] = 0u;
   __syncthreads();
 
-  // ---- bitonic sort of this row's ids: "before" = higher score, then lower id
-  for (int size = 2; size <= nbp; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = lane; t < nbp / 2; t += 64) {
-        const int a = 2 * t - (t & (stride - 1));
-        const int b = a + stride;
-        const int ia = ord[a], ib = ord[b];
-        const bool asc = (a & size) == 0;
-        const bool swap = asc ? before(ib, ia, sc, nb) : before(ia, ib, sc, nb);
-        if (swap) {
-          ord[a] = (short)ib;
-          ord[b] = (short)ia;
+  // ---- top-k by radix select on the order-preserving 64-bit keys, one row
+  // per wave.  Lane l owns candidates j = l + 64 u.  Each pass histograms the
+  // next 8-bit digit of the candidates still in play, finds the digit value d*
+  // holding the k-th largest, selects the candidates above it and keeps those
+  // equal to it in play.  After 8 passes the ones left tie exactly with the
+  // k-th largest score; the lowest block ids among them fill the rest.
+  const int nu = nbp / 64;                                // candidates per lane (<= 32)
+  unsigned inplay = 0u, chosen = 0u;
+  for (int u = 0; u < nu; ++u)
+    if (lane + 64 * u < nb) inplay |= 1u << u;
+  int krem = k;
+  for (int pass = 7; pass >= 0; --pass) {
+    const int shift = 8 * pass;
+    for (int b = lane; b < 256; b += 64) hist[b] = 0u;
+    __syncthreads();
+    for (int u = 0; u < nu; ++u)
+      if ((inplay >> u) & 1u) atomicAdd(&hist[(order_key(sc[lane + 64 * u]) >> shift) & 255u], 1u);
+    __syncthreads();
+    // this lane holds histogram bins 4l .. 4l + 3
+    unsigned h[4], own = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = hist[4 * lane + e];
+      own += h[e];
+    }
+    // exclusive suffix sum over lanes: above = sum of `own` over lanes > this lane
+    unsigned above;
+    {
+      unsigned incl = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const unsigned y = __shfl_down(incl, off);
+        if (lane + off < 64) incl += y;
+      }
+      above = incl - own;
+    }
+    int dstar = -1;
+    unsigned cnt_above = 0u;
+    {
+      unsigned acc = above;                               // count of bins > 4l + 3
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        if (dstar < 0 && acc < (unsigned)krem && acc + h[e] >= (unsigned)krem) {
+          dstar = 4 * lane + e;
+          cnt_above = acc;
+        }
+        acc += h[e];
+      }
+    }
+    const unsigned long long who = __ballot(dstar >= 0);
+    const int src = __ffsll(who) - 1;
+    dstar = __shfl(dstar, src);
+    cnt_above = __shfl(cnt_above, src);
+    krem -= (int)cnt_above;
+    for (int u = 0; u < nu; ++u)
+      if ((inplay >> u) & 1u) {
+        const int dg = (int)((order_key(sc[lane + 64 * u]) >> shift) & 255u);
+        if (dg > dstar) {
+          chosen |= 1u << u;
+          inplay &= ~(1u << u);
+        } else if (dg < dstar) {
+          inplay &= ~(1u << u);
         }
       }
-      __syncthreads();
-    }
+    __syncthreads();
   }
-
-  // ---- the first k ids, written in ascending order
-  for (int t = lane; t < k; t += 64) {
-    const int j = ord[t];
-    atomicOr(&sel[j >> 5], 1u << (j & 31));
+  // exact ties with the k-th largest: lowest block ids first
+  for (int u = 0; u < nu && krem > 0; ++u) {
+    const bool tie = (inplay >> u) & 1u;
+    const unsigned long long m = __ballot(tie);
+    const int before_me = __popcll(m & ((1ull << lane) - 1));
+    if (tie && before_me < krem) chosen |= 1u << u;
+    krem -= min(krem, __popcll(m));
   }
+  for (int u = 0; u < nu; ++u)
+    if ((chosen >> u) & 1u) atomicOr(&sel[(lane + 64 * u) >> 5], 1u << ((lane + 64 * u) & 31));
   __syncthreads();
+
+  // ---- the selected ids, written in ascending order
   if (!active) return;
   int32_t* out = idx + ((size_t)bh * nb + i) * k;
   const int nw = nbp / 32;                                   // <= 64 words

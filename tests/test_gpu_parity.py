@@ -262,3 +262,21 @@ def test_packed_and_fp32_statistics_paths_agree(torch, wid):
     b = pisa.attention(Qd, Kd, Vd, idx, dict(st, packed=None), w.block, mode="approx")
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("nb,k", [(16, 5), (72, 30), (512, 64), (2048, 700)])
+def test_route_exact_ties_go_to_lower_ids(torch, nb, k):
+    """Zero queries make every score lambda * M_j; M with many repeated values
+    (and +-0) forces exact ties at the k-th score, which the oracle breaks
+    towards the lower block id."""
+    pisa = pisa_mod()
+    B, d = 64, 128
+    g = np.random.default_rng(nb)
+    Q = np.zeros((1, 2, nb * B, d), dtype=np.float32)
+    M = g.integers(-2, 3, (1, 2, nb)).astype(np.float32)
+    M[0, 1, ::3] = -0.0
+    cen = np.zeros((1, 2, nb, d), dtype=np.float32)
+    st = {"centroid": torch.from_numpy(cen).cuda(), "M": torch.from_numpy(M).cuda()}
+    idx = pisa.route(to_dev(Q, "bf16"), st, k, 1.0, B)
+    ref = oracle.route(Q, cen, M, k, 1.0, B, 1 / math.sqrt(d))
+    assert np.array_equal(idx.cpu().numpy(), ref)
