@@ -131,8 +131,25 @@ struct RowState {
 
 // The running max is only raised when a row's new maximum exceeds it by more
 // than kTau (log2 units); until then the weights exp2(x - m) stay below 2^kTau.
-// Any m gives the same N / D, so this only saves rescales of acc.
+// Any m gives the same N / D, so this only saves rescales of acc.  The weights
+// of a tile are computed against the current m first; only if a lane's sum
+// reaches 2^kTau (which it does whenever one weight exceeds 2^kTau, and on
+// inf / NaN) is the row max formed and the tile redone, so the common path has
+// no max reduction and no cross-lane wait before the exponentials.
 constexpr float kTau = 8.f;
+constexpr float kSumCap = 256.f;     // 2^kTau
+
+// Lanes l and l ^ 32 hold the two halves of one query row.  permlane32_swap of
+// x with itself gives every lane the pair (x[l % 32], x[l % 32 + 32]), so the
+// row total / max is formed in the same order in both halves.
+__device__ __forceinline__ float row_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float row_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // Per-lane LDS byte offsets, fixed for the whole kernel:
 //   koff[ks]       K row 32 kt + q32 (kt added as an immediate), columns 16 ks + 8 hh ..
@@ -208,23 +225,26 @@ __device__ __forceinline__ void chunk(RowState<C::D>& st, const bf16x8 (&qf)[C::
         if ((wbits >> (8 * (r / 4) + (r % 4))) & 1u) s[kt][r] = -INFINITY;
     }
   }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kt = 0; kt < C::NKT; ++kt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
-  if (__any(mx > st.m + kTau)) {
-    const float mnew = fmaxf(st.m, mx);
-    const float corr = fast_exp2(st.m - mnew);
-    st.m = mnew;
-    st.l *= corr;
-    st.a *= corr;
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) st.acc[mt] *= corr;
-  }
   u32x4 pf[C::NSL];
-  const float ps = weights_bf16<C::NKT>(s, c2, -st.m, pf);
+  float ps = weights_bf16<C::NKT>(s, c2, -st.m, pf);
+  if (__any(!(ps < kSumCap))) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    mx = row_max(mx) * c2;
+    if (__any(mx > st.m + kTau)) {
+      const float mnew = fmaxf(st.m, mx);
+      const float corr = fast_exp2(st.m - mnew);
+      st.m = mnew;
+      st.l *= corr;
+      st.a *= corr;
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) st.acc[mt] *= corr;
+      ps = weights_bf16<C::NKT>(s, c2, -st.m, pf);
+    }
+  }
   if (STAGE2) {
     st.l += (float)C::BLK * ps;
     st.a += ps;
@@ -435,7 +455,7 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
       }
     }
     // ---- stage 3: global first-order correction, acc += scale * (q Hbar) * sum alpha
-    const float atot = st.a + __shfl_xor(st.a, 32);
+    const float atot = row_sum(st.a);
     const float f = scale * atot;
     if (packed) {
       // A operand (Hbar^T rows) straight from the bf16 pack, two d-tiles at a time
@@ -471,7 +491,7 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
   }
 
   // ---- epilogue: o = N / D (0 when nothing was attended in keep-or-drop)
-  const float ltot = st.l + __shfl_xor(st.l, 32);
+  const float ltot = row_sum(st.l);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   bf16* orow = p.O + ((size_t)bh * L + (size_t)i * BLK + 32 * w + q32) * D;
 #pragma unroll
