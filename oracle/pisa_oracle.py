@@ -26,7 +26,20 @@ Functions, one per call of the C ABI:
 * ``precompute(K, V, B)`` -> block centroids, value sums, per-block H_j, Hbar, M_j
 * ``route(Q, centroid, M, k, lam, B, scale)`` -> per-query-block exact set S_i
   (``route_scores`` exposes the float64 scores it ranks)
-* ``attention(Q, K, V, idx, centroid, vsum, Hbar, mode, scale, B)`` -> O
+* ``attention(Q, K, V, idx, centroid, vsum, Hbar, mode, scale, B, H=None)`` -> O
+
+Approximation orders of the unselected blocks (``mode``):
+
+* ``MODE_APPROX`` -- the PISA mixed order: zeroth-order block terms plus the
+  global first-order correction with Hbar.
+* ``MODE_ZEROTH`` -- the zeroth-order block terms alone (no correction).
+* ``MODE_FIRST`` -- a separate first-order term for every unselected block,
+  alpha_{t,j} * (q H_j), i.e. the full block Taylor expansion that the mixed
+  order approximates by replacing each H_j with Hbar (PISA page, section 2,
+  "Core algorithm", the global first-order correction, which the page
+  introduces to avoid exactly these per-block terms; section 3, the mixed-order
+  scheme).
+* ``MODE_DROP`` -- keep-or-drop block-sparse attention over S_i only.
 
 Readings where the pages are silent or ambiguous:
 
@@ -58,6 +71,8 @@ import numpy as np
 
 MODE_APPROX = 0
 MODE_DROP = 1
+MODE_ZEROTH = 2
+MODE_FIRST = 3
 
 
 def _blocks(X: np.ndarray, B: int) -> np.ndarray:
@@ -139,7 +154,7 @@ def route(Q: np.ndarray, centroid: np.ndarray, M: np.ndarray, k: int, lam: float
 
 def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
               centroid: np.ndarray, vsum: np.ndarray, Hbar: np.ndarray,
-              mode: int, scale: float, B: int, qblocks=None) -> np.ndarray:
+              mode: int, scale: float, B: int, qblocks=None, H=None) -> np.ndarray:
     """PISA exact-or-approximate attention, or keep-or-drop block-sparse attention.
 
     PISA page, section 2, "Core algorithm": o_t = N_t / D_t with
@@ -151,6 +166,12 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
 
     Block-sparse notes, section 3.3 (mode == MODE_DROP): only the S_i terms
     remain, i.e. softmax over the selected blocks' keys; an empty S_i gives 0.
+
+    MODE_ZEROTH drops the q_t Hbar term.  MODE_FIRST replaces it with the
+    per-block first-order terms sum_{j in U_i} alpha_{t,j} (q H_j), which needs
+    ``H`` [b,h,nb,d,d] from ``precompute``; the denominator is the same in all
+    three orders because the first-order term of a block sums to zero over its
+    keys.
 
     idx: int [b,h,nqb,kmax]; entries are block ids, -1 entries are padding.
     qblocks: optional iterable of (b, h, i) triples; only those query blocks are
@@ -164,8 +185,12 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
     vsum = np.asarray(vsum, dtype=np.float64)
     Hbar = np.asarray(Hbar, dtype=np.float64)
     idx = np.asarray(idx)
-    if mode not in (MODE_APPROX, MODE_DROP):
+    if mode not in (MODE_APPROX, MODE_DROP, MODE_ZEROTH, MODE_FIRST):
         raise ValueError(f"unknown mode {mode}")
+    if mode == MODE_FIRST:
+        if H is None:
+            raise ValueError("MODE_FIRST needs the per-block H_j")
+        H = np.asarray(H, dtype=np.float64)
     b, h, nqb, _, d = Qb.shape
     nb = Kb.shape[2]
     dv = Vb.shape[-1]
@@ -199,7 +224,13 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
         w = np.exp(ell - m)                                          # exact weights
         a = np.exp(c - m)                                            # alpha, shifted by m
         asum = a.sum(axis=1, keepdims=True)                          # sum_{U} alpha
-        N = w @ VS + a @ vsum[bi, hi, U] + (q @ Hbar[bi, hi]) * asum
+        N = w @ VS + a @ vsum[bi, hi, U]
+        if mode == MODE_APPROX:
+            N = N + (q @ Hbar[bi, hi]) * asum
+        elif mode == MODE_FIRST and U:
+            # sum_j alpha_{t,j} (q_t H_j): one (B x d) @ (d x dv) product per block
+            qH = np.matmul(q[None, :, :], H[bi, hi, U])              # [|U|, B, dv]
+            N = N + np.einsum("tj,jtc->tc", a, qH)
         D = w.sum(axis=1, keepdims=True) + B * asum
         out[bi, hi, i] = N / D
     return out.reshape(b, h, nqb * B, dv)

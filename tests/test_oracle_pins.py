@@ -14,7 +14,7 @@ import pytest
 import torch
 import torch.nn.functional as F
 
-from oracle import MODE_APPROX, MODE_DROP, attention, precompute, route
+from oracle import MODE_APPROX, MODE_DROP, MODE_FIRST, MODE_ZEROTH, attention, precompute, route
 
 RTOL = 1e-12
 
@@ -46,7 +46,7 @@ def rand_idx(seed, b, h, nqb, nb, k):
 
 def run(Q, K, V, idx, B, mode, scale, st=None):
     st = precompute(K, V, B) if st is None else st
-    return attention(Q, K, V, idx, st["centroid"], st["vsum"], st["Hbar"], mode, scale, B)
+    return attention(Q, K, V, idx, st["centroid"], st["vsum"], st["Hbar"], mode, scale, B, H=st["H"])
 
 
 def block_mask(idx, B, L):
@@ -324,6 +324,117 @@ def test_error_is_second_order_in_block_spread():
     assert all(1.7 < x < 2.3 for x in r0), r0
 
 
+# ---------------------------------------------------------------- approximation orders
+
+def het_inputs(seed, eps, nb=6, B=8, d=4):
+    """Blocks with their own centroid and their own zero-mean key deviations of
+    size eps, independent N(0,1) values: every H_j differs (and is not
+    symmetric), so Hbar != H_j."""
+    g = np.random.default_rng(seed)
+    cen = g.standard_normal((nb, d))
+    dev = g.standard_normal((nb, B, d))
+    dev -= dev.mean(axis=1, keepdims=True)
+    K = (cen[:, None, :] + eps * dev).reshape(1, 1, nb * B, d)
+    V = g.standard_normal((1, 1, nb * B, d))
+    Q = g.standard_normal((1, 1, nb * B, d))
+    return Q, K, V
+
+
+def zeroth_bruteforce(Q, K, V, idx, B, s):
+    """Token-level zeroth-order expansion from its definition: exact weights
+    e^{q k} on S_i, the weight e^{q kbar_j} on every token of a block of U_i.
+    Pure Python loops; only for tiny inputs."""
+    _, _, L, d = Q.shape
+    nb = L // B
+    out = np.zeros((L, d))
+    for t in range(L):
+        i = t // B
+        S = {int(j) for j in idx[0, 0, i] if j >= 0}
+        q = [s * Q[0, 0, t, a] for a in range(d)]
+        num, den = [0.0] * d, 0.0
+        for j in range(nb):
+            toks = range(j * B, (j + 1) * B)
+            kbar = [sum(K[0, 0, n, a] for n in toks) / B for a in range(d)]
+            alpha = math.exp(sum(q[a] * kbar[a] for a in range(d)))
+            for n in toks:
+                w = math.exp(sum(q[a] * K[0, 0, n, a] for a in range(d))) if j in S else alpha
+                den += w
+                for c in range(d):
+                    num[c] += w * V[0, 0, n, c]
+        out[t] = [x / den for x in num]
+    return out
+
+
+@pytest.mark.parametrize("seed", [40, 41])
+def test_first_order_per_block_equals_token_taylor(seed):
+    """MODE_FIRST is the token-level first-order expansion of every unselected
+    block, for heterogeneous (non-symmetric) H_j and any S_i, including a row
+    with an empty S_i."""
+    Q, K, V = het_inputs(seed, 0.7)
+    B, nb, s = 8, 6, 0.5
+    idx = rand_idx(seed + 1, 1, 1, nb, nb, 2)
+    idx[0, 0, 3] = -1
+    st = precompute(K, V, B)
+    assert not np.allclose(st["H"][0, 0, 0], st["H"][0, 0, 0].T)
+    out = run(Q, K, V, idx, B, MODE_FIRST, s, st)
+    assert np.allclose(out[0, 0], taylor_bruteforce(Q, K, V, idx, B, s), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [42, 43])
+def test_zeroth_order_equals_token_zeroth(seed):
+    Q, K, V = het_inputs(seed, 0.7)
+    B, nb, s = 8, 6, 0.5
+    idx = rand_idx(seed + 1, 1, 1, nb, nb, 3)
+    out = run(Q, K, V, idx, B, MODE_ZEROTH, s)
+    assert np.allclose(out[0, 0], zeroth_bruteforce(Q, K, V, idx, B, s), rtol=1e-11, atol=1e-12)
+
+
+def test_error_order_of_each_approximation():
+    """Against dense attention, with heterogeneous H_j: the per-block first
+    order errs as eps^2; the zeroth order and the mixed order (whose global
+    Hbar leaves H_j - Hbar uncorrected) err as eps."""
+    B, nb, s = 8, 6, 0.5
+    idx = rand_idx(24, 1, 1, nb, nb, 2)
+    ratios = {}
+    for mode in (MODE_APPROX, MODE_ZEROTH, MODE_FIRST):
+        errs = []
+        for eps in (0.1, 0.05, 0.025):
+            Q, K, V = het_inputs(31, eps)
+            errs.append(np.abs(run(Q, K, V, idx, B, mode, s) - sdpa(Q, K, V, s)).max())
+        ratios[mode] = [errs[i] / errs[i + 1] for i in range(2)]
+    assert all(3.4 < x < 4.6 for x in ratios[MODE_FIRST]), ratios
+    assert all(1.7 < x < 2.3 for x in ratios[MODE_APPROX]), ratios
+    assert all(1.7 < x < 2.3 for x in ratios[MODE_ZEROTH]), ratios
+
+
+def test_orders_coincide_in_their_special_cases():
+    """All H_j equal (so Hbar = H_j): the per-block and the mixed order agree.
+    Values constant inside every block (so every H_j = 0): all three agree.
+    Density one (U empty): all four modes are dense attention."""
+    B, nb, s = 8, 6, 0.5
+    idx = rand_idx(50, 1, 1, nb, nb, 2)
+    Q, K, V = equal_H_inputs(51, 0.8)
+    assert np.allclose(run(Q, K, V, idx, B, MODE_FIRST, s), run(Q, K, V, idx, B, MODE_APPROX, s),
+                       rtol=1e-11, atol=1e-12)
+    Q, K, _ = het_inputs(52, 0.8)
+    Vc = np.repeat(np.random.default_rng(53).standard_normal((1, 1, nb, 1, 4)), B, axis=3).reshape(K.shape)
+    outs = [run(Q, K, Vc, idx, B, m, s) for m in (MODE_APPROX, MODE_ZEROTH, MODE_FIRST)]
+    assert np.allclose(outs[0], outs[1], rtol=1e-11, atol=1e-12)
+    assert np.allclose(outs[0], outs[2], rtol=1e-11, atol=1e-12)
+    full = np.broadcast_to(np.arange(nb, dtype=np.int32), (1, 1, nb, nb)).copy()
+    ref = sdpa(Q, K, Vc, s)
+    for m in (MODE_APPROX, MODE_ZEROTH, MODE_FIRST, MODE_DROP):
+        assert np.allclose(run(Q, K, Vc, full, B, m, s), ref, rtol=1e-10, atol=1e-12)
+
+
+def test_first_order_needs_H():
+    Q, K, V = het_inputs(54, 0.5)
+    st = precompute(K, V, 8)
+    idx = rand_idx(55, 1, 1, 6, 6, 2)
+    with pytest.raises(ValueError):
+        attention(Q, K, V, idx, st["centroid"], st["vsum"], st["Hbar"], MODE_FIRST, 0.5, 8)
+
+
 # ---------------------------------------------------------------- worked examples
 
 LN3 = math.log(3.0)
@@ -447,4 +558,26 @@ def test_pins_catch_planted_statistic_mistakes():
     }
     for name, (c, vs, hb) in mutants.items():
         bad = attention(Q, K, V, idx, c, vs, hb, MODE_APPROX, s, B)
+        assert not np.allclose(bad[0, 0], ref, rtol=1e-6), name
+
+
+def test_pins_catch_planted_first_order_mistakes():
+    """Plausible mistakes in the per-block first-order term (H_j transposed,
+    Hbar used in place of H_j, the first-order term scaled by B, a block's H
+    taken from its neighbour) each fail the token-level Taylor pin."""
+    Q, K, V = het_inputs(56, 0.6)
+    B, nb, s = 8, 6, 0.5
+    idx = rand_idx(57, 1, 1, nb, nb, 2)
+    st = precompute(K, V, B)
+    ref = taylor_bruteforce(Q, K, V, idx, B, s)
+    args = (Q, K, V, idx, st["centroid"], st["vsum"], st["Hbar"], MODE_FIRST, s, B)
+    assert np.allclose(attention(*args, H=st["H"])[0, 0], ref, rtol=1e-11, atol=1e-12)
+    mutants = {
+        "H_j transposed": np.swapaxes(st["H"], -1, -2),
+        "Hbar for every block": np.broadcast_to(st["Hbar"][:, :, None], st["H"].shape),
+        "first order times B": st["H"] * B,
+        "H of the next block": np.roll(st["H"], 1, axis=2),
+    }
+    for name, Hm in mutants.items():
+        bad = attention(*args, H=Hm)
         assert not np.allclose(bad[0, 0], ref, rtol=1e-6), name
