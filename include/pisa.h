@@ -64,7 +64,13 @@ typedef enum {
 
 typedef enum {
   PISA_MODE_APPROX = 0,     /* PISA: exact S_i + zeroth-order U_i + global first-order correction */
-  PISA_MODE_DROP = 1        /* keep-or-drop block-sparse attention over S_i only */
+  PISA_MODE_DROP = 1,       /* keep-or-drop block-sparse attention over S_i only */
+  PISA_MODE_ZEROTH = 2,     /* exact S_i + zeroth-order U_i, no first-order term */
+  PISA_MODE_FIRST = 3       /* exact S_i + zeroth-order U_i + a first-order term per U_i block,
+                               alpha_{t,j} (q H_j): the expansion that the global Hbar stands
+                               in for (PISA summary, section 2, "Core algorithm": the mixed
+                               order avoids these per-block terms because each needs its own
+                               d x d matrix) */
 } pisa_mode;
 
 typedef struct {
@@ -92,6 +98,10 @@ typedef struct {
                                Hbar^T row = value dim).  Written by pisa_precompute when
                                non-NULL; read by pisa_attention (PISA mode) when non-NULL,
                                which otherwise converts the fp32 statistics itself.         */
+  void* Ht;                 /* NULLABLE, bf16 inputs only: bfloat16 [b,h,nb,d,d] holding H_j^T
+                               (row = value dim, column = key dim), b*h*nb*d*d*2 bytes.
+                               Written by pisa_precompute when non-NULL; required by
+                               PISA_MODE_FIRST with bf16 inputs (fp32 inputs read H).       */
 } pisa_stats;
 
 /* Version of the library (PISA_VERSION at build time). */
@@ -119,7 +129,8 @@ size_t pisa_packed_size(const pisa_shape* shape);
  * "Hardware implementation" places this computation before the attention).
  *
  *   K, V       [b,h,L,d] of shape->dtype (device, read only)
- *   out        centroid, vsum, Hbar, M required; H and packed optional (see pisa_stats)
+ *   out        centroid, vsum, Hbar, M required; H, packed and Ht optional (see
+ *              pisa_stats; Ht must be NULL for fp32 inputs)
  *   workspace  device scratch of at least pisa_workspace_size(shape) bytes,
  *              caller-owned; contents on entry are ignored
  *
@@ -163,8 +174,9 @@ pisa_status pisa_route(const pisa_shape* shape, const void* Q, const float* cent
  *             < nb (ids >= nb are skipped, duplicates are counted twice; no
  *             fault either way).  Rows may be fully padded (S_i empty).
  *   kmax      row length of idx, 1 <= kmax <= nb
- *   stats     centroid, vsum, Hbar (and packed, when non-NULL) read in APPROX
- *             mode (may be NULL in DROP mode); H and M are not read
+ *   stats     centroid, vsum, Hbar (and packed, when non-NULL) read in APPROX;
+ *             centroid, vsum (and packed) in ZEROTH; centroid, vsum, packed and Ht
+ *             (bf16) or H (fp32) in FIRST; may be NULL in DROP.  M is not read.
  *   mode      pisa_mode
  *   scale     softmax scale applied to every q_t (exact logits, alpha and the
  *             correction), finite
@@ -174,6 +186,8 @@ pisa_status pisa_route(const pisa_shape* shape, const void* Q, const float* cent
  *   N_t = sum_{S_i,n} e^{q k} v + sum_{U_i} e^{q kbar_j} sigma_j + (q Hbar) sum_{U_i} e^{q kbar_j}
  *   D_t = sum_{S_i,n} e^{q k}   + block * sum_{U_i} e^{q kbar_j}
  * (the first-order term adds nothing to D_t: block deviations sum to zero).
+ * ZEROTH: the same without the (q Hbar) term.  FIRST: the (q Hbar) term
+ * replaced by sum_{U_i} e^{q kbar_j} (q H_j).
  * DROP: softmax over the keys of S_i only; o_t = 0 when S_i is empty.
  */
 pisa_status pisa_attention(const pisa_shape* shape, const void* Q, const void* K,

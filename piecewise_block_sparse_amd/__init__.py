@@ -8,6 +8,11 @@ in libpisa's gfx950 kernels.  If libpisa.so is missing the calls raise.
     idx = route(Q, stats, k, lam, block)                  # [b,h,nb,k] int32, ascending
     O = attention(Q, K, V, idx, stats, block, mode="approx")
 
+Modes: "approx" (PISA: exact blocks, zeroth-order blocks, global Hbar
+correction), "zeroth" (no correction), "first" (a first-order term per
+unselected block; needs precompute(..., store_Ht=True) for bf16 inputs or
+store_H=True for fp32 inputs), "drop" (keep-or-drop block-sparse attention).
+
 Q, K, V: contiguous [b, h, L, d] CUDA tensors, bfloat16 or float32, L a
 multiple of `block`.
 """
@@ -19,10 +24,13 @@ import math
 from . import _lib
 
 __all__ = ["precompute", "route", "attention", "workspace_size", "version", "MODE_APPROX",
-           "MODE_DROP"]
+           "MODE_DROP", "MODE_ZEROTH", "MODE_FIRST"]
 
 MODE_APPROX = _lib.MODE_APPROX
 MODE_DROP = _lib.MODE_DROP
+MODE_ZEROTH = _lib.MODE_ZEROTH
+MODE_FIRST = _lib.MODE_FIRST
+_MODES = {"approx": MODE_APPROX, "drop": MODE_DROP, "zeroth": MODE_ZEROTH, "first": MODE_FIRST}
 
 
 def _torch():
@@ -76,11 +84,13 @@ def workspace_size(X, block: int) -> int:
     return _lib.load().pisa_workspace_size(ctypes.byref(_shape(X, block)))
 
 
-def precompute(K, V, block: int, store_H: bool = False, workspace=None, packed: bool = True) -> dict:
+def precompute(K, V, block: int, store_H: bool = False, workspace=None, packed: bool = True,
+               store_Ht: bool = False) -> dict:
     """Block statistics (fp32): centroid, vsum, Hbar, M, and H when store_H.
 
     For bf16 inputs (and packed=True) also the bf16 pack that the attention
-    kernel streams in PISA mode (key "packed")."""
+    kernel streams in PISA mode (key "packed"), and with store_Ht the bf16
+    H_j^T per block (key "Ht") that mode "first" streams."""
     torch = _torch()
     lib = _lib.load()
     _same(K, V)
@@ -95,14 +105,19 @@ def precompute(K, V, block: int, store_H: bool = False, workspace=None, packed: 
         "Hbar": torch.empty((b, h, d, d), **f32),
         "M": torch.empty((b, h, nb), **f32),
         "packed": None,
+        "Ht": None,
     }
+    if store_Ht:
+        if K.dtype != torch.bfloat16:
+            raise ValueError("store_Ht is for bf16 inputs (fp32 mode 'first' reads H)")
+        out["Ht"] = torch.empty((b, h, nb, d, d), dtype=torch.bfloat16, device=K.device)
     npk = lib.pisa_packed_size(ctypes.byref(shp)) if packed else 0
     if npk:
         out["packed"] = torch.empty(npk, dtype=torch.uint8, device=K.device)
     need = lib.pisa_workspace_size(ctypes.byref(shp))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=K.device)
-    st = _lib.PisaStats(*(_ptr(out[n]) for n in ("centroid", "vsum", "H", "Hbar", "M", "packed")))
+    st = _lib.PisaStats(*(_ptr(out[n]) for n in ("centroid", "vsum", "H", "Hbar", "M", "packed", "Ht")))
     _lib.check("pisa_precompute", lib.pisa_precompute(
         ctypes.byref(shp), _ptr(K), _ptr(V), ctypes.byref(st), _ptr(workspace),
         workspace.numel(), _stream(K)))
@@ -128,12 +143,12 @@ def route(Q, stats: dict, k: int, lam: float, block: int, scale: float | None = 
 
 def attention(Q, K, V, idx, stats: dict | None, block: int, mode: int | str = "approx",
               scale: float | None = None, out=None):
-    """PISA (mode "approx") or keep-or-drop (mode "drop") block-sparse attention."""
+    """PISA block-sparse attention; mode "approx", "zeroth", "first" or "drop"."""
     torch = _torch()
     lib = _lib.load()
     _same(Q, K, V)
     if isinstance(mode, str):
-        mode = {"approx": MODE_APPROX, "drop": MODE_DROP}[mode]
+        mode = _MODES[mode]
     shp = _shape(Q, block)
     d = Q.shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -145,18 +160,23 @@ def attention(Q, K, V, idx, stats: dict | None, block: int, mode: int | str = "a
     O = torch.empty_like(Q) if out is None else out
     _same(Q, O)
     st = None
-    if mode == MODE_APPROX:
+    if mode != MODE_DROP:
         if stats is None:
-            raise ValueError("approx mode needs the block statistics")
+            raise ValueError("modes other than drop need the block statistics")
         _expect(stats["centroid"], (b, h, nb, d), torch.float32, "stats['centroid']")
         _expect(stats["vsum"], (b, h, nb, d), torch.float32, "stats['vsum']")
-        _expect(stats["Hbar"], (b, h, d, d), torch.float32, "stats['Hbar']")
+        if mode == MODE_APPROX:
+            _expect(stats["Hbar"], (b, h, d, d), torch.float32, "stats['Hbar']")
+        if mode == MODE_FIRST and Q.dtype == torch.bfloat16:
+            _expect(stats.get("Ht"), (b, h, nb, d, d), torch.bfloat16, "stats['Ht']")
+        if mode == MODE_FIRST and Q.dtype == torch.float32:
+            _expect(stats.get("H"), (b, h, nb, d, d), torch.float32, "stats['H']")
     if stats is not None:
         pk = stats.get("packed")
         if pk is not None and pk.numel() != lib.pisa_packed_size(ctypes.byref(shp)):
             raise ValueError("stats['packed'] does not match this shape")
-        st = _lib.PisaStats(_ptr(stats["centroid"]), _ptr(stats["vsum"]), None,
-                            _ptr(stats["Hbar"]), None, _ptr(pk))
+        st = _lib.PisaStats(_ptr(stats["centroid"]), _ptr(stats["vsum"]), _ptr(stats.get("H")),
+                            _ptr(stats["Hbar"]), None, _ptr(pk), _ptr(stats.get("Ht")))
     _lib.check("pisa_attention", lib.pisa_attention(
         ctypes.byref(shp), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), int(idx.shape[-1]),
         ctypes.byref(st) if st is not None else None, int(mode), scale, _ptr(O), _stream(Q)))

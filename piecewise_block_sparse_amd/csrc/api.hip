@@ -96,6 +96,7 @@ pisa_status pisa_precompute(const pisa_shape* shape, const void* K, const void* 
   if (!out->centroid || !out->vsum || !out->Hbar || !out->M)
     return fail(PISA_ERR_NULL, "centroid, vsum, Hbar and M outputs are required");
   const bool bf = shape->dtype == PISA_DTYPE_BF16;
+  if (!bf && out->Ht) return fail(PISA_ERR_ARG, "Ht (bf16 H_j^T) is for bf16 inputs only");
   const bool needs_ws = bf || out->H == nullptr;
   if (needs_ws) {
     const size_t need = pisa_workspace_size(shape);
@@ -104,8 +105,8 @@ pisa_status pisa_precompute(const pisa_shape* shape, const void* K, const void* 
       return fail(PISA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   }
   pisa::StatsArgs a{K, V, out->centroid, out->vsum, out->H, out->Hbar, out->M,
-                    bf ? out->packed : nullptr, workspace, bh, nb, shape->head_dim, shape->block,
-                    (hipStream_t)stream};
+                    bf ? out->packed : nullptr, bf ? out->Ht : nullptr, workspace, bh, nb,
+                    shape->head_dim, shape->block, (hipStream_t)stream};
   return hip_status(bf ? pisa::launch_stats_bf16(a) : pisa::launch_stats_f32(a), "pisa_precompute");
 }
 
@@ -135,19 +136,32 @@ pisa_status pisa_attention(const pisa_shape* shape, const void* Q, const void* K
   pisa_status st = check_shape(shape, &bh, &nb);
   if (st != PISA_OK) return st;
   if (!Q || !K || !V || !idx || !O) return fail(PISA_ERR_NULL, "Q, K, V, idx and O are required");
-  if (mode != PISA_MODE_APPROX && mode != PISA_MODE_DROP)
+  if (mode != PISA_MODE_APPROX && mode != PISA_MODE_DROP && mode != PISA_MODE_ZEROTH &&
+      mode != PISA_MODE_FIRST)
     return fail(PISA_ERR_ARG, "unknown mode %d", mode);
   if (kmax < 1 || kmax > nb) return fail(PISA_ERR_ARG, "kmax=%d outside [1, %d]", kmax, nb);
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(PISA_ERR_ARG, "scale must be finite and positive");
-  const bool approx = mode == PISA_MODE_APPROX;
-  if (approx && (!stats || !stats->centroid || !stats->vsum || !stats->Hbar))
-    return fail(PISA_ERR_NULL, "APPROX mode needs stats centroid, vsum and Hbar");
+  const bool approx = mode != PISA_MODE_DROP;
   const bool bf = shape->dtype == PISA_DTYPE_BF16;
+  const int order = mode == PISA_MODE_ZEROTH  ? pisa::kOrderZeroth
+                    : mode == PISA_MODE_FIRST ? pisa::kOrderFirst
+                                              : pisa::kOrderMixed;
+  if (approx && (!stats || !stats->centroid || !stats->vsum))
+    return fail(PISA_ERR_NULL, "modes other than DROP need stats centroid and vsum");
+  if (mode == PISA_MODE_APPROX && !stats->Hbar)
+    return fail(PISA_ERR_NULL, "APPROX mode needs stats Hbar");
+  if (mode == PISA_MODE_FIRST && bf && (!stats->Ht || !stats->packed))
+    return fail(PISA_ERR_NULL, "FIRST mode with bf16 inputs needs stats Ht and packed");
+  if (mode == PISA_MODE_FIRST && !bf && !stats->H)
+    return fail(PISA_ERR_NULL, "FIRST mode with fp32 inputs needs stats H");
   pisa::AttnArgs a{Q, K, V, idx, kmax,
                    approx ? stats->centroid : nullptr, approx ? stats->vsum : nullptr,
-                   approx ? stats->Hbar : nullptr, (approx && bf) ? stats->packed : nullptr,
-                   approx ? 1 : 0, scale, O, bh, nb, shape->head_dim, shape->block,
+                   mode == PISA_MODE_APPROX ? stats->Hbar : nullptr,
+                   (approx && bf) ? stats->packed : nullptr,
+                   (mode == PISA_MODE_FIRST && bf) ? stats->Ht : nullptr,
+                   (mode == PISA_MODE_FIRST && !bf) ? stats->H : nullptr,
+                   approx ? 1 : 0, order, scale, O, bh, nb, shape->head_dim, shape->block,
                    (hipStream_t)stream};
   return hip_status(bf ? pisa::launch_attn_bf16(a) : pisa::launch_attn_f32(a), "pisa_attention");
 }

@@ -60,6 +60,9 @@ struct Cfg {
                 "per-wave copies: half K, half V, whole swizzle periods");
   static_assert(D * RB <= LDSB && (D / 2) * RB <= STB, "Hbar^T (fallback) halves fit the stages");
   static_assert(BLK % CK == 0 && CK % 32 == 0, "chunking");
+  // per-block first order: H_j^T (D rows) streams as HP ring chunks of RP rows
+  static constexpr int RP = (2 * CK < D) ? 2 * CK : D;
+  static constexpr int HP = D / RP;
 };
 
 // 16-byte slot of logical column chunk c in row r is c ^ swz(r).
@@ -266,6 +269,47 @@ __device__ __forceinline__ void chunk(RowState<C::D>& st, const bf16x8 (&qf)[C::
     }
 }
 
+// First-order term of one unselected block j (per-block order): the stage
+// holds RP rows (value dims part * RP ..) of H_j^T in the K-chunk layout.
+//   alpha = exp2(c2 * q . kbar_j - m)  (q . kbar_j by v_dot2 over the lane's half
+//           of q and of the bf16 centroid, summed with the partner lane),
+//   acc[d] += scale * alpha * (q H_j)[d]  for the RP value dims of this part,
+// with q H_j as MFMAs: A = H_j^T rows from LDS, B = the query fragments.
+// alpha uses the current running max, as every other term added now.
+template <class C>
+__device__ __forceinline__ void first_order_part(RowState<C::D>& st, const bf16x8 (&qf)[C::KS],
+                                                 const char* stage, const Offsets<C>& off,
+                                                 float c2, float scale, const bf16* cen_j,
+                                                 int part, int hh) {
+  constexpr int MTP = C::RP / 32;                     // 32-row tiles per part
+  // bf16 -> fp32 by placing the 16 bits high (exact), then fp32 FMAs.  (v_dot2
+  // on 32-bit lanes of a bit-cast 128-bit vector is miscompiled to read one
+  // register pair for every lane.)
+  float dot = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const u32x4 kc = ld16(cen_j + 16 * ks + 8 * hh);
+    const u32x4 qq = __builtin_bit_cast(u32x4, qf[ks]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dot = fmaf(__uint_as_float(qq[e] << 16), __uint_as_float(kc[e] << 16), dot);
+      dot = fmaf(__uint_as_float(qq[e] & 0xffff0000u), __uint_as_float(kc[e] & 0xffff0000u), dot);
+    }
+  }
+  const float f = scale * fast_exp2(row_sum(dot) * c2 - st.m);
+  f32x16 hq[MTP];
+#pragma unroll
+  for (int mtl = 0; mtl < MTP; ++mtl) {
+    hq[mtl] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      hq[mtl] = mfma32(as_bf16x8(ld16(stage + mtl * 32 * C::RB + off.koff[ks])), qf[ks], hq[mtl]);
+  }
+  // acc tile mt belongs to part mt / MTP; the other parts' tiles get a zero factor
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) st.acc[mt] += (mt / MTP == part ? f : 0.f) * hq[mt % MTP];
+}
+
 // fp32 statistics -> bf16 chunk of CK centroids / value sums in the stage
 // layout (used when no bf16 pack was supplied); rows past nb are zero.
 template <class C>
@@ -316,6 +360,7 @@ struct AttnPtrs {
   const bf16* pk_cen;
   const bf16* pk_vsum;
   const bf16* pk_hbart;
+  const bf16* ht;        // H_j^T per block, bf16 [bh][nb][D][D] (per-block first order)
   bf16* O;
 };
 
@@ -323,13 +368,14 @@ constexpr int kBitWords = (kMaxBlocks + 128) / 32;
 
 template <class C>
 __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kmax, int approx,
-                                                             float scale, int nb) {
+                                                             int order, float scale, int nb) {
   constexpr int D = C::D, BLK = C::BLK, CK = C::CK;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDSB];
   __shared__ unsigned bits[kBitWords];
-  __shared__ short s_list[kMaxBlocks];                 // exact block ids of S_i, in order
+  __shared__ short s_list[kMaxBlocks];                 // exact block ids of S_i, in order;
+                                                       // then (per-block first order) U_i
   __shared__ short s_clist[kBitWords];                 // centroid chunks to sweep
-  __shared__ int s_cnt[2];
+  __shared__ int s_cnt[3];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q32 = lane & 31, hh = lane >> 5;
@@ -341,6 +387,7 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
   const bf16* Vh = p.V + (size_t)bh * L * D;
   const int32_t* row = p.idx + ((size_t)bh * nb + i) * kmax;
   const bool packed = approx && p.pk_cen != nullptr;
+  const bool first = approx && order == kOrderFirst && packed && p.ht != nullptr;
 
   if (approx) {
     // bit j set: block j is exact (in S_i) or padding (j >= nb)
@@ -400,19 +447,33 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
       if (need) s_clist[ccnt + __popcll(m & ((1ull << lane) - 1))] = (short)tcv;
       ccnt += __popcll(m);
     }
+    int ucnt = 0;
+    if (first) {
+      // unselected blocks (bit clear), ascending, after the exact ids
+      for (int c0 = 0; c0 < nb; c0 += 64) {
+        const int j = c0 + lane;
+        const bool u = j < nb && !((bits[j >> 5] >> (j & 31)) & 1u) && cnt + ucnt + lane < kMaxBlocks;
+        const unsigned long long m = __ballot(u);
+        if (u) s_list[cnt + ucnt + __popcll(m & ((1ull << lane) - 1))] = (short)j;
+        ucnt += __popcll(m);
+      }
+    }
     if (lane == 0) {
       s_cnt[0] = cnt;
       s_cnt[1] = ccnt;
+      s_cnt[2] = ucnt;
     }
   }
   __syncthreads();
-  const int nex = s_cnt[0] * SPB, ntot = nex + s_cnt[1];
+  const int ncnt = s_cnt[0];
+  const int nex = ncnt * SPB, ncen = nex + s_cnt[1], ntot = ncen + s_cnt[2] * C::HP;
   const int ws = __builtin_amdgcn_readfirstlane(w);
   const unsigned lds_m0 = (unsigned)(uintptr_t)(lvoid*)lds;
   const char* Kb = reinterpret_cast<const char*>(Kh);
   const char* Vb = reinterpret_cast<const char*>(Vh);
   const char* Cb = packed ? reinterpret_cast<const char*>(p.pk_cen + (size_t)bh * nbp * D) : nullptr;
   const char* Sb = packed ? reinterpret_cast<const char*>(p.pk_vsum + (size_t)bh * nbp * D) : nullptr;
+  const char* Hb = first ? reinterpret_cast<const char*>(p.ht + (size_t)bh * nb * D * D) : nullptr;
   // copy chunk t into stage t & 1
   auto issue = [&](int t) {
     const unsigned m0 = lds_m0 + (unsigned)((t & 1) * C::STB);
@@ -420,10 +481,16 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
       const int j = __builtin_amdgcn_readfirstlane((int)s_list[t / SPB]);
       const size_t off = ((size_t)j * BLK + (size_t)(t % SPB) * CK) * C::RB;
       dma_stage<C>(Kb + off, Vb + off, m0, ws, loff);
-    } else {
+    } else if (t < ncen) {
       const int tcv = __builtin_amdgcn_readfirstlane((int)s_clist[t - nex]);
       const size_t off = (size_t)tcv * CK * C::RB;
       dma_stage<C>(Cb + off, Sb + off, m0, ws, loff);
+    } else {
+      // rows part * RP .. of H_j^T; with RP = D < 2 CK the second half repeats them
+      const int hc = t - ncen;
+      const int j = __builtin_amdgcn_readfirstlane((int)s_list[ncnt + hc / C::HP]);
+      const char* g = Hb + ((size_t)j * D + (size_t)(hc % C::HP) * C::RP) * C::RB;
+      dma_stage<C>(g, (2 * CK <= D) ? g + CK * C::RB : g, m0, ws, loff);
     }
   };
   if (ntot > 0) issue(0);
@@ -434,12 +501,21 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
     if (t + 1 < ntot) issue(t + 1);
     chunk<C, false>(st, qf, lds + (t & 1) * C::STB, off, c2, hh, bits, 0);
   }
-  for (; t < ntot; ++t) {                   // stage 2: centroid / value-sum chunks
+  for (; t < ncen; ++t) {                   // stage 2: centroid / value-sum chunks
     wait_vm0();
     __syncthreads();
     if (t + 1 < ntot) issue(t + 1);
     const int jbase = (int)s_clist[t - nex] * CK;
     chunk<C, true>(st, qf, lds + (t & 1) * C::STB, off, c2, hh, bits, jbase);
+  }
+  for (; t < ntot; ++t) {                   // per-block first order: H_j^T parts
+    wait_vm0();
+    __syncthreads();
+    if (t + 1 < ntot) issue(t + 1);
+    const int hc = t - ncen;
+    const int j = (int)s_list[ncnt + hc / C::HP];
+    first_order_part<C>(st, qf, lds + (t & 1) * C::STB, off, c2, scale,
+                        p.pk_cen + ((size_t)bh * nbp + j) * D, hc % C::HP, hh);
   }
 
   if (approx) {
@@ -454,6 +530,8 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
         chunk<C, true>(st, qf, lds, off, c2, hh, bits, j0);
       }
     }
+  }
+  if (approx && order == kOrderMixed) {
     // ---- stage 3: global first-order correction, acc += scale * (q Hbar) * sum alpha
     const float atot = row_sum(st.a);
     const float f = scale * atot;
@@ -511,9 +589,9 @@ hipError_t launch_t(const AttnArgs& a) {
   const bf16* pk = static_cast<const bf16*>(a.packed);
   AttnPtrs p{(const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.idx, a.centroid, a.vsum,
              a.hbar, pk, pk ? pk + (size_t)a.bh * nbp * C::D : nullptr,
-             pk ? pk + (size_t)2 * a.bh * nbp * C::D : nullptr, (bf16*)a.O};
+             pk ? pk + (size_t)2 * a.bh * nbp * C::D : nullptr, (const bf16*)a.ht, (bf16*)a.O};
   hipLaunchKernelGGL((attn_bf16_kernel<C>), dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax,
-                     a.approx, a.scale, a.nb);
+                     a.approx, a.order, a.scale, a.nb);
   return hipGetLastError();
 }
 

@@ -19,8 +19,8 @@ template <int D>
 __global__ __launch_bounds__(128) void attn_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const int32_t* __restrict__ idx, int kmax, const float* __restrict__ centroid,
-    const float* __restrict__ vsum, const float* __restrict__ hbar, int approx, float scale,
-    float* __restrict__ O, int nb, int BLK) {
+    const float* __restrict__ vsum, const float* __restrict__ hbar, const float* __restrict__ H,
+    int approx, int order, float scale, float* __restrict__ O, int nb, int BLK) {
   __shared__ float kt[CH][D];
   __shared__ float vt[CH][D];
   __shared__ unsigned bits[kMaxBlocks / 32];
@@ -121,12 +121,12 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
       __syncthreads();
       consume(true, j0, min(CH, nb - j0));
     }
-    // stage 3: acc += scale * asum * (q Hbar), Hbar rows staged CH at a time
-    const float* hb = hbar + (size_t)bh * D * D;
-    const float f = scale * asum;
+  }
+  // acc += f * (q G) for a d x d matrix G (row = key dim), rows staged CH at a time
+  auto add_qG = [&](const float* G, float f) {
     for (int r0 = 0; r0 < D; r0 += CH) {
       __syncthreads();
-      for (int t = tid; t < CH * D; t += BLK) kt[t / D][t % D] = hb[(size_t)(r0 + t / D) * D + t % D];
+      for (int t = tid; t < CH * D; t += BLK) kt[t / D][t % D] = G[(size_t)(r0 + t / D) * D + t % D];
       __syncthreads();
 #pragma unroll
       for (int n = 0; n < CH; ++n) {
@@ -134,6 +134,22 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
 #pragma unroll
         for (int c = 0; c < D; ++c) acc[c] = fmaf(fq, kt[n][c], acc[c]);
       }
+    }
+  };
+  if (approx && order == kOrderMixed) {
+    // stage 3: acc += scale * asum * (q Hbar)
+    add_qG(hbar + (size_t)bh * D * D, scale * asum);
+  }
+  if (approx && order == kOrderFirst) {
+    // per-block first order: acc += scale * alpha_j * (q H_j) for every j outside S_i,
+    // alpha_j = e^{q kbar_j} against the running max (the same shift as every term)
+    const float* cen = centroid + (size_t)bh * nb * D;
+    for (int j = 0; j < nb; ++j) {
+      if ((bits[j >> 5] >> (j & 31)) & 1u) continue;
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) s = fmaf(q[c], cen[(size_t)j * D + c], s);
+      add_qG(H + ((size_t)bh * nb + j) * D * D, scale * exp2f(s * c2 - m));
     }
   }
 
@@ -147,7 +163,8 @@ template <int D>
 hipError_t attn_f32_t(const AttnArgs& a) {
   hipLaunchKernelGGL((attn_f32_kernel<D>), dim3(a.bh * a.nb), dim3(a.BLK), 0, a.stream,
                      (const float*)a.Q, (const float*)a.K, (const float*)a.V, a.idx, a.kmax,
-                     a.centroid, a.vsum, a.hbar, a.approx, a.scale, (float*)a.O, a.nb, a.BLK);
+                     a.centroid, a.vsum, a.hbar, a.H, a.approx, a.order, a.scale, (float*)a.O,
+                     a.nb, a.BLK);
   return hipGetLastError();
 }
 

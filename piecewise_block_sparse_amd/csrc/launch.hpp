@@ -17,7 +17,10 @@ struct AttnArgs {
   const float* vsum;
   const float* hbar;
   const void* packed;   // nullable bf16 pack of the statistics
-  int approx;
+  const void* ht;       // bf16 H_j^T per block (FIRST order, bf16 path)
+  const float* H;       // fp32 H_j per block (FIRST order, fp32 path)
+  int approx;           // 0: keep-or-drop, 1: add the unselected blocks
+  int order;            // with approx: kOrderMixed / kOrderZeroth / kOrderFirst
   float scale;
   void* O;
   int bh;   // batch * heads
@@ -36,6 +39,7 @@ struct StatsArgs {
   float* hbar;
   float* M;
   void* packed;  // nullable bf16 pack of the statistics
+  void* ht;      // nullable bf16 H_j^T per block
   void* ws;
   int bh;
   int nb;
@@ -58,6 +62,11 @@ struct RouteArgs {
   int BLK;
   hipStream_t stream;
 };
+
+// first-order treatment of the unselected blocks
+constexpr int kOrderMixed = 0;    // global Hbar correction
+constexpr int kOrderZeroth = 1;   // none
+constexpr int kOrderFirst = 2;    // per-block H_j
 
 // largest nb (= L / block) the kernels accept
 constexpr int kMaxBlocks = 2048;

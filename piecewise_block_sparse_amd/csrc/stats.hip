@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void stats_bf16_kernel(
     const bf16* __restrict__ K, const bf16* __restrict__ V, int nb, float* __restrict__ centroid,
     float* __restrict__ vsum, float* __restrict__ partial, const float* __restrict__ hbar,
     float* __restrict__ M, float* __restrict__ Hout, bf16* __restrict__ pk_cen,
-    bf16* __restrict__ pk_vsum) {
+    bf16* __restrict__ pk_vsum, bf16* __restrict__ Ht) {
   using C = SCfg<D, BLK>;
   __shared__ __attribute__((aligned(16))) bf16 Kt[D * C::ROW];
   __shared__ __attribute__((aligned(16))) bf16 Vt[D * C::ROW];
@@ -184,6 +184,20 @@ __global__ __launch_bounds__(256) void stats_bf16_kernel(
             sq += dlt * dlt;
             if (Hj) Hj[(32 * (mt0 + a) + 8 * (r / 4) + 4 * hh + (r % 4)) * D + 32 * (nt0 + b) + q32] = x;
           }
+      if (Ht) {
+        // H_j^T in bf16: row = value dim, 4 consecutive key-dim columns per store
+        bf16* Hj = Ht + ((size_t)bh * nb + j) * D * D;
+#pragma unroll
+        for (int a = 0; a < C::TM; ++a)
+#pragma unroll
+          for (int b = 0; b < C::TM; ++b)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const f32x16& x = acc[a][b];
+              const u32x2 v = {pack2(x[4 * g4], x[4 * g4 + 1]), pack2(x[4 * g4 + 2], x[4 * g4 + 3])};
+              st8(Hj + (size_t)(32 * (nt0 + b) + q32) * D + 32 * (mt0 + a) + 8 * g4 + 4 * hh, v);
+            }
+      }
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
       if (lane == 0) s_red[w] = sq;
@@ -321,7 +335,8 @@ hipError_t stats_bf16_t(const StatsArgs& a) {
   const int grid = a.bh * ngrp;
   hipLaunchKernelGGL((stats_bf16_kernel<D, BLK, false>), dim3(grid), dim3(256), 0, a.stream,
                      (const bf16*)a.K, (const bf16*)a.V, a.nb, a.centroid, a.vsum, parts,
-                     (const float*)nullptr, (float*)nullptr, (float*)nullptr, pk_cen, pk_vsum);
+                     (const float*)nullptr, (float*)nullptr, (float*)nullptr, pk_cen, pk_vsum,
+                     (bf16*)nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int total = a.bh * D * D;
@@ -333,7 +348,7 @@ hipError_t stats_bf16_t(const StatsArgs& a) {
   hipLaunchKernelGGL((stats_bf16_kernel<D, BLK, true>), dim3(grid), dim3(256), 0, a.stream,
                      (const bf16*)a.K, (const bf16*)a.V, a.nb, (float*)nullptr, (float*)nullptr,
                      (float*)nullptr, (const float*)a.hbar, a.M, a.H, (bf16*)nullptr,
-                     (bf16*)nullptr);
+                     (bf16*)nullptr, static_cast<bf16*>(a.ht));
   return hipGetLastError();
 }
 

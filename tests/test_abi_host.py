@@ -106,9 +106,32 @@ def test_attention_arguments(lib):
     s = shape()
     assert att(lib, s, kmax=0) == 3
     assert att(lib, s, kmax=17) == 3
-    assert att(lib, s, mode=2) == 3
+    assert att(lib, s, mode=4) == 3
+    assert att(lib, s, mode=-1) == 3
     assert att(lib, s, scale=float("nan")) == 3
     assert att(lib, s, scale=-0.5) == 3
     assert att(lib, s, O=None) == 1
     assert att(lib, s, st=stats(full=False)) == 1                  # APPROX needs centroids
-    assert b"APPROX" in lib.pisa_last_error()
+    assert b"centroid" in lib.pisa_last_error()
+    for m in (_lib.MODE_ZEROTH, _lib.MODE_FIRST):
+        assert att(lib, s, mode=m, st=stats(full=False)) == 1
+    p = FAKE.value
+    no_hbar = _lib.PisaStats(p, p, None, None, p, p, p)
+    assert att(lib, s, mode=_lib.MODE_APPROX, st=no_hbar) == 1     # APPROX needs Hbar
+    assert b"Hbar" in lib.pisa_last_error()
+    no_ht = _lib.PisaStats(p, p, p, p, p, p, None)
+    assert att(lib, s, mode=_lib.MODE_FIRST, st=no_ht) == 1        # bf16 FIRST needs Ht
+    assert b"Ht" in lib.pisa_last_error()
+    no_pack = _lib.PisaStats(p, p, p, p, p, None, p)
+    assert att(lib, s, mode=_lib.MODE_FIRST, st=no_pack) == 1      # ... and the bf16 pack
+    f = shape(dtype=_lib.DTYPE_FP32)
+    no_h = _lib.PisaStats(p, p, None, p, p, None, p)
+    assert att(lib, f, mode=_lib.MODE_FIRST, st=no_h) == 1         # fp32 FIRST needs H
+    assert b"needs stats H" in lib.pisa_last_error()
+
+
+def test_precompute_Ht_is_bf16_only(lib):
+    p = FAKE.value
+    out = _lib.PisaStats(p, p, None, p, p, None, p)
+    assert pre(lib, shape(dtype=_lib.DTYPE_FP32), out=out) == 3
+    assert b"Ht" in lib.pisa_last_error()

@@ -123,6 +123,43 @@ def test_attention_parity(torch, wid, mode):
     print(f"{w.name}/{mode}: rel-L2 {err:.3e} max-abs {mab:.3e}")
 
 
+ORDER_MODES = {"zeroth": oracle.MODE_ZEROTH, "first": oracle.MODE_FIRST}
+
+
+@pytest.mark.parametrize("mode", ["zeroth", "first"])
+@pytest.mark.parametrize("wid", [1, 2, 5, 3, 4])
+def test_attention_orders_parity(torch, wid, mode):
+    """The zeroth-order and the per-block first-order treatments of the
+    unselected blocks, against the oracle's expansions of the same order."""
+    pisa = pisa_mod()
+    w, Q, K, V, Qd, Kd, Vd = inputs(wid)
+    bf = w.dtype == "bf16"
+    st = pisa.precompute(Kd, Vd, w.block, store_H=(mode == "first" and not bf),
+                         store_Ht=(mode == "first" and bf))
+    idx = _idx_for(pisa, w, Qd, st)
+    out = pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode=mode)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    heads = SAMPLE_HEADS[wid] or list(range(w.heads))
+    Qs, Ks, Vs = Q[:, heads], K[:, heads], V[:, heads]
+    ref_st = oracle.precompute(Ks, Vs, w.block)
+    qb = None if SAMPLE_HEADS[wid] is None else sample_qblocks(w, heads, per_head=4)
+    ref = oracle.attention(Qs, Ks, Vs, idx_np[:, heads], ref_st["centroid"], ref_st["vsum"],
+                           ref_st["Hbar"], ORDER_MODES[mode], w.scale, w.block, qblocks=qb,
+                           H=ref_st["H"])
+    err, mab = check_attention(to_np(out)[:, heads], ref, w.dtype, name=f"{w.name}/{mode}")
+    print(f"{w.name}/{mode}: rel-L2 {err:.3e} max-abs {mab:.3e}")
+
+
+def test_first_order_Ht_pack_is_H_transposed(torch):
+    """The bf16 H_j^T pack equals the fp32 H_j transposed, rounded to bf16."""
+    pisa = pisa_mod()
+    w, Q, K, V, Qd, Kd, Vd = inputs(2)
+    st = pisa.precompute(Kd, Vd, w.block, store_H=True, store_Ht=True)
+    torch.cuda.synchronize()
+    assert torch.equal(st["Ht"], st["H"].transpose(-1, -2).to(torch.bfloat16))
+
+
 # ---------------------------------------------------------------- edge cases
 
 def _rand(torch, shape, dtype, seed):
@@ -149,18 +186,19 @@ def test_small_shapes_full_pipeline(torch, dtype, d, B, L, k):
     if dtype == "bf16":
         K = wl.round_bf16(K)
     Qd, Kd, Vd = (to_dev(x, dtype) for x in (Q, K, V))
-    st = pisa.precompute(Kd, Vd, B, store_H=True)
+    st = pisa.precompute(Kd, Vd, B, store_H=True, store_Ht=dtype == "bf16")
     idx = pisa.route(Qd, st, k, 0.05, B)
-    outs = {m: pisa.attention(Qd, Kd, Vd, idx, st, B, mode=m) for m in ("approx", "drop")}
+    modes = {"approx": oracle.MODE_APPROX, "drop": oracle.MODE_DROP, **ORDER_MODES}
+    outs = {m: pisa.attention(Qd, Kd, Vd, idx, st, B, mode=m) for m in modes}
     torch.cuda.synchronize()
     ref_st = oracle.precompute(K, V, B)
     check_stats(st, ref_st, name="small")
     scale = 1 / math.sqrt(d)
     scores = oracle.route_scores(Q, to_np(st["centroid"]), to_np(st["M"]), 0.05, B, scale)
     check_route(idx.cpu().numpy(), scores, k, name="small")
-    for m, code in (("approx", oracle.MODE_APPROX), ("drop", oracle.MODE_DROP)):
+    for m, code in modes.items():
         ref = oracle.attention(Q, K, V, idx.cpu().numpy(), ref_st["centroid"], ref_st["vsum"],
-                               ref_st["Hbar"], code, scale, B)
+                               ref_st["Hbar"], code, scale, B, H=ref_st["H"])
         check_attention(to_np(outs[m]), ref, dtype, name=f"small/{m}")
 
 
@@ -170,11 +208,12 @@ def test_density_one_equals_dense(torch):
     B, L, d = 64, 1024, 128
     Q, K, V = (_rand(torch, (1, 2, L, d), "bf16", s) for s in (5, 6, 7))
     Qd, Kd, Vd = (to_dev(x, "bf16") for x in (Q, K, V))
-    st = pisa.precompute(Kd, Vd, B)
+    st = pisa.precompute(Kd, Vd, B, store_Ht=True)
     nb = L // B
     idx = torch.arange(nb, dtype=torch.int32, device="cuda").expand(1, 2, nb, nb).contiguous()
     a = pisa.attention(Qd, Kd, Vd, idx, st, B, mode="approx")
     dr = pisa.attention(Qd, Kd, Vd, idx, st, B, mode="drop")
+    others = [pisa.attention(Qd, Kd, Vd, idx, st, B, mode=m) for m in ("zeroth", "first")]
     torch.cuda.synchronize()
     ref_st = oracle.precompute(K, V, B)
     ref = oracle.attention(Q, K, V, idx.cpu().numpy(), ref_st["centroid"], ref_st["vsum"],
@@ -182,6 +221,8 @@ def test_density_one_equals_dense(torch):
     check_attention(to_np(a), ref, "bf16", "dense/approx")
     check_attention(to_np(dr), ref, "bf16", "dense/drop")
     assert torch.equal(a, dr)
+    for o in others:
+        assert torch.equal(o, dr)
 
 
 def test_padding_empty_rows_and_out_of_range_ids(torch):
@@ -195,15 +236,16 @@ def test_padding_empty_rows_and_out_of_range_ids(torch):
     rows = [[3, -1, 5, -1], [-1, -1, -1, -1], [-1, 0, -1, 7], [1, 2, 3, 4],
             [6, 99, -1, -1], [0, -1, -1, -1], [-1, -1, -1, 2], [5, 6, 7, -1]]
     idx = torch.tensor(rows, dtype=torch.int32).reshape(1, 1, nb, 4).cuda()
-    st = pisa.precompute(Kd, Vd, B)
-    outs = {m: to_np(pisa.attention(Qd, Kd, Vd, idx, st, B, mode=m)) for m in ("approx", "drop")}
+    st = pisa.precompute(Kd, Vd, B, store_Ht=True)
+    modes = {"approx": oracle.MODE_APPROX, "drop": oracle.MODE_DROP, **ORDER_MODES}
+    outs = {m: to_np(pisa.attention(Qd, Kd, Vd, idx, st, B, mode=m)) for m in modes}
     torch.cuda.synchronize()
     clean = np.array([([j for j in r if 0 <= j < nb] + [-1] * 4)[:4] for r in rows],
                      dtype=np.int32).reshape(1, 1, nb, 4)
     ref_st = oracle.precompute(K, V, B)
-    for m, code in (("approx", oracle.MODE_APPROX), ("drop", oracle.MODE_DROP)):
+    for m, code in modes.items():
         ref = oracle.attention(Q, K, V, clean, ref_st["centroid"], ref_st["vsum"], ref_st["Hbar"],
-                               code, 1 / math.sqrt(d), B)
+                               code, 1 / math.sqrt(d), B, H=ref_st["H"])
         check_attention(outs[m], ref, "bf16", f"padding/{m}")
     assert np.all(outs["drop"][0, 0, B:2 * B] == 0.0)
 
