@@ -10,10 +10,12 @@ Prints ONE JSON line.  `value` is the algorithmic TFLOP/s of the whole step;
 `ms_per_step` its latency; `roofline` describes the fused attention kernel
 (the dominant one) against the bf16 MFMA peak; `phases` splits the step by
 kernel (HIP events on the launch stream); `dense` is the same kernel run with
-every block exact; `cpu_baseline` is the fp64 oracle on a bounded sample.
+every block exact; `orders` times the zeroth-order and the per-block
+first-order treatments of the unselected blocks on the same inputs;
+`cpu_baseline` is the fp64 oracle on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4|3]
-                    [--no-cpu-baseline] [--no-dense] [--copy-calibration]
+                    [--no-cpu-baseline] [--no-dense] [--no-orders] [--copy-calibration]
 """
 import argparse
 import json
@@ -41,8 +43,11 @@ def flops(w, k):
     approx = bh * L * (4 * d * (nb - k) + 2 * d * d)      # centroid logits + sigma sums + q Hbar
     stats = 2 * bh * nb * 2 * B * d * d                   # K_j^T V_j, two passes
     route = bh * nb * nb * 2 * d                          # pooled-q . kbar (fp64)
+    zeroth = bh * L * 4 * d * (nb - k)                     # approx without the q Hbar term
+    first_blocks = bh * L * 2 * d * d * (nb - k)          # q H_j for every unselected block
     return {"exact": exact, "approx": approx, "attention": exact + approx, "stats": stats,
-            "route": route, "step": exact + approx + stats + route}
+            "route": route, "step": exact + approx + stats + route,
+            "attention_zeroth": exact + zeroth, "attention_first": exact + zeroth + first_blocks}
 
 
 def bytes_moved(w):
@@ -160,6 +165,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-orders", action="store_true",
+                    help="skip timing the zeroth-order and per-block first-order modes")
     ap.add_argument("--no-exact-split", action="store_true",
                     help="skip the keep-or-drop timing that splits exact / approximate phases")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -186,7 +193,7 @@ def main():
         torch.cuda.synchronize()
         del x, y
 
-    def run(wid, steps, warmup, with_dense, split=True):
+    def run(wid, steps, warmup, with_dense, split=True, orders=False):
         w = wl.WORKLOADS[wid]
         log(f"{w.name}: generating inputs")
         Q, K, V = wl.make_inputs(w)
@@ -217,12 +224,27 @@ def main():
             fd = flops(w, nb)["exact"]
             res["dense"] = {"ms": t_dense, "tflops": fd / t_dense / 1e9,
                             "speedup_of_pisa_attention": t_dense / ph["attention"]}
+        if orders:
+            # the other treatments of the unselected blocks, same inputs and idx
+            log(f"{w.name}: zeroth-order and per-block first-order modes")
+            st_ht = pisa.precompute(Kd, Vd, w.block, store_Ht=True)
+            t0 = time_attention(pisa, torch, Qd, Kd, Vd, idx, st_ht, w, "zeroth", max(5, steps // 2))
+            t1 = time_attention(pisa, torch, Qd, Kd, Vd, idx, st_ht, w, "first", 3)
+            hbytes = w.batch * w.heads * w.nb * (w.nb - w.k) * w.head_dim ** 2 * 2
+            res["orders"] = {
+                "zeroth": {"ms": t0, "tflops": f["attention_zeroth"] / t0 / 1e9},
+                "first_per_block": {"ms": t1, "tflops": f["attention_first"] / t1 / 1e9,
+                                    "H_stream_gbs": hbytes / (t1 - t0) / 1e6},
+            }
+            res["gflop"]["attention_zeroth"] = f["attention_zeroth"] / 1e9
+            res["gflop"]["attention_first"] = f["attention_first"] / 1e9
+            del st_ht
         del Qd, Kd, Vd, st, idx
         torch.cuda.empty_cache()
         return w, res
 
     w, main_res = run(args.workload, args.steps, args.warmup, not args.no_dense,
-                      not args.no_exact_split)
+                      not args.no_exact_split, not args.no_orders)
     f = flops(w, w.k)
     ms = main_res["wall_ms_per_step"]
     t_attn = main_res["phases_ms"]["attention"]
