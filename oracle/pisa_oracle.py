@@ -23,7 +23,8 @@ Sources (cited by page title and section; no line numbers):
 
 Functions, one per call of the C ABI:
 
-* ``precompute(K, V, B)`` -> block centroids, value sums, per-block H_j, Hbar, M_j
+* ``precompute(K, V, B, norm="fro")`` -> block centroids, value sums, per-block
+  H_j, Hbar, M_j (``norm="spectral"``: the other reading of ||.||_2, below)
 * ``route(Q, centroid, M, k, lam, B, scale)`` -> per-query-block exact set S_i
   (``route_scores`` exposes the float64 scores it ranks)
 * ``attention(Q, K, V, idx, centroid, vsum, Hbar, mode, scale, B, H=None)`` -> O
@@ -56,7 +57,9 @@ Readings where the pages are silent or ambiguous:
 * Centroid = arithmetic mean of the block's B keys; value sum = plain sum.
 * H_j = sum_n (k_{j,n} - kbar_j)^T v_{j,n} is d_k x d_v; q Hbar is a row vector.
 * Hbar = mean of H_j over all blocks of the same (batch, head).
-* ||.||_2 of a matrix read as the Frobenius norm (entrywise 2-norm).
+* ||.||_2 of a matrix read as the Frobenius norm (entrywise 2-norm) by default;
+  ``norm="spectral"`` takes the operator 2-norm (largest singular value)
+  instead, the other standard meaning of the symbol.
 * Routing score: scale * qbar_i . kbar_j + lam * M_j with qbar_i the mean query
   of block i; the k largest are exact, ties go to the lower block index, and
   the set is returned in ascending order.  One S_i serves the whole query block.
@@ -88,15 +91,16 @@ def _blocks(X: np.ndarray, B: int) -> np.ndarray:
     return X.reshape(b, h, L // B, B, d)
 
 
-def precompute(K: np.ndarray, V: np.ndarray, B: int) -> dict:
+def precompute(K: np.ndarray, V: np.ndarray, B: int, norm: str = "fro") -> dict:
     """Block statistics of the PISA precompute stage.
 
     PISA page, section 2, "Core algorithm": the zeroth-order term of block j
     uses the block centroid kbar_j and the block value sum sum_n v_{j,n}; the
     first-order term uses H_j = sum_n (k_{j,n} - kbar_j)^T v_{j,n} and the
     global Hbar, the mean of H_j over all blocks.  "Covariance-aware routing":
-    M_j = ||H_j - Hbar||_2 (Frobenius reading).  "Hardware implementation":
-    these are computed before the attention stages.
+    M_j = ||H_j - Hbar||_2 (Frobenius reading, or with norm="spectral" the
+    largest singular value).  "Hardware implementation": these are computed
+    before the attention stages.
 
     Returns a dict of float64 arrays:
       centroid [b,h,nb,d], vsum [b,h,nb,d], H [b,h,nb,d,d] (row = key dim,
@@ -113,7 +117,12 @@ def precompute(K: np.ndarray, V: np.ndarray, B: int) -> dict:
     H = np.matmul(np.swapaxes(dev, -1, -2), Vb)
     Hbar = H.mean(axis=2)                           # mean over the nb blocks of this (b, h)
     diff = H - Hbar[:, :, None, :, :]
-    M = np.sqrt((diff * diff).sum(axis=(-2, -1)))   # Frobenius norm of H_j - Hbar
+    if norm == "fro":
+        M = np.sqrt((diff * diff).sum(axis=(-2, -1)))   # Frobenius norm of H_j - Hbar
+    elif norm == "spectral":
+        M = np.linalg.norm(diff, ord=2, axis=(-2, -1))  # largest singular value (LAPACK SVD)
+    else:
+        raise ValueError(f"unknown norm {norm!r}")
     return {"centroid": centroid, "vsum": vsum, "H": H, "Hbar": Hbar, "M": M}
 
 

@@ -581,3 +581,76 @@ def test_pins_catch_planted_first_order_mistakes():
     for name, Hm in mutants.items():
         bad = attention(*args, H=Hm)
         assert not np.allclose(bad[0, 0], ref, rtol=1e-6), name
+
+
+# ---------------------------------------------------------------- spectral M_j
+
+def diag34_blocks():
+    """Two blocks of B = 4 tokens, d = 2.  Block 0: key deviations e1, -e1, e2,
+    -e2 around a centroid, values 3 e1, 0, 4 e2, 0, so H_0 = diag(3, 4); block 1
+    has the values negated, so H_1 = -H_0, Hbar = 0 and H_j - Hbar = +-diag(3, 4):
+    spectral norm 4, Frobenius norm 5."""
+    e1, e2 = np.array([1.0, 0.0]), np.array([0.0, 1.0])
+    c0, c1 = np.array([0.3, -0.2]), np.array([-1.0, 0.5])
+    dev = np.stack([e1, -e1, e2, -e2])
+    K = np.concatenate([c0 + dev, c1 + dev])[None, None]
+    v0 = np.stack([3 * e1, 0 * e1, 4 * e2, 0 * e2])
+    V = np.concatenate([v0, -v0])[None, None]
+    return K, V
+
+
+def test_spectral_norm_closed_form():
+    K, V = diag34_blocks()
+    sp = precompute(K, V, 4, norm="spectral")
+    fr = precompute(K, V, 4)
+    assert np.allclose(sp["H"][0, 0, 0], np.diag([3.0, 4.0]), atol=1e-15)
+    assert np.allclose(sp["Hbar"], 0.0, atol=1e-15)
+    assert np.allclose(sp["M"], 4.0, rtol=1e-14)
+    assert np.allclose(fr["M"], 5.0, rtol=1e-14)
+
+
+def power_iteration_sigma(A, iters=3000):
+    """Largest singular value by plain power iteration on A^T A, pure Python."""
+    n = len(A)
+    x = [1.0 + 0.1 * i for i in range(n)]
+    lam = 0.0
+    for _ in range(iters):
+        y = [sum(A[r][c] * x[c] for c in range(n)) for r in range(n)]
+        z = [sum(A[r][c] * y[r] for r in range(n)) for c in range(n)]
+        nz = math.sqrt(sum(t * t for t in z))
+        lam = nz / math.sqrt(sum(t * t for t in x))
+        x = [t / nz for t in z]
+    return math.sqrt(lam)
+
+
+def test_spectral_norm_bruteforce_invariance_and_bounds():
+    """Tiny random blocks: spectral M equals a power-iteration brute force, is
+    unchanged by orthogonal rotations of the key and value spaces
+    (K -> K R, V -> V S turns H_j into R^T H_j S), and sits between
+    ||.||_F / sqrt(d) and ||.||_F."""
+    Q, K, V = rand_qkv(60, h=1, L=24, d=3)
+    B = 6
+    sp = precompute(K, V, B, norm="spectral")
+    fr = precompute(K, V, B)
+    diff = sp["H"] - sp["Hbar"][:, :, None]
+    for j in range(4):
+        assert math.isclose(sp["M"][0, 0, j], power_iteration_sigma(diff[0, 0, j].tolist()),
+                            rel_tol=1e-9)
+    g = np.random.default_rng(61)
+    R, _ = np.linalg.qr(g.standard_normal((3, 3)))
+    S, _ = np.linalg.qr(g.standard_normal((3, 3)))
+    rot = precompute(K @ R, V @ S, B, norm="spectral")
+    assert np.allclose(rot["M"], sp["M"], rtol=1e-12)
+    assert np.all(sp["M"] <= fr["M"] * (1 + 1e-12))
+    assert np.all(sp["M"] >= fr["M"] / math.sqrt(3) * (1 - 1e-12))
+    assert not np.allclose(sp["M"], fr["M"], rtol=1e-3)
+
+
+def test_spectral_is_an_option_not_a_change():
+    """The default (Frobenius) statistics and everything but M are unchanged by the option."""
+    Q, K, V = rand_qkv(62, h=1, L=64, d=8)
+    a, b = precompute(K, V, 8), precompute(K, V, 8, norm="spectral")
+    for key in ("centroid", "vsum", "H", "Hbar"):
+        assert np.array_equal(a[key], b[key])
+    with pytest.raises(ValueError):
+        precompute(K, V, 8, norm="nuclear")
