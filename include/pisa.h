@@ -73,6 +73,11 @@ typedef enum {
                                d x d matrix) */
 } pisa_mode;
 
+typedef enum {
+  PISA_NORM_FROBENIUS = 0,  /* M_j = ||H_j - Hbar||_F (entrywise 2-norm)                    */
+  PISA_NORM_SPECTRAL = 1    /* M_j = largest singular value of H_j - Hbar                  */
+} pisa_norm;
+
 typedef struct {
   int32_t batch;            /* b */
   int32_t heads;            /* h */
@@ -102,6 +107,10 @@ typedef struct {
                                (row = value dim, column = key dim), b*h*nb*d*d*2 bytes.
                                Written by pisa_precompute when non-NULL; required by
                                PISA_MODE_FIRST with bf16 inputs (fp32 inputs read H).       */
+  int32_t m_norm;           /* INPUT to pisa_precompute: pisa_norm used for M_j (the PISA
+                               summary, "Covariance-aware routing", writes ||.||_2 of a
+                               matrix; FROBENIUS is the default reading).  SPECTRAL with
+                               bf16 inputs needs H (it is computed from the stored H_j).    */
 } pisa_stats;
 
 /* Version of the library (PISA_VERSION at build time). */
@@ -130,7 +139,10 @@ size_t pisa_packed_size(const pisa_shape* shape);
  *
  *   K, V       [b,h,L,d] of shape->dtype (device, read only)
  *   out        centroid, vsum, Hbar, M required; H, packed and Ht optional (see
- *              pisa_stats; Ht must be NULL for fp32 inputs)
+ *              pisa_stats; Ht must be NULL for fp32 inputs); out->m_norm selects
+ *              the norm of M_j (SPECTRAL: 24 Lanczos steps on (H_j - Hbar)^T
+ *              (H_j - Hbar) per block, then the largest eigenvalue of the
+ *              tridiagonal by Sturm multisection in fp64)
  *   workspace  device scratch of at least pisa_workspace_size(shape) bytes,
  *              caller-owned; contents on entry are ignored
  *

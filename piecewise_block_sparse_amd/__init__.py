@@ -85,8 +85,11 @@ def workspace_size(X, block: int) -> int:
 
 
 def precompute(K, V, block: int, store_H: bool = False, workspace=None, packed: bool = True,
-               store_Ht: bool = False) -> dict:
+               store_Ht: bool = False, norm: str = "fro") -> dict:
     """Block statistics (fp32): centroid, vsum, Hbar, M, and H when store_H.
+
+    norm: "fro" (M_j = Frobenius norm of H_j - Hbar) or "spectral" (its largest
+    singular value; with bf16 inputs this also returns H, which it reads).
 
     For bf16 inputs (and packed=True) also the bf16 pack that the attention
     kernel streams in PISA mode (key "packed"), and with store_Ht the bf16
@@ -95,6 +98,9 @@ def precompute(K, V, block: int, store_H: bool = False, workspace=None, packed: 
     lib = _lib.load()
     _same(K, V)
     shp = _shape(K, block)
+    m_norm = {"fro": _lib.NORM_FROBENIUS, "spectral": _lib.NORM_SPECTRAL}[norm]
+    if m_norm == _lib.NORM_SPECTRAL and K.dtype == torch.bfloat16:
+        store_H = True
     b, h, L, d = K.shape
     nb = L // block if L % block == 0 else 0
     f32 = dict(dtype=torch.float32, device=K.device)
@@ -117,7 +123,8 @@ def precompute(K, V, block: int, store_H: bool = False, workspace=None, packed: 
     need = lib.pisa_workspace_size(ctypes.byref(shp))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=K.device)
-    st = _lib.PisaStats(*(_ptr(out[n]) for n in ("centroid", "vsum", "H", "Hbar", "M", "packed", "Ht")))
+    st = _lib.PisaStats(*(_ptr(out[n]) for n in ("centroid", "vsum", "H", "Hbar", "M", "packed", "Ht")),
+                        m_norm)
     _lib.check("pisa_precompute", lib.pisa_precompute(
         ctypes.byref(shp), _ptr(K), _ptr(V), ctypes.byref(st), _ptr(workspace),
         workspace.numel(), _stream(K)))

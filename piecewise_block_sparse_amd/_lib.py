@@ -19,6 +19,8 @@ MODE_APPROX = 0
 MODE_DROP = 1
 MODE_ZEROTH = 2
 MODE_FIRST = 3
+NORM_FROBENIUS = 0
+NORM_SPECTRAL = 1
 
 # every symbol the header declares
 EXPORTS = ("pisa_version", "pisa_status_string", "pisa_last_error", "pisa_workspace_size",
@@ -33,7 +35,7 @@ class PisaShape(ctypes.Structure):
 class PisaStats(ctypes.Structure):
     _fields_ = [("centroid", ctypes.c_void_p), ("vsum", ctypes.c_void_p), ("H", ctypes.c_void_p),
                 ("Hbar", ctypes.c_void_p), ("M", ctypes.c_void_p), ("packed", ctypes.c_void_p),
-                ("Ht", ctypes.c_void_p)]
+                ("Ht", ctypes.c_void_p), ("m_norm", ctypes.c_int32)]
 
 
 class PisaError(RuntimeError):

@@ -97,6 +97,11 @@ pisa_status pisa_precompute(const pisa_shape* shape, const void* K, const void* 
     return fail(PISA_ERR_NULL, "centroid, vsum, Hbar and M outputs are required");
   const bool bf = shape->dtype == PISA_DTYPE_BF16;
   if (!bf && out->Ht) return fail(PISA_ERR_ARG, "Ht (bf16 H_j^T) is for bf16 inputs only");
+  if (out->m_norm != PISA_NORM_FROBENIUS && out->m_norm != PISA_NORM_SPECTRAL)
+    return fail(PISA_ERR_ARG, "unknown m_norm %d", out->m_norm);
+  const bool spectral = out->m_norm == PISA_NORM_SPECTRAL;
+  if (spectral && bf && !out->H)
+    return fail(PISA_ERR_NULL, "the spectral M_j with bf16 inputs needs the H output");
   const bool needs_ws = bf || out->H == nullptr;
   if (needs_ws) {
     const size_t need = pisa_workspace_size(shape);
@@ -105,8 +110,8 @@ pisa_status pisa_precompute(const pisa_shape* shape, const void* K, const void* 
       return fail(PISA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   }
   pisa::StatsArgs a{K, V, out->centroid, out->vsum, out->H, out->Hbar, out->M,
-                    bf ? out->packed : nullptr, bf ? out->Ht : nullptr, workspace, bh, nb,
-                    shape->head_dim, shape->block, (hipStream_t)stream};
+                    bf ? out->packed : nullptr, bf ? out->Ht : nullptr, workspace,
+                    spectral ? 1 : 0, bh, nb, shape->head_dim, shape->block, (hipStream_t)stream};
   return hip_status(bf ? pisa::launch_stats_bf16(a) : pisa::launch_stats_f32(a), "pisa_precompute");
 }
 

@@ -41,6 +41,7 @@ struct StatsArgs {
   void* packed;  // nullable bf16 pack of the statistics
   void* ht;      // nullable bf16 H_j^T per block
   void* ws;
+  int spectral;  // M_j as the largest singular value (bf16 path: needs H)
   int bh;
   int nb;
   int D;

@@ -323,6 +323,162 @@ __global__ __launch_bounds__(256) void frob_kernel(const float* __restrict__ Hbu
   if (tid == 0) M[blockIdx.x] = sqrtf(s_red[0] + s_red[1] + s_red[2] + s_red[3]);
 }
 
+// ---- spectral reading of M_j = ||H_j - Hbar||_2: the largest singular value
+//
+// One workgroup per block.  A = H_j - Hbar is staged in LDS (rows padded to
+// D + 4 floats, so the row reads of A v are conflict-free 16-byte reads and the
+// column reads of A^T u conflict-free 4-byte reads).  kLanczos steps of plain
+// Lanczos on A^T A from a fixed start vector give a tridiagonal T whose largest
+// eigenvalue approximates sigma_max^2 from below; without reorthogonalisation
+// the extreme eigenvalue still converges (lost orthogonality only repeats
+// converged values).  Wave 0 then finds lambda_max(T) by multisection on Sturm
+// counts in fp64 (64 points per round, 6 rounds: 65^6 > 7e10), and
+// M_j = sqrt(lambda_max).
+// Reductions run in a fixed order, so the result is bitwise reproducible.
+constexpr int kLanczos = 24;
+
+template <int NT>
+__device__ __forceinline__ float block_sum(float x, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) s += red[i];
+  __syncthreads();
+  return s;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void spectral_kernel(const float* __restrict__ H,
+                                                       const float* __restrict__ hbar, int nb,
+                                                       float* __restrict__ M) {
+  constexpr int NT = 256, LD = D + 4, NH = NT / D, CW = D / NH;
+  __shared__ __attribute__((aligned(16))) float A[D * LD];
+  __shared__ __attribute__((aligned(16))) float v[D];
+  __shared__ float vp[D], u[D], part[NT], red[NT / 64];
+  __shared__ float s_al[kLanczos], s_be[kLanczos];
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x, bh = blk / nb;
+  const float* Hj = H + (size_t)blk * D * D;
+  const float* Hb = hbar + (size_t)bh * D * D;
+  for (int e = 4 * tid; e < D * D; e += 4 * NT) {
+    const f32x4 h = *reinterpret_cast<const f32x4*>(Hj + e);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(Hb + e);
+    *reinterpret_cast<f32x4*>(&A[(e / D) * LD + e % D]) = h - b;
+  }
+  const int r = tid % D, h = tid / D;            // row (or column) and which slice of it
+  float x0 = 0.f;
+  if (tid < D) x0 = 1.f + (float)((unsigned)tid * 2654435761u % 1024u) * (1.f / 1024.f);
+  const float n0 = block_sum<NT>(x0 * x0, red);
+  if (tid < D) {
+    v[tid] = x0 / sqrtf(n0);
+    vp[tid] = 0.f;
+  }
+  __syncthreads();
+  float beta = 0.f;
+  int kk = 0;
+  for (int it = 0; it < kLanczos; ++it) {
+    // u = A v: thread (r, h) sums columns h*CW .. h*CW + CW - 1 of row r
+    f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};             // four independent FMA chains
+    {
+      const float* Ar = &A[r * LD + h * CW];
+      const float* vv = &v[h * CW];
+#pragma unroll
+      for (int c = 0; c < CW; c += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(Ar + c);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(vv + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc4[e] = fmaf(a[e], b[e], acc4[e]);
+      }
+    }
+    part[tid] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    __syncthreads();
+    if (tid < D) {
+      float t = 0.f;
+#pragma unroll
+      for (int q = 0; q < NH; ++q) t += part[q * D + tid];
+      u[tid] = t;
+    }
+    __syncthreads();
+    // w = A^T u: thread (c = r, h) sums rows h*CW .. h*CW + CW - 1 of column c
+    acc4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int rr = h * CW; rr < h * CW + CW; rr += 4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc4[e] = fmaf(A[(rr + e) * LD + r], u[rr + e], acc4[e]);
+    }
+    part[tid] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    __syncthreads();
+    float w = 0.f, vc = 0.f;
+    if (tid < D) {
+#pragma unroll
+      for (int q = 0; q < NH; ++q) w += part[q * D + tid];
+      vc = v[tid];
+    }
+    const float alpha = block_sum<NT>(vc * w, red);
+    if (tid < D) w = w - alpha * vc - beta * vp[tid];
+    const float bnew = sqrtf(block_sum<NT>(w * w, red));
+    if (tid == 0) {
+      s_al[it] = alpha;
+      s_be[it] = bnew;
+    }
+    kk = it + 1;
+    if (!(bnew > 1e-6f * fabsf(alpha))) break;      // invariant subspace (or A = 0)
+    if (tid < D) {
+      vp[tid] = vc;
+      v[tid] = w / bnew;
+    }
+    beta = bnew;
+    __syncthreads();
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // lambda_max of the kk x kk tridiagonal (diag s_al, off-diag s_be) by
+    // multisection: count(x) = number of eigenvalues below x = number of
+    // negative pivots of T - x I; lanes with count < kk lie below lambda_max.
+    const int lane = tid;
+    double hi = 0.0;
+    for (int i = 0; i < kk; ++i) {
+      double g = fabs((double)s_al[i]);
+      if (i > 0) g += fabs((double)s_be[i - 1]);
+      if (i + 1 < kk) g += fabs((double)s_be[i]);
+      hi = fmax(hi, g);
+    }
+    double lo = 0.0;                               // A^T A is positive semidefinite
+    for (int round = 0; round < 6; ++round) {
+      const double step = (hi - lo) / 65.0;
+      const double x = lo + step * (lane + 1);
+      int cnt = 0;
+      double dd = 1.0;
+      for (int i = 0; i < kk; ++i) {
+        const double b2 = (i > 0) ? (double)s_be[i - 1] * (double)s_be[i - 1] : 0.0;
+        dd = ((double)s_al[i] - x) - (i > 0 ? b2 / dd : 0.0);
+        if (dd == 0.0) dd = -1e-300;
+        cnt += dd < 0.0;
+      }
+      const unsigned long long below = __ballot(cnt < kk);
+      if (below == 0ull) {
+        hi = lo + step;
+      } else {
+        const int l = 63 - __clzll(below);
+        const double nlo = lo + step * (l + 1);
+        hi = (l == 63) ? hi : lo + step * (l + 2);
+        lo = nlo;
+      }
+    }
+    if (lane == 0) M[blk] = (float)sqrt(0.5 * (lo + hi));
+  }
+}
+
+template <int D>
+hipError_t launch_spectral(const float* H, const float* hbar, int bh, int nb, float* M,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL((spectral_kernel<D>), dim3(bh * nb), dim3(256), 0, stream, H, hbar, nb, M);
+  return hipGetLastError();
+}
+
 template <int D, int BLK>
 hipError_t stats_bf16_t(const StatsArgs& a) {
   const int ngrp = (a.nb + kStatsGroup - 1) / kStatsGroup;
@@ -349,7 +505,9 @@ hipError_t stats_bf16_t(const StatsArgs& a) {
                      (const bf16*)a.K, (const bf16*)a.V, a.nb, (float*)nullptr, (float*)nullptr,
                      (float*)nullptr, (const float*)a.hbar, a.M, a.H, (bf16*)nullptr,
                      (bf16*)nullptr, static_cast<bf16*>(a.ht));
-  return hipGetLastError();
+  err = hipGetLastError();
+  if (err != hipSuccess || !a.spectral) return err;
+  return launch_spectral<D>(a.H, a.hbar, a.bh, a.nb, a.M, a.stream);
 }
 
 template <int D>
@@ -366,6 +524,7 @@ hipError_t stats_f32_t(const StatsArgs& a) {
                      (bf16*)nullptr, (bf16*)nullptr, a.nb);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (a.spectral) return launch_spectral<D>(Hbuf, a.hbar, a.bh, a.nb, a.M, a.stream);
   hipLaunchKernelGGL((frob_kernel<D>), dim3(grid), dim3(256), 0, a.stream, (const float*)Hbuf,
                      (const float*)a.hbar, a.nb, a.M);
   return hipGetLastError();

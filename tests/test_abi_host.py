@@ -130,6 +130,16 @@ def test_attention_arguments(lib):
     assert b"needs stats H" in lib.pisa_last_error()
 
 
+def test_precompute_norm_option(lib):
+    p = FAKE.value
+    bad = _lib.PisaStats(p, p, None, p, p, None, None, 7)
+    assert pre(lib, shape(), out=bad) == 3
+    assert b"m_norm" in lib.pisa_last_error()
+    spec_no_h = _lib.PisaStats(p, p, None, p, p, None, None, _lib.NORM_SPECTRAL)
+    assert pre(lib, shape(), out=spec_no_h) == 1                    # bf16 spectral reads H
+    assert b"needs the H output" in lib.pisa_last_error()
+
+
 def test_precompute_Ht_is_bf16_only(lib):
     p = FAKE.value
     out = _lib.PisaStats(p, p, None, p, p, None, p)
