@@ -239,6 +239,20 @@ def main():
             res["gflop"]["attention_zeroth"] = f["attention_zeroth"] / 1e9
             res["gflop"]["attention_first"] = f["attention_first"] / 1e9
             del st_ht
+            # the spectral reading of M_j (largest singular value) in the statistics
+            for _ in range(2):
+                st_sp = pisa.precompute(Kd, Vd, w.block, norm="spectral")
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(torch.cuda.current_stream())
+            for _ in range(3):
+                st_sp = pisa.precompute(Kd, Vd, w.block, norm="spectral")
+            b.record(torch.cuda.current_stream())
+            b.synchronize()
+            idx_sp = pisa.route(Qd, st_sp, w.k, w.lam, w.block)
+            same = (idx_sp.view(-1, w.k).unsqueeze(-1) == idx.view(-1, w.k).unsqueeze(-2)).any(-1)
+            res["spectral_M"] = {"precompute_ms": a.elapsed_time(b) / 3,
+                                 "routing_overlap_with_frobenius": float(same.float().mean())}
+            del st_sp, idx_sp, same
         del Qd, Kd, Vd, st, idx
         torch.cuda.empty_cache()
         return w, res
