@@ -65,6 +65,19 @@ Readings where the pages are silent or ambiguous:
   the set is returned in ascending order.  One S_i serves the whole query block.
 * Keep-or-drop with an empty S_i gives o_t = 0.
 
+Variable lengths (``seq_lens``, one valid length per batch entry).  The
+block-sparse notes pad each modality to a multiple of the block size
+(section 4.1) and pad a batch of different lengths to its longest sample
+(section 8.2) but never say what the padding does to the statistics.
+Reading: tokens at or beyond the valid length are not part of the sequence.
+Block j then holds n_j = clip(len - j B, 0, B) tokens and every statistic
+counts only those (centroid = their mean; the denominator weight of an
+unselected block is n_j alpha instead of B alpha); Hbar is the mean over the
+non-empty blocks; empty blocks are never routed (their M_j is reported as 0);
+a query block with no valid token gets an all -1 row; output rows of padding
+queries are 0.  If fewer than k blocks are non-empty, the row holds all of
+them followed by -1.
+
 All arithmetic is float64.  Inputs of any float dtype are upcast exactly.
 """
 
@@ -91,7 +104,17 @@ def _blocks(X: np.ndarray, B: int) -> np.ndarray:
     return X.reshape(b, h, L // B, B, d)
 
 
-def precompute(K: np.ndarray, V: np.ndarray, B: int, norm: str = "fro") -> dict:
+def _valid(seq_lens, b: int, nb: int, B: int) -> np.ndarray:
+    """Boolean [b, nb, B]: token n of block j of batch entry bi is in the sequence."""
+    L = nb * B
+    lens = np.full(b, L) if seq_lens is None else np.clip(np.asarray(seq_lens, dtype=np.int64), 0, L)
+    if lens.shape != (b,):
+        raise ValueError("seq_lens must hold one length per batch entry")
+    pos = np.arange(L).reshape(nb, B)
+    return pos[None] < lens[:, None, None]
+
+
+def precompute(K: np.ndarray, V: np.ndarray, B: int, norm: str = "fro", seq_lens=None) -> dict:
     """Block statistics of the PISA precompute stage.
 
     PISA page, section 2, "Core algorithm": the zeroth-order term of block j
@@ -105,17 +128,27 @@ def precompute(K: np.ndarray, V: np.ndarray, B: int, norm: str = "fro") -> dict:
     Returns a dict of float64 arrays:
       centroid [b,h,nb,d], vsum [b,h,nb,d], H [b,h,nb,d,d] (row = key dim,
       column = value dim), Hbar [b,h,d,d], M [b,h,nb].
+
+    seq_lens: optional valid length per batch entry (see the module notes);
+    only the n_j valid tokens of a block enter its statistics.
     """
     Kb = _blocks(K, B)
     Vb = _blocks(V, B)
     if Kb.shape != Vb.shape:
         raise ValueError("K and V must have the same shape")
-    centroid = Kb.mean(axis=3)                      # kbar_j: mean of the block's keys
-    vsum = Vb.sum(axis=3)                           # sum_n v_{j,n}
-    dev = Kb - centroid[:, :, :, None, :]           # k_{j,n} - kbar_j
+    b, _, nb, _, _ = Kb.shape
+    valid = _valid(seq_lens, b, nb, B)[:, None, :, :, None]        # [b,1,nb,B,1]
+    n = valid.sum(axis=3)                                          # n_j [b,1,nb,1]
+    Kv = np.where(valid, Kb, 0.0)                   # padding never enters (even NaN)
+    Vv = np.where(valid, Vb, 0.0)
+    centroid = Kv.sum(axis=3) / np.maximum(n, 1)    # kbar_j: mean of the block's keys
+    vsum = Vv.sum(axis=3)                           # sum_n v_{j,n}
+    dev = np.where(valid, Kb - centroid[:, :, :, None, :], 0.0)    # k_{j,n} - kbar_j
     # H_j[a, c] = sum_n dev[n, a] * v[n, c]: a (d x B) @ (B x d) product per block
-    H = np.matmul(np.swapaxes(dev, -1, -2), Vb)
-    Hbar = H.mean(axis=2)                           # mean over the nb blocks of this (b, h)
+    H = np.matmul(np.swapaxes(dev, -1, -2), Vv)
+    nonempty = n[..., 0] > 0                                       # [b,1,nb]
+    # Hbar: mean over the (non-empty) blocks of this (b, h)
+    Hbar = H.sum(axis=2) / np.maximum(nonempty.sum(axis=2), 1)[:, :, None, None]
     diff = H - Hbar[:, :, None, :, :]
     if norm == "fro":
         M = np.sqrt((diff * diff).sum(axis=(-2, -1)))   # Frobenius norm of H_j - Hbar
@@ -123,30 +156,42 @@ def precompute(K: np.ndarray, V: np.ndarray, B: int, norm: str = "fro") -> dict:
         M = np.linalg.norm(diff, ord=2, axis=(-2, -1))  # largest singular value (LAPACK SVD)
     else:
         raise ValueError(f"unknown norm {norm!r}")
+    M = np.where(nonempty, M, 0.0)                  # empty blocks are never routed
     return {"centroid": centroid, "vsum": vsum, "H": H, "Hbar": Hbar, "M": M}
 
 
 def route_scores(Q: np.ndarray, centroid: np.ndarray, M: np.ndarray, lam: float,
-                 B: int, scale: float) -> np.ndarray:
+                 B: int, scale: float, seq_lens=None) -> np.ndarray:
     """Routing scores (PISA page, section 2, "Covariance-aware routing"):
     score_ij = scale * qbar_i . kbar_j + lam * M_j, with qbar_i the mean of the
-    B queries of block i.  Returns float64 [b,h,nqb,nb]."""
+    B queries of block i.  Returns float64 [b,h,nqb,nb].
+
+    With seq_lens, qbar_i is the mean of block i's valid queries, and the score
+    is -inf for an empty key block and on every entry of an empty query block."""
     Qb = _blocks(Q, B)
     centroid = np.asarray(centroid, dtype=np.float64)
     M = np.asarray(M, dtype=np.float64)
-    qbar = Qb.mean(axis=3)                                          # [b,h,nqb,d]
-    return scale * np.matmul(qbar, np.swapaxes(centroid, -1, -2)) + lam * M[:, :, None, :]
+    b, _, nqb, _, _ = Qb.shape
+    valid = _valid(seq_lens, b, nqb, B)[:, None, :, :, None]
+    n = valid.sum(axis=3)                                           # [b,1,nqb,1]
+    qbar = np.where(valid, Qb, 0.0).sum(axis=3) / np.maximum(n, 1)  # [b,h,nqb,d]
+    sc = scale * np.matmul(qbar, np.swapaxes(centroid, -1, -2)) + lam * M[:, :, None, :]
+    empty = n[..., 0] == 0                                          # [b,1,nqb]
+    sc = np.where(empty[:, :, None, :], -np.inf, sc)                # empty key blocks
+    return np.where(empty[:, :, :, None], -np.inf, sc)             # empty query blocks
 
 
 def route(Q: np.ndarray, centroid: np.ndarray, M: np.ndarray, k: int, lam: float,
-          B: int, scale: float) -> np.ndarray:
+          B: int, scale: float, seq_lens=None) -> np.ndarray:
     """Covariance-aware top-k block selection (PISA page, section 2,
     "Covariance-aware routing").
 
     S_i = the k highest ``route_scores`` of query block i, ties broken towards
-    the lower block index; returned ascending as int32 [b,h,nqb,k].
+    the lower block index; returned ascending as int32 [b,h,nqb,k].  Blocks
+    with a -inf score (empty ones, with seq_lens) are never chosen; a row with
+    fewer than k candidates holds them all followed by -1.
     """
-    scores = route_scores(Q, centroid, M, lam, B, scale)
+    scores = route_scores(Q, centroid, M, lam, B, scale, seq_lens)
     b, h, nqb, nb = scores.shape
     if not (1 <= k <= nb):
         raise ValueError(f"k={k} must lie in [1, {nb}]")
@@ -157,13 +202,15 @@ def route(Q: np.ndarray, centroid: np.ndarray, M: np.ndarray, k: int, lam: float
             for i in range(nqb):
                 # sort by score descending, then block index ascending
                 order = np.lexsort((order_key, -scores[bi, hi, i]))
-                idx[bi, hi, i] = np.sort(order[:k])
+                top = np.sort([j for j in order[:k] if np.isfinite(scores[bi, hi, i, j])])
+                idx[bi, hi, i] = np.concatenate([top, -np.ones(k - len(top))]).astype(np.int32)
     return idx
 
 
 def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
               centroid: np.ndarray, vsum: np.ndarray, Hbar: np.ndarray,
-              mode: int, scale: float, B: int, qblocks=None, H=None) -> np.ndarray:
+              mode: int, scale: float, B: int, qblocks=None, H=None,
+              seq_lens=None) -> np.ndarray:
     """PISA exact-or-approximate attention, or keep-or-drop block-sparse attention.
 
     PISA page, section 2, "Core algorithm": o_t = N_t / D_t with
@@ -185,6 +232,9 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
     idx: int [b,h,nqb,kmax]; entries are block ids, -1 entries are padding.
     qblocks: optional iterable of (b, h, i) triples; only those query blocks are
       computed and every other output row is NaN.
+    seq_lens: optional valid length per batch entry: keys beyond it are not
+      attended, block j weighs n_j alpha in D_t, empty blocks are not in U_i,
+      and output rows of padding queries are 0.
     Returns float64 [b,h,L,d].
     """
     Qb = _blocks(Q, B)
@@ -203,6 +253,8 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
     b, h, nqb, _, d = Qb.shape
     nb = Kb.shape[2]
     dv = Vb.shape[-1]
+    valid = _valid(seq_lens, b, nb, B)                              # [b, nb, B]
+    count = valid.sum(axis=2)                                       # n_j [b, nb]
     out = np.full((b, h, nqb, B, dv), np.nan)
     if qblocks is None:
         qblocks = [(bi, hi, i) for bi in range(b) for hi in range(h) for i in range(nqb)]
@@ -210,21 +262,25 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
         row = [int(j) for j in idx[bi, hi, i] if j >= 0]
         if len(set(row)) != len(row) or any(j >= nb for j in row):
             raise ValueError(f"idx row ({bi},{hi},{i}) has duplicates or out-of-range ids")
-        S = sorted(row)
+        S = sorted(j for j in row if count[bi, j] > 0)               # empty blocks hold no key
         chosen = set(S)
-        U = [j for j in range(nb) if j not in chosen]
-        q = scale * Qb[bi, hi, i]                                    # [B, d]
-        # exact logits over the selected blocks' keys
-        KS = Kb[bi, hi, S].reshape(-1, d)                            # [|S|*B, d]
-        VS = Vb[bi, hi, S].reshape(-1, dv)
-        ell = q @ KS.T                                               # [B, |S|*B]
+        U = [j for j in range(nb) if j not in chosen and count[bi, j] > 0]
+        qv = valid[bi, i]                                            # valid query rows
+        out[bi, hi, i] = 0.0                                         # rows of padding queries
+        if not qv.any():
+            continue
+        q = scale * Qb[bi, hi, i][qv]                                # [n_i, d]
+        # exact logits over the selected blocks' valid keys
+        kv = valid[bi, S].reshape(-1)
+        KS = Kb[bi, hi, S].reshape(-1, d)[kv]                        # [sum n_j, d]
+        VS = Vb[bi, hi, S].reshape(-1, dv)[kv]
+        ell = q @ KS.T                                               # [n_i, sum n_j]
         if mode == MODE_DROP:
             if len(S) == 0:
-                out[bi, hi, i] = 0.0
                 continue
             m = ell.max(axis=1, keepdims=True)
             w = np.exp(ell - m)
-            out[bi, hi, i] = (w @ VS) / w.sum(axis=1, keepdims=True)
+            out[bi, hi, i, qv] = (w @ VS) / w.sum(axis=1, keepdims=True)
             continue
         # zeroth-order block terms over U_i: alpha_{t,j} = e^{q . kbar_j}
         c = q @ centroid[bi, hi, U].T                                # [B, |U|]
@@ -237,9 +293,10 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
         if mode == MODE_APPROX:
             N = N + (q @ Hbar[bi, hi]) * asum
         elif mode == MODE_FIRST and U:
-            # sum_j alpha_{t,j} (q_t H_j): one (B x d) @ (d x dv) product per block
-            qH = np.matmul(q[None, :, :], H[bi, hi, U])              # [|U|, B, dv]
+            # sum_j alpha_{t,j} (q_t H_j): one (n_i x d) @ (d x dv) product per block
+            qH = np.matmul(q[None, :, :], H[bi, hi, U])              # [|U|, n_i, dv]
             N = N + np.einsum("tj,jtc->tc", a, qH)
-        D = w.sum(axis=1, keepdims=True) + B * asum
-        out[bi, hi, i] = N / D
+        # a block of n_j tokens weighs n_j alpha in the denominator (B when full)
+        D = w.sum(axis=1, keepdims=True) + a @ count[bi, U].astype(np.float64)[:, None]
+        out[bi, hi, i, qv] = N / D
     return out.reshape(b, h, nqb * B, dv)

@@ -258,23 +258,28 @@ def equal_H_inputs(seed, eps, nb=6, B=8, d=4, L_q=None):
     return Q, K, V
 
 
-def taylor_bruteforce(Q, K, V, idx, B, s):
+def taylor_bruteforce(Q, K, V, idx, B, s, Lvalid=None):
     """Token-level first-order block Taylor expansion written from its
     definition: exact weights e^{q k} on S_i, weights
     e^{q kbar_j} (1 + q (k - kbar_j)) on every token of U_i; o = sum w v / sum w.
+    With Lvalid only tokens t < Lvalid exist (kbar_j is the mean of the block's
+    existing keys, empty blocks drop out) and later rows are 0.
     Pure Python loops; only for tiny inputs."""
     _, _, L, d = Q.shape
+    Lv = L if Lvalid is None else Lvalid
     nb = L // B
     out = np.zeros((L, d))
-    for t in range(L):
+    for t in range(Lv):
         i = t // B
         S = {int(j) for j in idx[0, 0, i] if j >= 0}
         q = [s * Q[0, 0, t, a] for a in range(d)]
         num = [0.0] * d
         den = 0.0
         for j in range(nb):
-            toks = range(j * B, (j + 1) * B)
-            kbar = [sum(K[0, 0, n, a] for n in toks) / B for a in range(d)]
+            toks = range(j * B, min((j + 1) * B, Lv))
+            if len(toks) == 0:
+                continue
+            kbar = [sum(K[0, 0, n, a] for n in toks) / len(toks) for a in range(d)]
             alpha = math.exp(sum(q[a] * kbar[a] for a in range(d)))
             for n in toks:
                 if j in S:
@@ -340,21 +345,25 @@ def het_inputs(seed, eps, nb=6, B=8, d=4):
     return Q, K, V
 
 
-def zeroth_bruteforce(Q, K, V, idx, B, s):
+def zeroth_bruteforce(Q, K, V, idx, B, s, Lvalid=None):
     """Token-level zeroth-order expansion from its definition: exact weights
-    e^{q k} on S_i, the weight e^{q kbar_j} on every token of a block of U_i.
+    e^{q k} on S_i, the weight e^{q kbar_j} on every token of a block of U_i
+    (with Lvalid: existing tokens only, as in taylor_bruteforce).
     Pure Python loops; only for tiny inputs."""
     _, _, L, d = Q.shape
+    Lv = L if Lvalid is None else Lvalid
     nb = L // B
     out = np.zeros((L, d))
-    for t in range(L):
+    for t in range(Lv):
         i = t // B
         S = {int(j) for j in idx[0, 0, i] if j >= 0}
         q = [s * Q[0, 0, t, a] for a in range(d)]
         num, den = [0.0] * d, 0.0
         for j in range(nb):
-            toks = range(j * B, (j + 1) * B)
-            kbar = [sum(K[0, 0, n, a] for n in toks) / B for a in range(d)]
+            toks = range(j * B, min((j + 1) * B, Lv))
+            if len(toks) == 0:
+                continue
+            kbar = [sum(K[0, 0, n, a] for n in toks) / len(toks) for a in range(d)]
             alpha = math.exp(sum(q[a] * kbar[a] for a in range(d)))
             for n in toks:
                 w = math.exp(sum(q[a] * K[0, 0, n, a] for a in range(d))) if j in S else alpha
@@ -654,3 +663,133 @@ def test_spectral_is_an_option_not_a_change():
         assert np.array_equal(a[key], b[key])
     with pytest.raises(ValueError):
         precompute(K, V, 8, norm="nuclear")
+
+
+# ---------------------------------------------------------------- variable lengths
+
+def varlen_inputs(seed, b=2, h=2, L=48, d=4, B=8):
+    Q, K, V = rand_qkv(seed, b=b, h=h, L=L, d=d)
+    K = K + np.repeat(np.random.default_rng(seed + 1).standard_normal((b, h, L // B, 1, d)),
+                      B, axis=3).reshape(K.shape)
+    return Q, K, V
+
+
+def runv(Q, K, V, idx, B, mode, scale, lens, st=None):
+    st = precompute(K, V, B, seq_lens=lens) if st is None else st
+    return attention(Q, K, V, idx, st["centroid"], st["vsum"], st["Hbar"], mode, scale, B,
+                     H=st["H"], seq_lens=lens)
+
+
+ALL_MODES = (MODE_APPROX, MODE_ZEROTH, MODE_FIRST, MODE_DROP)
+
+
+def test_varlen_full_lengths_are_the_plain_call():
+    Q, K, V = varlen_inputs(70)
+    B, nb, s = 8, 6, 0.5
+    idx = rand_idx(71, 2, 2, nb, nb, 2)
+    lens = [48, 48]
+    a, b_ = precompute(K, V, B), precompute(K, V, B, seq_lens=lens)
+    for key in a:
+        assert np.allclose(a[key], b_[key], rtol=1e-13, atol=1e-13)
+    for m in ALL_MODES:
+        assert np.allclose(run(Q, K, V, idx, B, m, s), runv(Q, K, V, idx, B, m, s, lens),
+                           rtol=1e-12, atol=1e-13)
+
+
+def test_varlen_density_one_is_sdpa_on_the_valid_prefix():
+    """Every non-empty block exact: each batch entry is dense attention over its
+    own valid tokens (torch SDPA on the truncated tensors); padding rows are 0."""
+    Q, K, V = varlen_inputs(72)
+    B, nb, s = 8, 6, 0.5
+    lens = [37, 16]                       # a partial block; an exact multiple of B
+    full = np.broadcast_to(np.arange(nb, dtype=np.int32), (2, 2, nb, nb)).copy()
+    for m in ALL_MODES:
+        out = runv(Q, K, V, full, B, m, s, lens)
+        for bi, n in enumerate(lens):
+            ref = sdpa(Q[bi:bi + 1, :, :n], K[bi:bi + 1, :, :n], V[bi:bi + 1, :, :n], s)
+            assert np.allclose(out[bi:bi + 1, :, :n], ref, rtol=1e-10, atol=1e-12), m
+            assert np.all(out[bi, :, n:] == 0.0)
+
+
+def test_varlen_drop_is_masked_sdpa():
+    Q, K, V = varlen_inputs(73)
+    B, nb, s = 8, 6, 0.5
+    lens = [37, 21]
+    idx = rand_idx(74, 2, 2, nb, nb, 3)
+    out = runv(Q, K, V, idx, B, MODE_DROP, s, lens)
+    mask = block_mask(idx, B, 48)
+    for bi, n in enumerate(lens):
+        mk = mask[bi:bi + 1, :, :n, :n]
+        ref = sdpa(Q[bi:bi + 1, :, :n], K[bi:bi + 1, :, :n], V[bi:bi + 1, :, :n], s, mask=mk)
+        rows = mk.any(axis=-1)                      # query rows with at least one valid key
+        got = out[bi:bi + 1, :, :n]
+        assert np.allclose(got[rows], ref[rows], rtol=1e-10, atol=1e-12)
+        assert np.all(got[~rows] == 0.0)
+
+
+@pytest.mark.parametrize("Lv", [37, 40, 33])
+def test_varlen_first_and_zeroth_equal_token_expansions(Lv):
+    """Ragged last block (and an empty one): the per-block first order and the
+    zeroth order equal their token-level expansions over the existing tokens."""
+    Q, K, V = het_inputs(75, 0.7)
+    B, nb, s = 8, 6, 0.5
+    idx = rand_idx(76, 1, 1, nb, nb, 2)
+    idx[0, 0, 0] = [4, 5]                          # the partial / empty block as exact
+    idx[0, 0, 1] = [0, 5]
+    out1 = runv(Q, K, V, idx, B, MODE_FIRST, s, [Lv])
+    out0 = runv(Q, K, V, idx, B, MODE_ZEROTH, s, [Lv])
+    assert np.allclose(out1[0, 0], taylor_bruteforce(Q, K, V, idx, B, s, Lv), rtol=1e-11, atol=1e-12)
+    assert np.allclose(out0[0, 0], zeroth_bruteforce(Q, K, V, idx, B, s, Lv), rtol=1e-11, atol=1e-12)
+
+
+def test_varlen_padding_contents_never_matter():
+    """NaN in every padding position: statistics and outputs are unchanged."""
+    Q, K, V = varlen_inputs(77)
+    B, nb, s = 8, 6, 0.5
+    lens = [37, 16]
+    idx = rand_idx(78, 2, 2, nb, nb, 2)
+    Qn, Kn, Vn = Q.copy(), K.copy(), V.copy()
+    for bi, n in enumerate(lens):
+        for X in (Qn, Kn, Vn):
+            X[bi, :, n:] = np.nan
+    a, b_ = precompute(K, V, B, seq_lens=lens), precompute(Kn, Vn, B, seq_lens=lens)
+    for key in a:
+        assert np.array_equal(a[key], b_[key]), key
+    for m in ALL_MODES:
+        assert np.array_equal(runv(Q, K, V, idx, B, m, s, lens), runv(Qn, Kn, Vn, idx, B, m, s, lens))
+
+
+def test_varlen_statistics_closed_forms():
+    """Partial block: centroid = mean of its valid keys; empty block: zero
+    statistics and M = 0; Hbar = mean of H_j over the non-empty blocks only."""
+    Q, K, V = varlen_inputs(79, b=1, h=1)
+    B = 8
+    st = precompute(K, V, B, seq_lens=[37])
+    assert np.allclose(st["centroid"][0, 0, 4], K[0, 0, 32:37].mean(axis=0), rtol=1e-14)
+    assert np.allclose(st["vsum"][0, 0, 4], V[0, 0, 32:37].sum(axis=0), rtol=1e-14)
+    dev = K[0, 0, 32:37] - K[0, 0, 32:37].mean(axis=0)
+    assert np.allclose(st["H"][0, 0, 4], dev.T @ V[0, 0, 32:37], rtol=1e-12, atol=1e-14)
+    assert np.all(st["centroid"][0, 0, 5] == 0) and np.all(st["H"][0, 0, 5] == 0)
+    assert st["M"][0, 0, 5] == 0.0
+    assert np.allclose(st["Hbar"][0, 0], st["H"][0, 0, :5].sum(axis=0) / 5, rtol=1e-13)
+
+
+def test_varlen_route_skips_empty_blocks():
+    """Empty key blocks are never chosen; a query block with no valid token gets
+    an all -1 row; with fewer than k non-empty blocks the row is padded with -1.
+    The rest is a plain sort of the prefix-pooled scores."""
+    Q, K, V = varlen_inputs(80)
+    B, nb, s = 8, 6, 0.5
+    lens = [37, 14]                                # entry 1: blocks 0 (8) and 1 (6) only
+    st = precompute(K, V, B, seq_lens=lens)
+    idx = route(Q, st["centroid"], st["M"], 3, 0.1, B, s, seq_lens=lens)
+    assert np.all(idx[0, :, :5] <= 4) and np.all(idx[0, :, 5] == -1)
+    assert np.all(idx[1, :, :2, :2] >= 0) and np.all(idx[1, :, :2, 2] == -1)
+    assert np.all(idx[1, :, 2:] == -1)
+    for hi in range(2):
+        for i in range(5):
+            toks = range(i * B, min((i + 1) * B, 37))
+            qbar = Q[0, hi, list(toks)].mean(axis=0)
+            sc = [s * qbar @ st["centroid"][0, hi, j] + 0.1 * st["M"][0, hi, j] for j in range(5)]
+            best = sorted(range(5), key=lambda j: (-sc[j], j))[:3]
+            assert list(idx[0, hi, i]) == sorted(best)
