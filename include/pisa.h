@@ -85,6 +85,19 @@ typedef struct {
   int32_t head_dim;         /* d: 64 or 128 (keys and values share it) */
   int32_t block;            /* B: 64 or 128 */
   int32_t dtype;            /* pisa_dtype of Q, K, V, O */
+  const int32_t* seq_lens;  /* NULLABLE device int32 [batch]: valid length of each sequence in
+                               its padded [L] buffer (values clamped to [0, L]).  Tokens at or
+                               beyond it are not part of the sequence: the statistics count the
+                               n_j = clip(len - j*block, 0, block) valid tokens of block j
+                               (centroid = their mean, Hbar = mean over non-empty blocks, M_j
+                               = 0 for empty blocks), routing never picks an empty block and
+                               pads a row with -1 when fewer than k blocks remain (an empty
+                               query block gets an all -1 row), attention skips padding keys,
+                               weighs an unselected block by n_j, and writes 0 to the rows of
+                               padding queries.  Padding contents are never read into a
+                               result.  (Block-sparse notes, sections 4.1 and 8.2: sequences
+                               are padded to a block multiple and batches to a common length.)
+                               NULL: every sequence has length L.                          */
 } pisa_shape;
 
 /* Block statistics, all float32 device arrays owned by the caller. */

@@ -14,7 +14,9 @@ unselected block; needs precompute(..., store_Ht=True) for bf16 inputs or
 store_H=True for fp32 inputs), "drop" (keep-or-drop block-sparse attention).
 
 Q, K, V: contiguous [b, h, L, d] CUDA tensors, bfloat16 or float32, L a
-multiple of `block`.
+multiple of `block`.  seq_lens (every call, optional): int32 CUDA tensor [b]
+with each sequence's valid length inside its padded buffer; the three calls
+must get the same lengths.
 """
 from __future__ import annotations
 
@@ -38,10 +40,14 @@ def _torch():
     return torch
 
 
-def _shape(X, block: int) -> _lib.PisaShape:
+def _shape(X, block: int, seq_lens=None) -> _lib.PisaShape:
     torch = _torch()
     if X.dim() != 4:
         raise ValueError("expected a [b, h, L, d] tensor")
+    if seq_lens is not None:
+        _expect(seq_lens, (X.shape[0],), torch.int32, "seq_lens")
+        if seq_lens.device != X.device:
+            raise ValueError("seq_lens must be on the device of the inputs")
     if X.dtype == torch.bfloat16:
         dt = _lib.DTYPE_BF16
     elif X.dtype == torch.float32:
@@ -49,7 +55,7 @@ def _shape(X, block: int) -> _lib.PisaShape:
     else:
         raise TypeError(f"unsupported dtype {X.dtype}")
     b, h, L, d = X.shape
-    return _lib.PisaShape(b, h, L, d, block, dt)
+    return _lib.PisaShape(b, h, L, d, block, dt, _ptr(seq_lens))
 
 
 def _ptr(t) -> int:
@@ -85,7 +91,7 @@ def workspace_size(X, block: int) -> int:
 
 
 def precompute(K, V, block: int, store_H: bool = False, workspace=None, packed: bool = True,
-               store_Ht: bool = False, norm: str = "fro") -> dict:
+               store_Ht: bool = False, norm: str = "fro", seq_lens=None) -> dict:
     """Block statistics (fp32): centroid, vsum, Hbar, M, and H when store_H.
 
     norm: "fro" (M_j = Frobenius norm of H_j - Hbar) or "spectral" (its largest
@@ -97,7 +103,7 @@ def precompute(K, V, block: int, store_H: bool = False, workspace=None, packed: 
     torch = _torch()
     lib = _lib.load()
     _same(K, V)
-    shp = _shape(K, block)
+    shp = _shape(K, block, seq_lens)
     m_norm = {"fro": _lib.NORM_FROBENIUS, "spectral": _lib.NORM_SPECTRAL}[norm]
     if m_norm == _lib.NORM_SPECTRAL and K.dtype == torch.bfloat16:
         store_H = True
@@ -131,11 +137,13 @@ def precompute(K, V, block: int, store_H: bool = False, workspace=None, packed: 
     return out
 
 
-def route(Q, stats: dict, k: int, lam: float, block: int, scale: float | None = None):
-    """Top-k exact blocks per query block, int32 [b, h, nb, k], rows ascending."""
+def route(Q, stats: dict, k: int, lam: float, block: int, scale: float | None = None,
+          seq_lens=None):
+    """Top-k exact blocks per query block, int32 [b, h, nb, k], rows ascending
+    (with seq_lens: -1 after the last candidate of a short row)."""
     torch = _torch()
     lib = _lib.load()
-    shp = _shape(Q, block)
+    shp = _shape(Q, block, seq_lens)
     b, h, L, d = Q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     idx = torch.empty((b, h, max(L // block, 0), max(k, 0)), dtype=torch.int32, device=Q.device)
@@ -149,14 +157,14 @@ def route(Q, stats: dict, k: int, lam: float, block: int, scale: float | None = 
 
 
 def attention(Q, K, V, idx, stats: dict | None, block: int, mode: int | str = "approx",
-              scale: float | None = None, out=None):
+              scale: float | None = None, out=None, seq_lens=None):
     """PISA block-sparse attention; mode "approx", "zeroth", "first" or "drop"."""
     torch = _torch()
     lib = _lib.load()
     _same(Q, K, V)
     if isinstance(mode, str):
         mode = _MODES[mode]
-    shp = _shape(Q, block)
+    shp = _shape(Q, block, seq_lens)
     d = Q.shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     b, h, L, _ = Q.shape

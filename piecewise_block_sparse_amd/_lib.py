@@ -29,7 +29,8 @@ EXPORTS = ("pisa_version", "pisa_status_string", "pisa_last_error", "pisa_worksp
 
 class PisaShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("seq_lens", ctypes.c_void_p)]
 
 
 class PisaStats(ctypes.Structure):

@@ -111,7 +111,8 @@ pisa_status pisa_precompute(const pisa_shape* shape, const void* K, const void* 
   }
   pisa::StatsArgs a{K, V, out->centroid, out->vsum, out->H, out->Hbar, out->M,
                     bf ? out->packed : nullptr, bf ? out->Ht : nullptr, workspace,
-                    spectral ? 1 : 0, bh, nb, shape->head_dim, shape->block, (hipStream_t)stream};
+                    spectral ? 1 : 0, bh, nb, shape->head_dim, shape->block, shape->seq_lens,
+                    shape->heads, (hipStream_t)stream};
   return hip_status(bf ? pisa::launch_stats_bf16(a) : pisa::launch_stats_f32(a), "pisa_precompute");
 }
 
@@ -127,7 +128,7 @@ pisa_status pisa_route(const pisa_shape* shape, const void* Q, const float* cent
   if (!std::isfinite(scale) || !std::isfinite(lambda))
     return fail(PISA_ERR_ARG, "scale and lambda must be finite");
   pisa::RouteArgs a{Q, centroid, M, k, scale, lambda, idx, bh, nb, shape->head_dim, shape->block,
-                    (hipStream_t)stream};
+                    shape->seq_lens, shape->heads, (hipStream_t)stream};
   const bool bf = shape->dtype == PISA_DTYPE_BF16;
   return hip_status(bf ? pisa::launch_route_bf16(a) : pisa::launch_route_f32(a), "pisa_route");
 }
@@ -167,7 +168,7 @@ pisa_status pisa_attention(const pisa_shape* shape, const void* Q, const void* K
                    (mode == PISA_MODE_FIRST && bf) ? stats->Ht : nullptr,
                    (mode == PISA_MODE_FIRST && !bf) ? stats->H : nullptr,
                    approx ? 1 : 0, order, scale, O, bh, nb, shape->head_dim, shape->block,
-                   (hipStream_t)stream};
+                   shape->seq_lens, shape->heads, (hipStream_t)stream};
   return hip_status(bf ? pisa::launch_attn_bf16(a) : pisa::launch_attn_f32(a), "pisa_attention");
 }
 

@@ -207,10 +207,14 @@ __device__ __forceinline__ float weights_bf16(const f32x16 (&s)[NKT], float c2, 
 // STAGE2: the keys are block centroids (values = block value sums); entries
 // whose block is in S_i or is padding (bit set in `bits`) are masked, and each
 // weight counts BLK times in the denominator.
+// Variable lengths: in stage 1 only the first kvalid keys of the chunk exist
+// (the rest get logit -inf); in stage 2 the block at chunk position jpart (if
+// >= 0) holds BLK - wmiss tokens, so its weight counts that many times.
 template <class C, bool STAGE2>
 __device__ __forceinline__ void chunk(RowState<C::D>& st, const bf16x8 (&qf)[C::KS],
                                       const char* stage, const Offsets<C>& off, float c2, int hh,
-                                      const unsigned* bits, int jbase) {
+                                      const unsigned* bits, int jbase, int kvalid = C::CK,
+                                      int jpart = -1, float wmiss = 0.f) {
   f32x16 s[C::NKT];
 #pragma unroll
   for (int kt = 0; kt < C::NKT; ++kt) {
@@ -227,6 +231,13 @@ __device__ __forceinline__ void chunk(RowState<C::D>& st, const bf16x8 (&qf)[C::
       for (int r = 0; r < 16; ++r)
         if ((wbits >> (8 * (r / 4) + (r % 4))) & 1u) s[kt][r] = -INFINITY;
     }
+  } else if (kvalid < C::CK) {
+    // keys past the sequence's end (key of register r: 32 kt + 8 (r / 4) + 4 hh + r % 4)
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * kt + 8 * (r / 4) + 4 * hh + (r % 4) >= kvalid) s[kt][r] = -INFINITY;
   }
   u32x4 pf[C::NSL];
   float ps = weights_bf16<C::NKT>(s, c2, -st.m, pf);
@@ -251,6 +262,17 @@ __device__ __forceinline__ void chunk(RowState<C::D>& st, const bf16x8 (&qf)[C::
   if (STAGE2) {
     st.l += (float)C::BLK * ps;
     st.a += ps;
+    if (jpart >= 0) {
+      // the ragged block weighs n_j = BLK - wmiss: take back wmiss times its
+      // (bf16) weight, recomputed exactly as weights_bf16 formed it
+      float sl = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < C::NKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kt + 8 * (r / 4) + 4 * hh + (r % 4) == jpart) sl = s[kt][r];
+      st.l -= wmiss * (float)(bf16)fast_exp2(fmaf(sl, c2, -st.m));
+    }
   } else {
     st.l += ps;
   }
@@ -366,9 +388,13 @@ struct AttnPtrs {
 
 constexpr int kBitWords = (kMaxBlocks + 128) / 32;
 
-template <class C>
+// VL: sequences have valid lengths (lens); without, the length code compiles away.
+// FO: the per-block first order (its stage lives only in these instantiations,
+// so the other modes keep their register budget).
+template <class C, bool VL, bool FO>
 __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kmax, int approx,
-                                                             int order, float scale, int nb) {
+                                                             int order, float scale, int nb,
+                                                             const int32_t* lens, int heads) {
   constexpr int D = C::D, BLK = C::BLK, CK = C::CK;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDSB];
   __shared__ unsigned bits[kBitWords];
@@ -387,20 +413,30 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
   const bf16* Vh = p.V + (size_t)bh * L * D;
   const int32_t* row = p.idx + ((size_t)bh * nb + i) * kmax;
   const bool packed = approx && p.pk_cen != nullptr;
-  const bool first = approx && order == kOrderFirst && packed && p.ht != nullptr;
+  // valid tokens: blocks j < nne are non-empty; query block i holds ni queries
+  const int Lv = VL ? valid_len(lens, bh, heads, (int)L) : (int)L;
+  const int nne = VL ? (Lv + BLK - 1) / BLK : nb;
+  const int ni = VL ? block_count(Lv, i, BLK) : BLK;
+  if (VL && ni == 0) {
+    // a query block past the sequence: its rows are 0
+    bf16* ob = p.O + ((size_t)bh * L + (size_t)i * BLK) * D;
+    for (int e = tid; e < BLK * D / 8; e += C::NT) st16(ob + 8 * e, u32x4{0u, 0u, 0u, 0u});
+    return;
+  }
+  const bool first = FO && approx && order == kOrderFirst && packed && p.ht != nullptr;
 
   if (approx) {
     // bit j set: block j is exact (in S_i) or padding (j >= nb)
     for (int e = tid; e < nbp / 32; e += C::NT) {
       const int lo = 32 * e;
-      unsigned pad = 0u;
-      if (lo + 32 > nb) pad = (lo >= nb) ? ~0u : (~0u << (nb - lo));
+      unsigned pad = 0u;                                 // padding and empty blocks: j >= nne
+      if (lo + 32 > nne) pad = (lo >= nne) ? ~0u : (~0u << (nne - lo));
       bits[e] = pad;
     }
     __syncthreads();
     for (int e = tid; e < kmax; e += C::NT) {
       const int j = row[e];
-      if (j >= 0 && j < nb) atomicOr(&bits[j >> 5], 1u << (j & 31));
+      if (j >= 0 && j < nne) atomicOr(&bits[j >> 5], 1u << (j & 31));
     }
     __syncthreads();
   }
@@ -411,6 +447,9 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
     const bf16* qrow = p.Q + ((size_t)bh * L + (size_t)i * BLK + 32 * w + q32) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_bf16x8(ld16(qrow + 16 * ks));
+    if (VL && 32 * w + q32 >= ni)                        // padding query: a zero row
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
   const Offsets<C> off = make_offsets<C>(lane);
   const DmaOff<C> loff = dma_lane_offsets<C>(w, lane);
@@ -432,7 +471,7 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
     for (int e0 = 0; e0 < kmax; e0 += 64) {
       const int e = e0 + lane;
       const int j = (e < kmax) ? row[e] : -1;
-      const bool ok = j >= 0 && j < nb;
+      const bool ok = j >= 0 && j < nne;
       const unsigned long long m = __ballot(ok);
       if (ok) s_list[cnt + __popcll(m & ((1ull << lane) - 1))] = (short)j;
       cnt += __popcll(m);
@@ -499,23 +538,39 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
     wait_vm0();
     __syncthreads();
     if (t + 1 < ntot) issue(t + 1);
-    chunk<C, false>(st, qf, lds + (t & 1) * C::STB, off, c2, hh, bits, 0);
+    // keys of this chunk inside the sequence (fewer only in a ragged last block)
+    const int kv = VL ? min(max(block_count(Lv, (int)s_list[t / SPB], BLK) - (t % SPB) * CK, 0), CK)
+                      : CK;
+    if (VL && kv < CK) {
+      // padding values must not reach the MFMA (0 * NaN): zero those V rows
+      char* vz = lds + (t & 1) * C::STB + C::SUBB;
+      for (int e = tid; e < (CK - kv) * C::CPR; e += C::NT)
+        st16(vz + (kv + e / C::CPR) * C::RB + 16 * (e % C::CPR), u32x4{0u, 0u, 0u, 0u});
+      __syncthreads();
+    }
+    chunk<C, false>(st, qf, lds + (t & 1) * C::STB, off, c2, hh, bits, 0, kv);
   }
+  // stage 2: the ragged last block (if any) weighs its n_j tokens
+  const int jrag = (VL && Lv % BLK != 0) ? nne - 1 : -1;
+  const float wmiss = (float)(BLK - (Lv - jrag * BLK));
   for (; t < ncen; ++t) {                   // stage 2: centroid / value-sum chunks
     wait_vm0();
     __syncthreads();
     if (t + 1 < ntot) issue(t + 1);
     const int jbase = (int)s_clist[t - nex] * CK;
-    chunk<C, true>(st, qf, lds + (t & 1) * C::STB, off, c2, hh, bits, jbase);
+    const int jp = (VL && jrag >= jbase && jrag < jbase + CK) ? jrag - jbase : -1;
+    chunk<C, true>(st, qf, lds + (t & 1) * C::STB, off, c2, hh, bits, jbase, CK, jp, wmiss);
   }
-  for (; t < ntot; ++t) {                   // per-block first order: H_j^T parts
-    wait_vm0();
-    __syncthreads();
-    if (t + 1 < ntot) issue(t + 1);
-    const int hc = t - ncen;
-    const int j = (int)s_list[ncnt + hc / C::HP];
-    first_order_part<C>(st, qf, lds + (t & 1) * C::STB, off, c2, scale,
-                        p.pk_cen + ((size_t)bh * nbp + j) * D, hc % C::HP, hh);
+  if (FO) {
+    for (; t < ntot; ++t) {                 // per-block first order: H_j^T parts
+      wait_vm0();
+      __syncthreads();
+      if (t + 1 < ntot) issue(t + 1);
+      const int hc = t - ncen;
+      const int j = (int)s_list[ncnt + hc / C::HP];
+      first_order_part<C>(st, qf, lds + (t & 1) * C::STB, off, c2, scale,
+                          p.pk_cen + ((size_t)bh * nbp + j) * D, hc % C::HP, hh);
+    }
   }
 
   if (approx) {
@@ -527,7 +582,8 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
         __syncthreads();
         stage_centroids<C>(cen, vs, j0, nb, lds, tid);
         __syncthreads();
-        chunk<C, true>(st, qf, lds, off, c2, hh, bits, j0);
+        const int jp = (VL && jrag >= j0 && jrag < j0 + CK) ? jrag - j0 : -1;
+        chunk<C, true>(st, qf, lds, off, c2, hh, bits, j0, CK, jp, wmiss);
       }
     }
   }
@@ -571,6 +627,7 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
   // ---- epilogue: o = N / D (0 when nothing was attended in keep-or-drop)
   const float ltot = row_sum(st.l);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  const bool live = !VL || 32 * w + q32 < ni;            // padding query rows are written 0
   bf16* orow = p.O + ((size_t)bh * L + (size_t)i * BLK + 32 * w + q32) * D;
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt)
@@ -578,6 +635,7 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
     for (int g4 = 0; g4 < 4; ++g4) {
       const f32x16& a = st.acc[mt];
       u32x2 pk = {pack2(a[4 * g4] * inv, a[4 * g4 + 1] * inv), pack2(a[4 * g4 + 2] * inv, a[4 * g4 + 3] * inv)};
+      if (!live) pk = u32x2{0u, 0u};
       st8(orow + 32 * mt + 8 * g4 + 4 * hh, pk);
     }
 }
@@ -590,8 +648,11 @@ hipError_t launch_t(const AttnArgs& a) {
   AttnPtrs p{(const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.idx, a.centroid, a.vsum,
              a.hbar, pk, pk ? pk + (size_t)a.bh * nbp * C::D : nullptr,
              pk ? pk + (size_t)2 * a.bh * nbp * C::D : nullptr, (const bf16*)a.ht, (bf16*)a.O};
-  hipLaunchKernelGGL((attn_bf16_kernel<C>), dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax,
-                     a.approx, a.order, a.scale, a.nb);
+  const bool fo = a.approx && a.order == kOrderFirst;
+  auto kern = a.lens ? (fo ? attn_bf16_kernel<C, true, true> : attn_bf16_kernel<C, true, false>)
+                     : (fo ? attn_bf16_kernel<C, false, true> : attn_bf16_kernel<C, false, false>);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax, a.approx, a.order,
+                     a.scale, a.nb, a.lens, a.heads);
   return hipGetLastError();
 }
 

@@ -20,7 +20,8 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const int32_t* __restrict__ idx, int kmax, const float* __restrict__ centroid,
     const float* __restrict__ vsum, const float* __restrict__ hbar, const float* __restrict__ H,
-    int approx, int order, float scale, float* __restrict__ O, int nb, int BLK) {
+    int approx, int order, float scale, float* __restrict__ O, int nb, int BLK,
+    const int32_t* __restrict__ lens, int heads) {
   __shared__ float kt[CH][D];
   __shared__ float vt[CH][D];
   __shared__ unsigned bits[kMaxBlocks / 32];
@@ -30,19 +31,24 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
   const float* Kh = K + (size_t)bh * L * D;
   const float* Vh = V + (size_t)bh * L * D;
   const int32_t* row = idx + ((size_t)bh * nb + i) * kmax;
+  // valid tokens: blocks j < nne are non-empty; this block holds ni queries
+  const int Lv = valid_len(lens, bh, heads, (int)L);
+  const int nne = (Lv + BLK - 1) / BLK;
+  const int ni = block_count(Lv, i, BLK);
 
   for (int e = tid; e < (nb + 31) / 32; e += BLK) bits[e] = 0u;
   __syncthreads();
   for (int e = tid; e < kmax; e += BLK) {
     const int j = row[e];
-    if (j >= 0 && j < nb) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    if (j >= 0 && j < nne) atomicOr(&bits[j >> 5], 1u << (j & 31));
   }
 
   float q[D], acc[D];
   const float* qrow = Q + ((size_t)bh * L + (size_t)i * BLK + tid) * D;
+  const bool live = tid < ni;                       // padding queries: a zero row
 #pragma unroll
   for (int c = 0; c < D; ++c) {
-    q[c] = qrow[c];
+    q[c] = live ? qrow[c] : 0.f;
     acc[c] = 0.f;
   }
   const float c2 = scale * kLog2e;
@@ -50,6 +56,9 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
 
   // one chunk of CH keys (or centroids) staged in kt / vt
   auto consume = [&](bool stage2, int jbase, int nvalid) {
+    float cntw[CH];                                 // stage 2: tokens of each centroid's block
+#pragma unroll
+    for (int n = 0; n < CH; ++n) cntw[n] = (float)block_count(Lv, jbase + n, BLK);
     float lg[CH];
     float mx = -INFINITY;
 #pragma unroll
@@ -61,7 +70,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
       if (n >= nvalid) x = -INFINITY;
       if (stage2) {
         const int j = jbase + n;
-        if (j < nb && ((bits[j >> 5] >> (j & 31)) & 1u)) x = -INFINITY;
+        if (j >= nne || ((bits[j >> 5] >> (j & 31)) & 1u)) x = -INFINITY;
       }
       lg[n] = x;
       mx = fmaxf(mx, x);
@@ -69,14 +78,15 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
     const float mnew = fmaxf(m, mx);
     const float corr = exp2f(m - mnew);
     m = mnew;
-    float ps = 0.f;
+    float ps = 0.f, pw = 0.f;
 #pragma unroll
     for (int n = 0; n < CH; ++n) {
       lg[n] = exp2f(lg[n] - mnew);
       ps += lg[n];
+      pw += cntw[n] * lg[n];
     }
     if (stage2) {
-      l = l * corr + (float)BLK * ps;
+      l = l * corr + pw;                            // each block weighs its n_j tokens
       asum = asum * corr + ps;
     } else {
       l = l * corr + ps;
@@ -93,16 +103,18 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
   // stage 1: exact keys of the selected blocks
   for (int e = 0; e < kmax; ++e) {
     const int j = row[e];
-    if (j < 0 || j >= nb) continue;
+    if (j < 0 || j >= nne) continue;
+    const int nj = block_count(Lv, j, BLK);
     for (int n0 = 0; n0 < BLK; n0 += CH) {
+      const int nv = min(max(nj - n0, 0), CH);       // keys of this chunk inside the sequence
       __syncthreads();
       for (int t = tid; t < CH * D; t += BLK) {
         const int n = t / D, c = t % D;
-        kt[n][c] = Kh[((size_t)j * BLK + n0 + n) * D + c];
-        vt[n][c] = Vh[((size_t)j * BLK + n0 + n) * D + c];
+        kt[n][c] = n < nv ? Kh[((size_t)j * BLK + n0 + n) * D + c] : 0.f;
+        vt[n][c] = n < nv ? Vh[((size_t)j * BLK + n0 + n) * D + c] : 0.f;
       }
       __syncthreads();
-      consume(false, 0, CH);
+      consume(false, 0, nv);
     }
   }
 
@@ -144,7 +156,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
     // per-block first order: acc += scale * alpha_j * (q H_j) for every j outside S_i,
     // alpha_j = e^{q kbar_j} against the running max (the same shift as every term)
     const float* cen = centroid + (size_t)bh * nb * D;
-    for (int j = 0; j < nb; ++j) {
+    for (int j = 0; j < nne; ++j) {
       if ((bits[j >> 5] >> (j & 31)) & 1u) continue;
       float s = 0.f;
 #pragma unroll
@@ -156,7 +168,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
   const float inv = l > 0.f ? 1.f / l : 0.f;
   float* orow = O + ((size_t)bh * L + (size_t)i * BLK + tid) * D;
 #pragma unroll
-  for (int c = 0; c < D; ++c) orow[c] = acc[c] * inv;
+  for (int c = 0; c < D; ++c) orow[c] = live ? acc[c] * inv : 0.f;
 }
 
 template <int D>
@@ -164,7 +176,7 @@ hipError_t attn_f32_t(const AttnArgs& a) {
   hipLaunchKernelGGL((attn_f32_kernel<D>), dim3(a.bh * a.nb), dim3(a.BLK), 0, a.stream,
                      (const float*)a.Q, (const float*)a.K, (const float*)a.V, a.idx, a.kmax,
                      a.centroid, a.vsum, a.hbar, a.H, a.approx, a.order, a.scale, (float*)a.O,
-                     a.nb, a.BLK);
+                     a.nb, a.BLK, a.lens, a.heads);
   return hipGetLastError();
 }
 

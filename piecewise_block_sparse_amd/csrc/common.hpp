@@ -67,4 +67,18 @@ __device__ __forceinline__ int xcd_remap(int wg, int grid) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Valid length of the sequence of (batch * heads) row bh: lens[bh / heads]
+// clamped to [0, L], or L when no lengths are given.
+__device__ __forceinline__ int valid_len(const int32_t* lens, int bh, int heads, int L) {
+  if (!lens) return L;
+  const int v = lens[bh / heads];
+  return v < 0 ? 0 : (v > L ? L : v);
+}
+
+// tokens of block j that lie inside a sequence of Lv valid tokens
+__device__ __forceinline__ int block_count(int Lv, int j, int BLK) {
+  const int n = Lv - j * BLK;
+  return n < 0 ? 0 : (n > BLK ? BLK : n);
+}
+
 }  // namespace pisa

@@ -27,6 +27,8 @@ struct AttnArgs {
   int nb;   // blocks per sequence
   int D;
   int BLK;
+  const int32_t* lens;  // nullable device [batch]: valid length of each sequence
+  int heads;
   hipStream_t stream;
 };
 
@@ -46,6 +48,8 @@ struct StatsArgs {
   int nb;
   int D;
   int BLK;
+  const int32_t* lens;
+  int heads;
   hipStream_t stream;
 };
 
@@ -61,6 +65,8 @@ struct RouteArgs {
   int nb;
   int D;
   int BLK;
+  const int32_t* lens;
+  int heads;
   hipStream_t stream;
 };
 

@@ -16,6 +16,10 @@
 // top k with a radix select over order-preserving 64-bit keys (ties at the
 // threshold resolved to the lower block ids).  LDS is sized to the padded
 // block count, so small nb keeps many workgroups resident.
+//
+// With valid lengths, block i pools its n_i valid queries, only the non-empty
+// blocks (a prefix: j < ceil(len / BLK)) are candidates, a row with fewer than
+// k candidates ends in -1, and an empty query block gets an all -1 row.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -71,7 +75,9 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
                                                             const float* __restrict__ centroid,
                                                             const float* __restrict__ M, int nb,
                                                             int nbp, int k, double scale,
-                                                            double lam, int32_t* __restrict__ idx) {
+                                                            double lam, int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ lens,
+                                                            int heads) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   double* s_q = reinterpret_cast<double*>(smem);
   double* s_sc = s_q + kRows * D;
@@ -84,6 +90,9 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
   const int i = (blockIdx.x - bh * nrb) * kRows + w;   // this wave's query block
   const bool active = i < nb;
   const size_t L = (size_t)nb * BLK;
+  const int Lv = valid_len(lens, bh, heads, (int)L);
+  const int nne = (Lv + BLK - 1) / BLK;                // non-empty blocks: j < nne
+  const int ni = block_count(Lv, i, BLK);              // valid queries of block i
 
   // ---- pool: qbar_i = (1/BLK) sum of the block's queries, exact in fp64
   {
@@ -102,16 +111,18 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) v[u] = Chunk8<T>::load(qb + (size_t)(r0 + u) * RPI * D);
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) Chunk8<T>::add(x, v[u]);
+        for (int u = 0; u < BATCH; ++u)
+          if (rs + (r0 + u) * RPI < ni) Chunk8<T>::add(x, v[u]);   // padding rows never enter
       }
     }
 #pragma unroll
     for (int off = CPR; off < 64; off <<= 1)
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] += __shfl_xor(x[e], off);
+    const double inv = (ni == BLK) ? 1.0 / BLK : 1.0 / (double)(ni > 0 ? ni : 1);
     if (rs == 0)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_q[w * D + 8 * c + e] = x[e] * (1.0 / BLK);
+      for (int e = 0; e < 8; ++e) s_q[w * D + 8 * c + e] = x[e] * inv;
   }
 
   // ---- scores against every block centroid: thread t owns centroid j0 + t
@@ -158,8 +169,9 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
   const int nu = nbp / 64;                                // candidates per lane (<= 32)
   unsigned inplay = 0u, chosen = 0u;
   for (int u = 0; u < nu; ++u)
-    if (lane + 64 * u < nb) inplay |= 1u << u;
-  int krem = k;
+    if (lane + 64 * u < nne) inplay |= 1u << u;
+  const int kk = (ni > 0) ? min(k, nne) : 0;            // blocks this row can hold
+  int krem = kk;
   for (int pass = 7; pass >= 0; --pass) {
     const int shift = 8 * pass;
     for (int b = lane; b < 256; b += 64) hist[b] = 0u;
@@ -199,9 +211,14 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
       }
     }
     const unsigned long long who = __ballot(dstar >= 0);
-    const int src = __ffsll(who) - 1;
-    dstar = __shfl(dstar, src);
-    cnt_above = __shfl(cnt_above, src);
+    if (who == 0ull) {                                    // krem == 0: nothing left to pick
+      dstar = 256;
+      cnt_above = 0u;
+    } else {
+      const int src = __ffsll(who) - 1;
+      dstar = __shfl(dstar, src);
+      cnt_above = __shfl(cnt_above, src);
+    }
     krem -= (int)cnt_above;
     for (int u = 0; u < nu; ++u)
       if ((inplay >> u) & 1u) {
@@ -245,6 +262,7 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
     out[pos++] = 32 * lane + b;
     wv &= wv - 1;
   }
+  for (int e = kk + lane; e < k; e += 64) out[e] = -1;   // fewer candidates than k
 }
 
 template <int D, int BLK, typename T>
@@ -260,7 +278,7 @@ hipError_t route_t(const RouteArgs& a) {
   }
   const int nrb = (a.nb + kRows - 1) / kRows;
   hipLaunchKernelGGL(kern, dim3(a.bh * nrb), dim3(64 * kRows), lds, a.stream, (const T*)a.Q,
-                     a.centroid, a.M, a.nb, nbp, a.k, a.scale, a.lam, a.idx);
+                     a.centroid, a.M, a.nb, nbp, a.k, a.scale, a.lam, a.idx, a.lens, a.heads);
   return hipGetLastError();
 }
 

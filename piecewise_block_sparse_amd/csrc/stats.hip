@@ -35,7 +35,8 @@ __global__ __launch_bounds__(256) void stats_bf16_kernel(
     const bf16* __restrict__ K, const bf16* __restrict__ V, int nb, float* __restrict__ centroid,
     float* __restrict__ vsum, float* __restrict__ partial, const float* __restrict__ hbar,
     float* __restrict__ M, float* __restrict__ Hout, bf16* __restrict__ pk_cen,
-    bf16* __restrict__ pk_vsum, bf16* __restrict__ Ht) {
+    bf16* __restrict__ pk_vsum, bf16* __restrict__ Ht, const int32_t* __restrict__ lens,
+    int heads) {
   using C = SCfg<D, BLK>;
   __shared__ __attribute__((aligned(16))) bf16 Kt[D * C::ROW];
   __shared__ __attribute__((aligned(16))) bf16 Vt[D * C::ROW];
@@ -53,6 +54,7 @@ __global__ __launch_bounds__(256) void stats_bf16_kernel(
   const bf16* Kh = K + (size_t)bh * L * D;
   const bf16* Vh = V + (size_t)bh * L * D;
   const int mt0 = (w >> 1) * C::TM, nt0 = (w & 1) * C::TM;
+  const int Lv = valid_len(lens, bh, heads, (int)L);      // tokens past Lv are not counted
 
   f32x16 acc[C::TM][C::TM];
 #pragma unroll
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void stats_bf16_kernel(
       }
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int nj) {
 #pragma unroll
     for (int u = 0; u < C::PER_T; ++u) {
       const int p = tid + u * C::NT;
@@ -94,6 +96,10 @@ __global__ __launch_bounds__(256) void stats_bf16_kernel(
         bf16* Xt = (p < C::SUB) ? Kt : Vt;
         const int q = p % C::SUB;
         const int g = q % (BLK / 8), c = q / (BLK / 8);
+        // tokens 8 g + e at or past the block's valid count are stored as zeros
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (8 * g + e >= nj) regs[u][e] = u32x4{0u, 0u, 0u, 0u};
         u32x4 col[8];
         transpose8x8(regs[u], col);
 #pragma unroll
@@ -104,8 +110,9 @@ __global__ __launch_bounds__(256) void stats_bf16_kernel(
 
   gload(j0);
   for (int j = j0; j < j1; ++j) {
+    const int nj = block_count(Lv, j, BLK);
     __syncthreads();
-    lstore();
+    lstore(nj);
     __syncthreads();
     if (j + 1 < j1) gload(j + 1);
 
@@ -121,10 +128,11 @@ __global__ __launch_bounds__(256) void stats_bf16_kernel(
       }
       const size_t prow = ((size_t)bh * ((nb + BLK - 1) / BLK * BLK) + j) * D;
       if (tid < D) {
-        s_k[tid] = s * (1.f / BLK);
+        const float kbar = (nj == BLK) ? s * (1.f / BLK) : (nj > 0 ? s / (float)nj : 0.f);
+        s_k[tid] = kbar;
         if (!PASS2) {
-          centroid[((size_t)bh * nb + j) * D + tid] = s * (1.f / BLK);
-          if (pk_cen) pk_cen[prow + tid] = (bf16)(s * (1.f / BLK));
+          centroid[((size_t)bh * nb + j) * D + tid] = kbar;
+          if (pk_cen) pk_cen[prow + tid] = (bf16)kbar;
         }
       } else {
         s_v[tid - D] = s;
@@ -202,7 +210,7 @@ __global__ __launch_bounds__(256) void stats_bf16_kernel(
       for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
       if (lane == 0) s_red[w] = sq;
       __syncthreads();
-      if (tid == 0) M[(size_t)bh * nb + j] = sqrtf(s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+      if (tid == 0) M[(size_t)bh * nb + j] = nj > 0 ? sqrtf(s_red[0] + s_red[1] + s_red[2] + s_red[3]) : 0.f;
     }
   }
 
@@ -226,7 +234,9 @@ __global__ __launch_bounds__(256) void hbar_reduce_kernel(const float* __restric
                                                           float* __restrict__ hbar,
                                                           bf16* __restrict__ pk_hbart,
                                                           bf16* __restrict__ pk_cen,
-                                                          bf16* __restrict__ pk_vsum, int nbp) {
+                                                          bf16* __restrict__ pk_vsum, int nbp,
+                                                          const int32_t* __restrict__ lens,
+                                                          int heads, int BLK) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   const int DD = D * D;
   if (t < total) {
@@ -234,7 +244,9 @@ __global__ __launch_bounds__(256) void hbar_reduce_kernel(const float* __restric
     const float* p = parts + (size_t)bh * ngrp * DD + e;
     double s = 0.0;
     for (int g = 0; g < ngrp; ++g) s += (double)p[(size_t)g * DD];
-    const float v = (float)(s / nb);
+    // mean over the non-empty blocks (all nb without lengths)
+    const int nne = (valid_len(lens, bh, heads, nb * BLK) + BLK - 1) / BLK;
+    const float v = nne > 0 ? (float)(s / nne) : 0.f;
     hbar[t] = v;
     if (pk_hbart) {
       const int a = e / D, c = e - a * D;
@@ -259,7 +271,8 @@ __global__ __launch_bounds__(256) void hbar_reduce_kernel(const float* __restric
 template <int D>
 __global__ __launch_bounds__(256) void stats_f32_block_kernel(
     const float* __restrict__ K, const float* __restrict__ V, int nb, int BLK,
-    float* __restrict__ centroid, float* __restrict__ vsum, float* __restrict__ Hbuf) {
+    float* __restrict__ centroid, float* __restrict__ vsum, float* __restrict__ Hbuf,
+    const int32_t* __restrict__ lens, int heads) {
   constexpr int NT = 256, CH = 32, PER = D * D / NT;
   __shared__ float kc[CH][D];
   __shared__ float vc[CH][D];
@@ -268,14 +281,16 @@ __global__ __launch_bounds__(256) void stats_f32_block_kernel(
   const int bh = blockIdx.x / nb, j = blockIdx.x - bh * nb;
   const float* Kb = K + ((size_t)bh * nb + j) * BLK * D;
   const float* Vb = V + ((size_t)bh * nb + j) * BLK * D;
+  const int nj = block_count(valid_len(lens, bh, heads, nb * BLK), j, BLK);   // valid tokens
   if (tid < D) {
     float sk = 0.f, sv = 0.f;
-    for (int n = 0; n < BLK; ++n) {
+    for (int n = 0; n < nj; ++n) {
       sk += Kb[(size_t)n * D + tid];
       sv += Vb[(size_t)n * D + tid];
     }
-    s_k[tid] = sk / BLK;
-    centroid[((size_t)bh * nb + j) * D + tid] = sk / BLK;
+    const float kbar = nj > 0 ? sk / nj : 0.f;
+    s_k[tid] = kbar;
+    centroid[((size_t)bh * nb + j) * D + tid] = kbar;
     vsum[((size_t)bh * nb + j) * D + tid] = sv;
   }
   __syncthreads();
@@ -285,8 +300,9 @@ __global__ __launch_bounds__(256) void stats_f32_block_kernel(
   for (int n0 = 0; n0 < BLK; n0 += CH) {
     for (int q = tid; q < CH * D; q += NT) {
       const int n = q / D, c = q % D;
-      kc[n][c] = Kb[(size_t)(n0 + n) * D + c] - s_k[c];
-      vc[n][c] = Vb[(size_t)(n0 + n) * D + c];
+      const bool ok = n0 + n < nj;
+      kc[n][c] = ok ? Kb[(size_t)(n0 + n) * D + c] - s_k[c] : 0.f;
+      vc[n][c] = ok ? Vb[(size_t)(n0 + n) * D + c] : 0.f;
     }
     __syncthreads();
     for (int n = 0; n < CH; ++n)
@@ -306,7 +322,8 @@ __global__ __launch_bounds__(256) void stats_f32_block_kernel(
 template <int D>
 __global__ __launch_bounds__(256) void frob_kernel(const float* __restrict__ Hbuf,
                                                    const float* __restrict__ hbar, int nb,
-                                                   float* __restrict__ M) {
+                                                   float* __restrict__ M, const int32_t* lens,
+                                                   int heads, int BLK) {
   __shared__ float s_red[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int bh = blockIdx.x / nb;
@@ -320,7 +337,9 @@ __global__ __launch_bounds__(256) void frob_kernel(const float* __restrict__ Hbu
   for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
   if (lane == 0) s_red[w] = sq;
   __syncthreads();
-  if (tid == 0) M[blockIdx.x] = sqrtf(s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+  const int j = blockIdx.x - bh * nb;
+  const bool empty = block_count(valid_len(lens, bh, heads, nb * BLK), j, BLK) == 0;
+  if (tid == 0) M[blockIdx.x] = empty ? 0.f : sqrtf(s_red[0] + s_red[1] + s_red[2] + s_red[3]);
 }
 
 // ---- spectral reading of M_j = ||H_j - Hbar||_2: the largest singular value
@@ -353,7 +372,8 @@ __device__ __forceinline__ float block_sum(float x, float* red) {
 template <int D>
 __global__ __launch_bounds__(256) void spectral_kernel(const float* __restrict__ H,
                                                        const float* __restrict__ hbar, int nb,
-                                                       float* __restrict__ M) {
+                                                       float* __restrict__ M, const int32_t* lens,
+                                                       int heads, int BLK) {
   constexpr int NT = 256, LD = D + 4, NH = NT / D, CW = D / NH;
   __shared__ __attribute__((aligned(16))) float A[D * LD];
   __shared__ __attribute__((aligned(16))) float v[D];
@@ -361,6 +381,10 @@ __global__ __launch_bounds__(256) void spectral_kernel(const float* __restrict__
   __shared__ float s_al[kLanczos], s_be[kLanczos];
   const int tid = threadIdx.x;
   const int blk = blockIdx.x, bh = blk / nb;
+  if (block_count(valid_len(lens, bh, heads, nb * BLK), blk - bh * nb, BLK) == 0) {
+    if (tid == 0) M[blk] = 0.f;                   // empty block: never routed
+    return;
+  }
   const float* Hj = H + (size_t)blk * D * D;
   const float* Hb = hbar + (size_t)bh * D * D;
   for (int e = 4 * tid; e < D * D; e += 4 * NT) {
@@ -474,8 +498,9 @@ __global__ __launch_bounds__(256) void spectral_kernel(const float* __restrict__
 
 template <int D>
 hipError_t launch_spectral(const float* H, const float* hbar, int bh, int nb, float* M,
-                           hipStream_t stream) {
-  hipLaunchKernelGGL((spectral_kernel<D>), dim3(bh * nb), dim3(256), 0, stream, H, hbar, nb, M);
+                           const StatsArgs& a) {
+  hipLaunchKernelGGL((spectral_kernel<D>), dim3(bh * nb), dim3(256), 0, a.stream, H, hbar, nb, M,
+                     a.lens, a.heads, a.BLK);
   return hipGetLastError();
 }
 
@@ -492,22 +517,22 @@ hipError_t stats_bf16_t(const StatsArgs& a) {
   hipLaunchKernelGGL((stats_bf16_kernel<D, BLK, false>), dim3(grid), dim3(256), 0, a.stream,
                      (const bf16*)a.K, (const bf16*)a.V, a.nb, a.centroid, a.vsum, parts,
                      (const float*)nullptr, (float*)nullptr, (float*)nullptr, pk_cen, pk_vsum,
-                     (bf16*)nullptr);
+                     (bf16*)nullptr, a.lens, a.heads);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int total = a.bh * D * D;
   hipLaunchKernelGGL(hbar_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, a.stream,
                      (const float*)parts, ngrp, a.nb, D, total, a.hbar, pk_hbart, pk_cen, pk_vsum,
-                     nbp);
+                     nbp, a.lens, a.heads, BLK);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((stats_bf16_kernel<D, BLK, true>), dim3(grid), dim3(256), 0, a.stream,
                      (const bf16*)a.K, (const bf16*)a.V, a.nb, (float*)nullptr, (float*)nullptr,
                      (float*)nullptr, (const float*)a.hbar, a.M, a.H, (bf16*)nullptr,
-                     (bf16*)nullptr, static_cast<bf16*>(a.ht));
+                     (bf16*)nullptr, static_cast<bf16*>(a.ht), a.lens, a.heads);
   err = hipGetLastError();
   if (err != hipSuccess || !a.spectral) return err;
-  return launch_spectral<D>(a.H, a.hbar, a.bh, a.nb, a.M, a.stream);
+  return launch_spectral<D>(a.H, a.hbar, a.bh, a.nb, a.M, a);
 }
 
 template <int D>
@@ -515,18 +540,19 @@ hipError_t stats_f32_t(const StatsArgs& a) {
   float* Hbuf = a.H ? a.H : static_cast<float*>(a.ws);
   const int grid = a.bh * a.nb;
   hipLaunchKernelGGL((stats_f32_block_kernel<D>), dim3(grid), dim3(256), 0, a.stream,
-                     (const float*)a.K, (const float*)a.V, a.nb, a.BLK, a.centroid, a.vsum, Hbuf);
+                     (const float*)a.K, (const float*)a.V, a.nb, a.BLK, a.centroid, a.vsum, Hbuf,
+                     a.lens, a.heads);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int total = a.bh * D * D;
   hipLaunchKernelGGL(hbar_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, a.stream,
                      (const float*)Hbuf, a.nb, a.nb, D, total, a.hbar, (bf16*)nullptr,
-                     (bf16*)nullptr, (bf16*)nullptr, a.nb);
+                     (bf16*)nullptr, (bf16*)nullptr, a.nb, a.lens, a.heads, a.BLK);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (a.spectral) return launch_spectral<D>(Hbuf, a.hbar, a.bh, a.nb, a.M, a.stream);
+  if (a.spectral) return launch_spectral<D>(Hbuf, a.hbar, a.bh, a.nb, a.M, a);
   hipLaunchKernelGGL((frob_kernel<D>), dim3(grid), dim3(256), 0, a.stream, (const float*)Hbuf,
-                     (const float*)a.hbar, a.nb, a.M);
+                     (const float*)a.hbar, a.nb, a.M, a.lens, a.heads, a.BLK);
   return hipGetLastError();
 }
 

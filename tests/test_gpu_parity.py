@@ -232,6 +232,99 @@ def test_norm_reading_diagnostic(torch):
     assert res[("fro", 0.0)] == res[("spectral", 0.0)]
 
 
+# ---------------------------------------------------------------- variable lengths
+
+VL_MODES = {"approx": oracle.MODE_APPROX, "drop": oracle.MODE_DROP, **ORDER_MODES}
+
+
+@pytest.mark.parametrize("dtype,d,B,L,k,lens", [
+    ("bf16", 128, 64, 1024, 5, [1024, 1000, 321]),      # full, ragged last block, empty blocks
+    ("bf16", 128, 128, 1024, 3, [1024, 700, 130]),
+    ("bf16", 64, 64, 1024, 4, [999, 64, 1]),
+    ("bf16", 64, 128, 1024, 2, [1024, 129, 0]),          # an empty sequence
+    ("fp32", 128, 64, 512, 3, [512, 300, 65]),
+    ("fp32", 64, 128, 512, 2, [257, 128, 5]),
+])
+def test_varlen_pipeline_parity(torch, dtype, d, B, L, k, lens):
+    """Each batch entry is a sequence of its own length inside a padded buffer:
+    statistics, routing and every attention mode against the oracle's
+    count-aware definitions; the padding holds NaN, which must not reach any
+    result, and padding query rows must come out 0."""
+    pisa = pisa_mod()
+    b, h = len(lens), 2
+    Q, K, V = (_rand(torch, (b, h, L, d), dtype, s) for s in (31, 32, 33))
+    K = K + np.repeat(_rand(torch, (b, h, L // B, d), "fp32", 34) * 0.5, B, axis=2)
+    if dtype == "bf16":
+        K = wl.round_bf16(K)
+    Qn, Kn, Vn = Q.copy(), K.copy(), V.copy()
+    for bi, n in enumerate(lens):
+        for X in (Qn, Kn, Vn):
+            X[bi, :, n:] = np.nan
+    Qd, Kd, Vd = (to_dev(x, dtype) for x in (Qn, Kn, Vn))
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    st = pisa.precompute(Kd, Vd, B, store_H=True, store_Ht=dtype == "bf16", seq_lens=sl)
+    idx = pisa.route(Qd, st, k, 0.05, B, seq_lens=sl)
+    outs = {m: pisa.attention(Qd, Kd, Vd, idx, st, B, mode=m, seq_lens=sl) for m in VL_MODES}
+    torch.cuda.synchronize()
+    ref_st = oracle.precompute(K, V, B, seq_lens=lens)
+    check_stats(st, ref_st, name="varlen")
+    scale = 1 / math.sqrt(d)
+    scores = oracle.route_scores(Q, to_np(st["centroid"]), to_np(st["M"]), 0.05, B, scale,
+                                 seq_lens=lens)
+    check_route(idx.cpu().numpy(), scores, k, name="varlen")
+    for m, code in VL_MODES.items():
+        ref = oracle.attention(Q, K, V, idx.cpu().numpy(), ref_st["centroid"], ref_st["vsum"],
+                               ref_st["Hbar"], code, scale, B, H=ref_st["H"], seq_lens=lens)
+        got = to_np(outs[m])
+        check_attention(got, ref, dtype, name=f"varlen/{m}")
+        for bi, n in enumerate(lens):
+            assert np.all(got[bi, :, n:] == 0.0), f"varlen/{m}: padding rows of entry {bi}"
+
+
+def test_varlen_full_lengths_match_the_plain_call(torch):
+    """Lengths equal to the buffer length reproduce the call without lengths."""
+    pisa = pisa_mod()
+    w, Q, K, V, Qd, Kd, Vd = inputs(2)
+    sl = torch.full((w.batch,), w.seq_len, dtype=torch.int32, device="cuda")
+    st0 = pisa.precompute(Kd, Vd, w.block, store_Ht=True)
+    st1 = pisa.precompute(Kd, Vd, w.block, store_Ht=True, seq_lens=sl)
+    idx0 = pisa.route(Qd, st0, w.k, w.lam, w.block)
+    idx1 = pisa.route(Qd, st1, w.k, w.lam, w.block, seq_lens=sl)
+    torch.cuda.synchronize()
+    for key in ("centroid", "vsum", "Hbar", "M", "packed", "Ht"):
+        assert torch.equal(st0[key], st1[key]), key
+    assert torch.equal(idx0, idx1)
+    for m in VL_MODES:
+        a = pisa.attention(Qd, Kd, Vd, idx0, st0, w.block, mode=m)
+        b_ = pisa.attention(Qd, Kd, Vd, idx0, st0, w.block, mode=m, seq_lens=sl)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b_), m
+
+
+def test_varlen_image_workload_sampled(torch):
+    """The image workload as a ragged sequence (4096 - 37 tokens), every mode,
+    on sampled query blocks including the ragged one."""
+    pisa = pisa_mod()
+    w, Q, K, V, Qd, Kd, Vd = inputs(2)
+    n = w.seq_len - 37
+    sl = torch.tensor([n], dtype=torch.int32, device="cuda")
+    st = pisa.precompute(Kd, Vd, w.block, store_Ht=True, seq_lens=sl)
+    idx = pisa.route(Qd, st, w.k, w.lam, w.block, seq_lens=sl)
+    outs = {m: to_np(pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode=m, seq_lens=sl))
+            for m in VL_MODES}
+    torch.cuda.synchronize()
+    heads = [0, 13]
+    Qs, Ks, Vs = Q[:, heads], K[:, heads], V[:, heads]
+    ref_st = oracle.precompute(Ks, Vs, w.block, seq_lens=[n])
+    qb = [(0, hi, i) for hi in range(2) for i in (0, 17, w.nb - 2, w.nb - 1)]
+    for m, code in VL_MODES.items():
+        ref = oracle.attention(Qs, Ks, Vs, idx.cpu().numpy()[:, heads], ref_st["centroid"],
+                               ref_st["vsum"], ref_st["Hbar"], code, w.scale, w.block, qblocks=qb,
+                               H=ref_st["H"], seq_lens=[n])
+        err, mab = check_attention(outs[m][:, heads], ref, w.dtype, name=f"varlen-image/{m}")
+        print(f"varlen image {m}: rel-L2 {err:.3e} max-abs {mab:.3e}")
+
+
 # ---------------------------------------------------------------- edge cases
 
 def _rand(torch, shape, dtype, seed):
