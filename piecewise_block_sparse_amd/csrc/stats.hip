@@ -30,10 +30,12 @@ struct SCfg {
   static_assert(2 * D <= NT, "column sums use one thread per column");
 };
 
-template <int D, int BLK, bool PASS2>
-__global__ __launch_bounds__(256) void stats_bf16_kernel(
+// STORE: pass 2 also writes the optional H_j (fp32) and H_j^T (bf16) outputs;
+// without them pass 2 fits 256 registers and runs two workgroups per CU.
+template <int D, int BLK, bool PASS2, bool STORE>
+__global__ __launch_bounds__(256, (PASS2 && STORE) ? 1 : 2) void stats_bf16_kernel(
     const bf16* __restrict__ K, const bf16* __restrict__ V, int nb, float* __restrict__ centroid,
-    float* __restrict__ vsum, float* __restrict__ partial, const float* __restrict__ hbar,
+    float* __restrict__ vsum, float* __restrict__ partial, const float* __restrict__ hbar_frag,
     float* __restrict__ M, float* __restrict__ Hout, bf16* __restrict__ pk_cen,
     bf16* __restrict__ pk_vsum, bf16* __restrict__ Ht, const int32_t* __restrict__ lens,
     int heads) {
@@ -62,17 +64,11 @@ __global__ __launch_bounds__(256) void stats_bf16_kernel(
 #pragma unroll
     for (int b = 0; b < C::TM; ++b) acc[a][b] = f32x16{};
 
-  float hb[C::TM][C::TM][16];
-  if (PASS2) {
-    const float* hbh = hbar + (size_t)bh * D * D;
-#pragma unroll
-    for (int a = 0; a < C::TM; ++a)
-#pragma unroll
-      for (int b = 0; b < C::TM; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          hb[a][b][r] = hbh[(32 * (mt0 + a) + 8 * (r / 4) + 4 * hh + (r % 4)) * D + 32 * (nt0 + b) + q32];
-  }
+  // pass 2: this lane's Hbar entries, stored by the reduction in fragment order
+  // (4 consecutive floats per (tile, row group)); re-read per block from L2
+  // rather than held in 64 registers for the whole loop
+  const float* hbf = PASS2 ? hbar_frag + (size_t)bh * D * D + (size_t)w * C::TM * C::TM * 1024 + 4 * lane
+                           : nullptr;
 
   u32x4 regs[C::PER_T][8];
   auto gload = [&](int j) {
@@ -180,19 +176,24 @@ __global__ __launch_bounds__(256) void stats_bf16_kernel(
 
     if (PASS2) {
       float sq = 0.f;
-      float* Hj = Hout ? Hout + ((size_t)bh * nb + j) * D * D : nullptr;
+      float* Hj = (STORE && Hout) ? Hout + ((size_t)bh * nb + j) * D * D : nullptr;
 #pragma unroll
       for (int a = 0; a < C::TM; ++a)
 #pragma unroll
         for (int b = 0; b < C::TM; ++b)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float x = acc[a][b][r];
-            const float dlt = x - hb[a][b][r];
-            sq += dlt * dlt;
-            if (Hj) Hj[(32 * (mt0 + a) + 8 * (r / 4) + 4 * hh + (r % 4)) * D + 32 * (nt0 + b) + q32] = x;
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 h4 = *reinterpret_cast<const f32x4*>(hbf + ((a * C::TM + b) * 4 + g) * 256);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int r = 4 * g + rr;
+              const float x = acc[a][b][r];
+              const float dlt = x - h4[rr];
+              sq += dlt * dlt;
+              if (Hj) Hj[(32 * (mt0 + a) + 8 * (r / 4) + 4 * hh + (r % 4)) * D + 32 * (nt0 + b) + q32] = x;
+            }
           }
-      if (Ht) {
+      if (STORE && Ht) {
         // H_j^T in bf16: row = value dim, 4 consecutive key-dim columns per store
         bf16* Hj = Ht + ((size_t)bh * nb + j) * D * D;
 #pragma unroll
@@ -236,7 +237,8 @@ __global__ __launch_bounds__(256) void hbar_reduce_kernel(const float* __restric
                                                           bf16* __restrict__ pk_cen,
                                                           bf16* __restrict__ pk_vsum, int nbp,
                                                           const int32_t* __restrict__ lens,
-                                                          int heads, int BLK) {
+                                                          int heads, int BLK,
+                                                          float* __restrict__ hbar_frag) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   const int DD = D * D;
   if (t < total) {
@@ -248,6 +250,17 @@ __global__ __launch_bounds__(256) void hbar_reduce_kernel(const float* __restric
     const int nne = (valid_len(lens, bh, heads, nb * BLK) + BLK - 1) / BLK;
     const float v = nne > 0 ? (float)(s / nne) : 0.f;
     hbar[t] = v;
+    if (hbar_frag) {
+      // fragment order of the statistics kernel's pass 2: wave w = 2 (row tile / TM) +
+      // (column tile / TM) holds tiles (a, b); lane q32 + 32 hh holds rows
+      // 32 mt + 8 g + 4 hh + rr of column 32 nt + q32; 4 rows rr are contiguous
+      const int TM = (D == 128) ? 2 : 1;
+      const int row = e / D, col = e - (e / D) * D;
+      const int mt = row >> 5, rem = row & 31, nt = col >> 5;
+      const int wv = 2 * (mt / TM) + nt / TM, a = mt % TM, b = nt % TM;
+      const int g = rem >> 3, hh = (rem >> 2) & 1, rr = rem & 3, ln = (col & 31) + 32 * hh;
+      hbar_frag[(size_t)bh * DD + ((((wv * TM + a) * TM + b) * 4 + g) * 64 + ln) * 4 + rr] = v;
+    }
     if (pk_hbart) {
       const int a = e / D, c = e - a * D;
       pk_hbart[(size_t)bh * DD + (size_t)c * D + a] = (bf16)v;
@@ -514,7 +527,8 @@ hipError_t stats_bf16_t(const StatsArgs& a) {
   bf16* pk_vsum = pk ? pk + (size_t)a.bh * nbp * D : nullptr;
   bf16* pk_hbart = pk ? pk + (size_t)2 * a.bh * nbp * D : nullptr;
   const int grid = a.bh * ngrp;
-  hipLaunchKernelGGL((stats_bf16_kernel<D, BLK, false>), dim3(grid), dim3(256), 0, a.stream,
+  float* frag = parts + (size_t)a.bh * ngrp * D * D;     // Hbar in pass 2's fragment order
+  hipLaunchKernelGGL((stats_bf16_kernel<D, BLK, false, false>), dim3(grid), dim3(256), 0, a.stream,
                      (const bf16*)a.K, (const bf16*)a.V, a.nb, a.centroid, a.vsum, parts,
                      (const float*)nullptr, (float*)nullptr, (float*)nullptr, pk_cen, pk_vsum,
                      (bf16*)nullptr, a.lens, a.heads);
@@ -523,12 +537,13 @@ hipError_t stats_bf16_t(const StatsArgs& a) {
   const int total = a.bh * D * D;
   hipLaunchKernelGGL(hbar_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, a.stream,
                      (const float*)parts, ngrp, a.nb, D, total, a.hbar, pk_hbart, pk_cen, pk_vsum,
-                     nbp, a.lens, a.heads, BLK);
+                     nbp, a.lens, a.heads, BLK, frag);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((stats_bf16_kernel<D, BLK, true>), dim3(grid), dim3(256), 0, a.stream,
+  auto pass2 = (a.H || a.ht) ? stats_bf16_kernel<D, BLK, true, true> : stats_bf16_kernel<D, BLK, true, false>;
+  hipLaunchKernelGGL(pass2, dim3(grid), dim3(256), 0, a.stream,
                      (const bf16*)a.K, (const bf16*)a.V, a.nb, (float*)nullptr, (float*)nullptr,
-                     (float*)nullptr, (const float*)a.hbar, a.M, a.H, (bf16*)nullptr,
+                     (float*)nullptr, (const float*)frag, a.M, a.H, (bf16*)nullptr,
                      (bf16*)nullptr, static_cast<bf16*>(a.ht), a.lens, a.heads);
   err = hipGetLastError();
   if (err != hipSuccess || !a.spectral) return err;
@@ -547,7 +562,7 @@ hipError_t stats_f32_t(const StatsArgs& a) {
   const int total = a.bh * D * D;
   hipLaunchKernelGGL(hbar_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, a.stream,
                      (const float*)Hbuf, a.nb, a.nb, D, total, a.hbar, (bf16*)nullptr,
-                     (bf16*)nullptr, (bf16*)nullptr, a.nb, a.lens, a.heads, a.BLK);
+                     (bf16*)nullptr, (bf16*)nullptr, a.nb, a.lens, a.heads, a.BLK, (float*)nullptr);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (a.spectral) return launch_spectral<D>(Hbuf, a.hbar, a.bh, a.nb, a.M, a);
@@ -559,8 +574,9 @@ hipError_t stats_f32_t(const StatsArgs& a) {
 }  // namespace
 
 size_t stats_workspace_bf16(int bh, int nb, int D) {
+  // per-group partial sums of H_j, then Hbar in pass 2's fragment order
   const size_t ngrp = (size_t)(nb + kStatsGroup - 1) / kStatsGroup;
-  return (size_t)bh * ngrp * D * D * sizeof(float);
+  return (size_t)bh * (ngrp + 1) * D * D * sizeof(float);
 }
 
 size_t stats_packed_bytes(int bh, int nb, int D, int BLK) {

@@ -82,7 +82,7 @@ def test_precompute_arguments(lib):
     s = shape()
     assert pre(lib, s, out=stats(full=False)) == 1                 # missing centroid
     need = lib.pisa_workspace_size(ctypes.byref(s))
-    assert need == 2 * (16 // 8) * 128 * 128 * 4                  # one fp32 d x d partial per 8 blocks
+    assert need == 2 * (16 // 8 + 1) * 128 * 128 * 4              # fp32 d x d: a partial per 8 blocks, Hbar
     assert pre(lib, s, ws=None) == 1
     assert pre(lib, s, wsb=need - 1) == 5
     assert b"needs" in lib.pisa_last_error()
