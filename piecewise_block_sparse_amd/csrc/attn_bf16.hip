@@ -55,9 +55,7 @@ struct Cfg {
   static constexpr int DPW = NDMA / NW;          // ... per wave
   static constexpr int RPD = 1024 / RB;          // rows per 1 KB copy
   static_assert(NDMA % NW == 0, "copies split evenly over waves");
-  static constexpr int NPH = ((NW * RPD) % 16 == 0) ? 1 : 16 / (NW * RPD);  // swizzle phases
-  static_assert(DPW % 2 == 0 && (NW * RPD * NPH) % 16 == 0 && (DPW / 2) % NPH == 0,
-                "per-wave copies: half K, half V, whole swizzle periods");
+  static_assert(DPW % 2 == 0, "per-wave copies: half K, half V");
   static_assert(D * RB <= LDSB && (D / 2) * RB <= STB, "Hbar^T (fallback) halves fit the stages");
   static_assert(BLK % CK == 0 && CK % 32 == 0, "chunking");
   // per-block first order: H_j^T (D rows) streams as HP ring chunks of RP rows
@@ -71,54 +69,69 @@ __device__ __forceinline__ int swz(int r) {
   return (D == 128) ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
 }
 
-// One global_load_lds_dwordx4: lane l copies 16 bytes from gbase + voff(l)
-// into LDS at m0 + 16 l (gbase and m0 wave-uniform).  Issued from asm so the
-// compiler does not track the copy: it neither orders later LDS reads of the
-// other ring stage behind it nor waits on it; every use of a stage is preceded
-// by wait_vm0() and a workgroup barrier instead.  The instruction has no
-// register result.
-__device__ __forceinline__ void dma16(const void* gbase, unsigned voff, unsigned m0v) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(m0v), "v"(voff), "s"(gbase)
-               : "memory", "m0");
-}
-
-// Copy one CK-row K chunk and V chunk (row stride D) into a stage.  Copy n
-// (wave w issues n = w, w + NW, ...) fills LDS bytes [1024 n, 1024 n + 1024) of
-// the stage: rows RPD n .. RPD n + RPD - 1 of the K chunk (n < NDMA/2) or of the
-// V chunk, lane l writing slot l % CPR of row RPD n + l / CPR.  The slot holds
-// logical column chunk (l % CPR) ^ swz(row).  swz has period 16 in the row, so a
-// lane's byte offset within a copy takes only NPH values over its copies (kept
-// in registers); copy u adds a wave-uniform constant to the base.
+// Copies global -> LDS with global_load_lds_dwordx4: lane l copies 16 bytes
+// from gbase + voff(l) + imm into LDS at m0 + imm + 16 l (the immediate offset
+// moves both addresses).  Issued from asm so the compiler does not track the
+// copies: it neither orders later LDS reads of the other ring stage behind
+// them nor waits on them; every use of a stage is preceded by wait_vm0() and a
+// workgroup barrier instead.  The instructions have no register result.
+//
+// A stage holds the K chunk (bytes [0, SUBB)) and the V chunk ([SUBB, 2 SUBB));
+// each is NDMA/2 pieces of 1 KB = RPD rows.  Wave w copies pieces
+// w H .. w H + H - 1 of each half (H = DPW / 2), so one scalar base and one M0
+// serve a half and the pieces follow as immediates 0, 1024, ...  Lane l writes
+// slot l % CPR of row RPD n + l / CPR of piece n; that slot holds logical
+// column chunk (l % CPR) ^ swz(row).  swz has period 16 rows and H RPD = 16, so
+// the lane's global offset within piece u depends on u only (H registers).
 template <class C>
 struct DmaOff {
-  unsigned v[C::NPH];
+  unsigned v[C::DPW / 2];
 };
 
 template <class C>
-__device__ __forceinline__ DmaOff<C> dma_lane_offsets(int w, int lane) {
+__device__ __forceinline__ DmaOff<C> dma_lane_offsets(int lane) {
+  static_assert((C::DPW / 2) * C::RPD == 16, "one swizzle period per wave's pieces");
   DmaOff<C> o;
 #pragma unroll
-  for (int ph = 0; ph < C::NPH; ++ph) {
-    const int r = (w + C::NW * ph) * C::RPD + lane / C::CPR;
-    o.v[ph] = 2u * ((lane / C::CPR) * C::D + 8 * ((lane % C::CPR) ^ swz<C::D>(r)));
+  for (int u = 0; u < C::DPW / 2; ++u) {
+    const int r = u * C::RPD + lane / C::CPR;
+    o.v[u] = 2u * ((lane / C::CPR) * C::D + 8 * ((lane % C::CPR) ^ swz<C::D>(r)));
   }
   return o;
+}
+
+// H consecutive 1 KB pieces: global gbase + 1024 u, LDS m0v + 1024 u
+template <class C>
+__device__ __forceinline__ void dma_half(const void* gbase, unsigned m0v, const DmaOff<C>& o) {
+  if constexpr (C::DPW / 2 == 4) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, %5\n\t"
+        "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
+        "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
+        "global_load_lds_dwordx4 %4, %5 offset:3072"
+        :
+        : "s"(m0v), "v"(o.v[0]), "v"(o.v[1]), "v"(o.v[2]), "v"(o.v[3]), "s"(gbase)
+        : "memory", "m0");
+  } else {
+    static_assert(C::DPW / 2 == 2, "2 or 4 pieces per wave and half");
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, %3\n\t"
+        "global_load_lds_dwordx4 %2, %3 offset:1024"
+        :
+        : "s"(m0v), "v"(o.v[0]), "v"(o.v[1]), "s"(gbase)
+        : "memory", "m0");
+  }
 }
 
 // gK, gV: first byte of the K and V chunk; stage_m0: LDS address of the stage
 template <class C>
 __device__ __forceinline__ void dma_stage(const char* gK, const char* gV, unsigned stage_m0,
                                           int w, const DmaOff<C>& loff) {
-  constexpr int half = C::DPW / 2;                       // copies of the K chunk per wave
-#pragma unroll
-  for (int u = 0; u < C::DPW; ++u) {
-    const bool isv = u >= half;
-    const int uu = isv ? u - half : u;
-    const char* base = (isv ? gV : gK) + (w + C::NW * uu) * C::RPD * C::RB;
-    dma16(base, loff.v[uu % C::NPH], stage_m0 + (w + C::NW * u) * 1024);
-  }
+  const unsigned wo = (unsigned)w * (C::DPW / 2) * 1024u;
+  dma_half<C>(gK + wo, stage_m0 + wo, loff);
+  dma_half<C>(gV + wo, stage_m0 + C::SUBB + wo, loff);
 }
 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -452,7 +465,7 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
       for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
   const Offsets<C> off = make_offsets<C>(lane);
-  const DmaOff<C> loff = dma_lane_offsets<C>(w, lane);
+  const DmaOff<C> loff = dma_lane_offsets<C>(lane);
   RowState<D> st;
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) st.acc[mt] = f32x16{};
