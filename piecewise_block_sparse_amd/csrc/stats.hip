@@ -244,8 +244,17 @@ __global__ __launch_bounds__(256) void hbar_reduce_kernel(const float* __restric
   if (t < total) {
     const int bh = t / DD, e = t - bh * DD;
     const float* p = parts + (size_t)bh * ngrp * DD + e;
+    // loads of 8 groups in flight, summed in group order (fixed, reproducible)
     double s = 0.0;
-    for (int g = 0; g < ngrp; ++g) s += (double)p[(size_t)g * DD];
+    int g = 0;
+    for (; g + 8 <= ngrp; g += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = p[(size_t)(g + u) * DD];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += (double)x[u];
+    }
+    for (; g < ngrp; ++g) s += (double)p[(size_t)g * DD];
     // mean over the non-empty blocks (all nb without lengths)
     const int nne = (valid_len(lens, bh, heads, nb * BLK) + BLK - 1) / BLK;
     const float v = nne > 0 ? (float)(s / nne) : 0.f;
