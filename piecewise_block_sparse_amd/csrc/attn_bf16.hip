@@ -54,6 +54,10 @@ struct Cfg {
   static constexpr int NDMA = STB / 1024;        // 1 KB wave copies per stage
   static constexpr int DPW = NDMA / NW;          // ... per wave
   static constexpr int RPD = 1024 / RB;          // rows per 1 KB copy
+  // workgroups per CU the register budget is sized for: three 4-wave groups
+  // (3 waves per SIMD, <= 168 VGPRs) for d = 128, block 128 with 32-key chunks
+  // (37 KB of LDS, so three fit); two otherwise
+  static constexpr int MINB = (D == 128 && BLK == 128 && CK == 32) ? 3 : 2;
   static_assert(NDMA % NW == 0, "copies split evenly over waves");
   static_assert(DPW % 2 == 0, "per-wave copies: half K, half V");
   static_assert(D * RB <= LDSB && (D / 2) * RB <= STB, "Hbar^T (fallback) halves fit the stages");
@@ -81,20 +85,19 @@ __device__ __forceinline__ int swz(int r) {
 // w H .. w H + H - 1 of each half (H = DPW / 2), so one scalar base and one M0
 // serve a half and the pieces follow as immediates 0, 1024, ...  Lane l writes
 // slot l % CPR of row RPD n + l / CPR of piece n; that slot holds logical
-// column chunk (l % CPR) ^ swz(row).  swz has period 16 rows and H RPD = 16, so
-// the lane's global offset within piece u depends on u only (H registers).
+// column chunk (l % CPR) ^ swz(row), so the lane's global offset within the
+// wave's piece u is fixed for the whole kernel (H registers per lane).
 template <class C>
 struct DmaOff {
   unsigned v[C::DPW / 2];
 };
 
 template <class C>
-__device__ __forceinline__ DmaOff<C> dma_lane_offsets(int lane) {
-  static_assert((C::DPW / 2) * C::RPD == 16, "one swizzle period per wave's pieces");
+__device__ __forceinline__ DmaOff<C> dma_lane_offsets(int w, int lane) {
   DmaOff<C> o;
 #pragma unroll
   for (int u = 0; u < C::DPW / 2; ++u) {
-    const int r = u * C::RPD + lane / C::CPR;
+    const int r = (w * (C::DPW / 2) + u) * C::RPD + lane / C::CPR;
     o.v[u] = 2u * ((lane / C::CPR) * C::D + 8 * ((lane % C::CPR) ^ swz<C::D>(r)));
   }
   return o;
@@ -405,7 +408,7 @@ constexpr int kBitWords = (kMaxBlocks + 128) / 32;
 // FO: the per-block first order (its stage lives only in these instantiations,
 // so the other modes keep their register budget).
 template <class C, bool VL, bool FO>
-__global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kmax, int approx,
+__global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, int kmax, int approx,
                                                              int order, float scale, int nb,
                                                              const int32_t* lens, int heads) {
   constexpr int D = C::D, BLK = C::BLK, CK = C::CK;
@@ -465,7 +468,7 @@ __global__ __launch_bounds__(C::NT, 2) void attn_bf16_kernel(AttnPtrs p, int kma
       for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
   const Offsets<C> off = make_offsets<C>(lane);
-  const DmaOff<C> loff = dma_lane_offsets<C>(lane);
+  const DmaOff<C> loff = dma_lane_offsets<C>(w, lane);
   RowState<D> st;
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt) st.acc[mt] = f32x16{};
@@ -673,7 +676,11 @@ hipError_t launch_t(const AttnArgs& a) {
 
 hipError_t launch_attn_bf16(const AttnArgs& a) {
   if (a.D == 128 && a.BLK == 64) return launch_t<Cfg<128, 64, 32>>(a);
-  if (a.D == 128 && a.BLK == 128) return launch_t<Cfg<128, 128, 64>>(a);
+  if (a.D == 128 && a.BLK == 128) {
+    // the per-block first order streams whole 128-row H_j^T matrices: 64-key chunks
+    if (a.approx && a.order == kOrderFirst) return launch_t<Cfg<128, 128, 64>>(a);
+    return launch_t<Cfg<128, 128, 32>>(a);
+  }
   if (a.D == 64 && a.BLK == 64) return launch_t<Cfg<64, 64, 32>>(a);
   if (a.D == 64 && a.BLK == 128) return launch_t<Cfg<64, 128, 64>>(a);
   return hipErrorInvalidValue;
