@@ -9,7 +9,9 @@
 // dot products are float64 FMAs.  S_i = the k highest scores, ties to the lower
 // j, written in ascending order.
 //
-// One workgroup = 4 waves = 4 query blocks of one head.  Each wave pools its
+// One workgroup = R waves = R query blocks of one head (R = 8 when there are at
+// least 512 blocks to score, so every thread owns a centroid, else 4; more rows
+// per workgroup means fewer re-reads of the head's centroids).  Each wave pools its
 // block's queries with fully unrolled 16-byte loads (the HBM-bound part); for
 // the scores each thread owns one centroid and forms its dot products with all
 // four pooled queries (broadcast LDS reads); each wave then selects its row's
@@ -26,7 +28,6 @@
 namespace pisa {
 namespace {
 
-constexpr int kRows = 4;       // query blocks per workgroup (one wave each)
 
 template <typename T>
 struct Chunk8;
@@ -55,12 +56,20 @@ struct Chunk8<float> {
   }
 };
 
-// dynamic LDS layout (bytes): q[kRows][D] f64 | sc[kRows][nbp] f64 |
-// hist[kRows][256] u32 | sel[kRows][nbp/32] u32
-template <int D>
+// dynamic LDS layout (bytes): q[R][D] f64 | sc[R][nbp] f64 |
+// hist[R][256] u32 | sel[R][nbp/32] u32
+template <int D, int R>
 __host__ __device__ constexpr size_t route_lds_bytes(int nbp) {
-  return (size_t)kRows * D * 8 + (size_t)kRows * nbp * 8 + (size_t)kRows * 256 * 4 +
-         (size_t)kRows * (nbp / 32) * 4;
+  return (size_t)R * D * 8 + (size_t)R * nbp * 8 + (size_t)R * 256 * 4 +
+         (size_t)R * (nbp / 32) * 4;
+}
+
+// Ordering of one wave's LDS accesses among its own lanes (each row's histogram
+// and selection bitmap belong to one wave, so no workgroup barrier is needed).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // fp64 score -> unsigned key with the same order (larger score, larger key);
@@ -70,7 +79,7 @@ __device__ __forceinline__ unsigned long long order_key(double x) {
   return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-template <int D, int BLK, typename T>
+template <int D, int BLK, typename T, int kRows>
 __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__ Q,
                                                             const float* __restrict__ centroid,
                                                             const float* __restrict__ M, int nb,
@@ -173,12 +182,22 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
   const int kk = (ni > 0) ? min(k, nne) : 0;            // blocks this row can hold
   int krem = kk;
   for (int pass = 7; pass >= 0; --pass) {
+    // every candidate still in play is needed: take them all and stop early
+    int ip = __popc(inplay);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ip += __shfl_xor(ip, off);
+    if (ip == krem) {
+      chosen |= inplay;
+      inplay = 0u;
+      krem = 0;
+      break;
+    }
     const int shift = 8 * pass;
     for (int b = lane; b < 256; b += 64) hist[b] = 0u;
-    __syncthreads();
+    wave_sync();
     for (int u = 0; u < nu; ++u)
       if ((inplay >> u) & 1u) atomicAdd(&hist[(order_key(sc[lane + 64 * u]) >> shift) & 255u], 1u);
-    __syncthreads();
+    wave_sync();
     // this lane holds histogram bins 4l .. 4l + 3
     unsigned h[4], own = 0u;
 #pragma unroll
@@ -230,7 +249,7 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
           inplay &= ~(1u << u);
         }
       }
-    __syncthreads();
+    wave_sync();
   }
   // exact ties with the k-th largest: lowest block ids first
   for (int u = 0; u < nu && krem > 0; ++u) {
@@ -242,7 +261,7 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
   }
   for (int u = 0; u < nu; ++u)
     if ((chosen >> u) & 1u) atomicOr(&sel[(lane + 64 * u) >> 5], 1u << ((lane + 64 * u) & 31));
-  __syncthreads();
+  wave_sync();
 
   // ---- the selected ids, written in ascending order
   if (!active) return;
@@ -265,21 +284,26 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
   for (int e = kk + lane; e < k; e += 64) out[e] = -1;   // fewer candidates than k
 }
 
-template <int D, int BLK, typename T>
-hipError_t route_t(const RouteArgs& a) {
-  int nbp = 64;
-  while (nbp < a.nb) nbp <<= 1;
-  const size_t lds = route_lds_bytes<D>(nbp);
-  auto kern = route_kernel<D, BLK, T>;
+template <int D, int BLK, typename T, int R>
+hipError_t route_launch(const RouteArgs& a, int nbp) {
+  const size_t lds = route_lds_bytes<D, R>(nbp);
+  auto kern = route_kernel<D, BLK, T, R>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const int nrb = (a.nb + kRows - 1) / kRows;
-  hipLaunchKernelGGL(kern, dim3(a.bh * nrb), dim3(64 * kRows), lds, a.stream, (const T*)a.Q,
+  const int nrb = (a.nb + R - 1) / R;
+  hipLaunchKernelGGL(kern, dim3(a.bh * nrb), dim3(64 * R), lds, a.stream, (const T*)a.Q,
                      a.centroid, a.M, a.nb, nbp, a.k, a.scale, a.lam, a.idx, a.lens, a.heads);
   return hipGetLastError();
+}
+
+template <int D, int BLK, typename T>
+hipError_t route_t(const RouteArgs& a) {
+  int nbp = 64;
+  while (nbp < a.nb) nbp <<= 1;
+  return a.nb >= 512 ? route_launch<D, BLK, T, 8>(a, nbp) : route_launch<D, BLK, T, 4>(a, nbp);
 }
 
 template <typename T>
