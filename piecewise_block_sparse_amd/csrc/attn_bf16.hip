@@ -507,10 +507,13 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       // unselected blocks (bit clear), ascending, after the exact ids
       for (int c0 = 0; c0 < nb; c0 += 64) {
         const int j = c0 + lane;
-        const bool u = j < nb && !((bits[j >> 5] >> (j & 31)) & 1u) && cnt + ucnt + lane < kMaxBlocks;
+        const bool u = j < nb && !((bits[j >> 5] >> (j & 31)) & 1u);
         const unsigned long long m = __ballot(u);
-        if (u) s_list[cnt + ucnt + __popcll(m & ((1ull << lane) - 1))] = (short)j;
-        ucnt += __popcll(m);
+        // exact ids plus U_i fill at most nb <= kMaxBlocks slots (more only for
+        // an idx row with duplicate ids, whose excess is dropped)
+        const int slot = cnt + ucnt + __popcll(m & ((1ull << lane) - 1));
+        if (u && slot < kMaxBlocks) s_list[slot] = (short)j;
+        ucnt = min(ucnt + __popcll(m), kMaxBlocks - cnt);
       }
     }
     if (lane == 0) {

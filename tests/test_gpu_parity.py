@@ -456,6 +456,27 @@ def test_route_max_blocks(torch):
     check_route(idx.cpu().numpy(), scores, k, name="nb2048")
 
 
+def test_attention_max_blocks_all_modes(torch):
+    """nb = 2048 (the largest supported block count) with a large k: every mode
+    against the oracle on sampled query blocks (first, middle, last)."""
+    pisa = pisa_mod()
+    B, L, d, k = 64, 2048 * 64, 128, 300
+    Q, K, V = (_rand(torch, (1, 1, L, d), "bf16", s) for s in (14, 15, 16))
+    K = wl.round_bf16(K + np.repeat(_rand(torch, (1, 1, L // B, d), "fp32", 17) * 0.5, B, axis=2))
+    Qd, Kd, Vd = (to_dev(x, "bf16") for x in (Q, K, V))
+    st = pisa.precompute(Kd, Vd, B, store_Ht=True)
+    idx = pisa.route(Qd, st, k, 0.02, B)
+    outs = {m: to_np(pisa.attention(Qd, Kd, Vd, idx, st, B, mode=m)) for m in VL_MODES}
+    torch.cuda.synchronize()
+    ref_st = oracle.precompute(K, V, B)
+    qb = [(0, 0, i) for i in (0, 1024, 2047)]
+    for m, code in VL_MODES.items():
+        ref = oracle.attention(Q, K, V, idx.cpu().numpy(), ref_st["centroid"], ref_st["vsum"],
+                               ref_st["Hbar"], code, 1 / math.sqrt(d), B, qblocks=qb, H=ref_st["H"])
+        err, mab = check_attention(outs[m], ref, "bf16", name=f"nb2048/{m}")
+        print(f"nb2048 {m}: rel-L2 {err:.3e} max-abs {mab:.3e}")
+
+
 @pytest.mark.parametrize("wid", [2, 5])
 def test_packed_and_fp32_statistics_paths_agree(torch, wid):
     """PISA mode reads the bf16 statistics pack when present and converts the
