@@ -137,7 +137,10 @@ const char* pisa_status_string(int32_t status);
 const char* pisa_last_error(void);
 
 /* Bytes of device workspace pisa_precompute needs for this shape (0 if the
- * shape is invalid).  The workspace holds deterministic partial sums of H_j. */
+ * shape is invalid).  The workspace holds deterministic partial sums of H_j:
+ * for bf16 inputs one d x d fp32 sum per group of eight blocks plus a copy of
+ * Hbar per head in the MFMA fragment order, for fp32 inputs one d x d fp32
+ * matrix per block. */
 size_t pisa_workspace_size(const pisa_shape* shape);
 
 /* Bytes of the optional bf16 statistics pack (pisa_stats.packed) for this

@@ -14,9 +14,10 @@
 // per workgroup means fewer re-reads of the head's centroids).  Each wave pools its
 // block's queries with fully unrolled 16-byte loads (the HBM-bound part); for
 // the scores each thread owns one centroid and forms its dot products with all
-// four pooled queries (broadcast LDS reads); each wave then selects its row's
+// R pooled queries (broadcast LDS reads); each wave then selects its row's
 // top k with a radix select over order-preserving 64-bit keys (ties at the
-// threshold resolved to the lower block ids).  LDS is sized to the padded
+// threshold resolved to the lower block ids), stopping as soon as the keys
+// still in play are exactly the ones it has left to take.  LDS is sized to the padded
 // block count, so small nb keeps many workgroups resident.
 //
 // With valid lengths, block i pools its n_i valid queries, only the non-empty
