@@ -54,9 +54,9 @@ struct Cfg {
   static constexpr int NDMA = STB / 1024;        // 1 KB wave copies per stage
   static constexpr int DPW = NDMA / NW;          // ... per wave
   static constexpr int RPD = 1024 / RB;          // rows per 1 KB copy
-  // workgroups per CU the register budget is sized for: three 4-wave groups
-  // (3 waves per SIMD, <= 168 VGPRs) for d = 128, block 128 with 32-key chunks
-  // (37 KB of LDS, so three fit); two otherwise
+  // waves per SIMD the register budget is sized for: three (<= 168 VGPRs)
+  // for d = 128, block 128 with 32-key chunks (three 4-wave groups per CU,
+  // 37 KB of LDS each); two otherwise
   static constexpr int MINB = (D == 128 && BLK == 128 && CK == 32) ? 3 : 2;
   static_assert(NDMA % NW == 0, "copies split evenly over waves");
   static_assert(DPW % 2 == 0, "per-wave copies: half K, half V");
@@ -198,6 +198,18 @@ __device__ __forceinline__ Offsets<C> make_offsets(int lane) {
   return o;
 }
 
+// A operand of O^T += V^T P^T for 16-key slab sl and d-tile mt: two
+// transposing reads of 4 keys each.
+template <class C>
+__device__ __forceinline__ u32x4 v_frag(const char* vst, int sl, int mt, const Offsets<C>& off) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (ls16x4*)(vst + sl * 16 * C::RB + off.voff[mt][0]));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (ls16x4*)(vst + sl * 16 * C::RB + off.voff[mt][1]));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
 // exp2 weights -> bf16 MFMA B operands, and the sum of the same bf16 weights.
 // Each pair is packed into its own 32-bit value and summed from that value
 // with v_dot2 against (1, 1).
@@ -219,26 +231,35 @@ __device__ __forceinline__ float weights_bf16(const f32x16 (&s)[NKT], float c2, 
   return sum;
 }
 
-// One CK-key chunk from a stage: S^T, softmax update, O^T += V^T P^T.
-// STAGE2: the keys are block centroids (values = block value sums); entries
-// whose block is in S_i or is padding (bit set in `bits`) are masked, and each
-// weight counts BLK times in the denominator.
-// Variable lengths: in stage 1 only the first kvalid keys of the chunk exist
-// (the rest get logit -inf); in stage 2 the block at chunk position jpart (if
-// >= 0) holds BLK - wmiss tokens, so its weight counts that many times.
-template <class C, bool STAGE2>
-__device__ __forceinline__ void chunk(RowState<C::D>& st, const bf16x8 (&qf)[C::KS],
-                                      const char* stage, const Offsets<C>& off, float c2, int hh,
-                                      const unsigned* bits, int jbase, int kvalid = C::CK,
-                                      int jpart = -1, float wmiss = 0.f) {
-  f32x16 s[C::NKT];
+// S^T of the chunk in `stage` (K rows) against this wave's queries.  PRE:
+// all K fragments of a tile are read before its MFMA chain (two-wave register
+// budget); otherwise each fragment is read next to its MFMA.
+template <class C, bool PRE>
+__device__ __forceinline__ void s_tiles(f32x16 (&s)[C::NKT], const bf16x8 (&qf)[C::KS],
+                                        const char* stage, const Offsets<C>& off) {
 #pragma unroll
   for (int kt = 0; kt < C::NKT; ++kt) {
     s[kt] = f32x16{};
+    if constexpr (PRE) {
+      u32x4 kf[C::KS];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      s[kt] = mfma32(as_bf16x8(ld16(stage + kt * 32 * C::RB + off.koff[ks])), qf[ks], s[kt]);
+      for (int ks = 0; ks < C::KS; ++ks) kf[ks] = ld16(stage + kt * 32 * C::RB + off.koff[ks]);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) s[kt] = mfma32(as_bf16x8(kf[ks]), qf[ks], s[kt]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        s[kt] = mfma32(as_bf16x8(ld16(stage + kt * 32 * C::RB + off.koff[ks])), qf[ks], s[kt]);
+    }
   }
+}
+
+// Logits of keys that do not take part -> -inf.  STAGE2: centroid entries
+// whose block is in S_i or is padding (bit set in `bits`); stage 1: keys past
+// the sequence's end (key of register r: 32 kt + 8 (r / 4) + 4 hh + r % 4).
+template <class C, bool STAGE2>
+__device__ __forceinline__ void mask_keys(f32x16 (&s)[C::NKT], int hh, const unsigned* bits,
+                                          int jbase, int kvalid) {
   if (STAGE2) {
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt) {
@@ -248,14 +269,23 @@ __device__ __forceinline__ void chunk(RowState<C::D>& st, const bf16x8 (&qf)[C::
         if ((wbits >> (8 * (r / 4) + (r % 4))) & 1u) s[kt][r] = -INFINITY;
     }
   } else if (kvalid < C::CK) {
-    // keys past the sequence's end (key of register r: 32 kt + 8 (r / 4) + 4 hh + r % 4)
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (32 * kt + 8 * (r / 4) + 4 * hh + (r % 4) >= kvalid) s[kt][r] = -INFINITY;
   }
-  u32x4 pf[C::NSL];
+}
+
+// Weights of one chunk's logits into the online softmax: bf16 B operands in
+// pf, the running max raised (and acc, l, a rescaled) only when needed, and
+// the chunk's share added to l (and, STAGE2, to a).  In stage 2 each weight
+// counts BLK times in the denominator; the block at chunk position jpart (if
+// >= 0) holds BLK - wmiss tokens, so its weight counts that many times.
+template <class C, bool STAGE2>
+__device__ __forceinline__ void softmax_update(RowState<C::D>& st, const f32x16 (&s)[C::NKT],
+                                               float c2, int hh, u32x4 (&pf)[C::NSL],
+                                               int jpart = -1, float wmiss = 0.f) {
   float ps = weights_bf16<C::NKT>(s, c2, -st.m, pf);
   if (__any(!(ps < kSumCap))) {
     float mx = -INFINITY;
@@ -292,19 +322,55 @@ __device__ __forceinline__ void chunk(RowState<C::D>& st, const bf16x8 (&qf)[C::
   } else {
     st.l += ps;
   }
-  const char* vst = stage + C::SUBB;
+}
+
+// All V fragments of a chunk (A operands of O^T += V^T P^T)
+template <class C>
+__device__ __forceinline__ void v_frags(u32x4 (&vf)[C::NSL][C::MT], const char* vst,
+                                        const Offsets<C>& off) {
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-    for (int sl = 0; sl < C::NSL; ++sl) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (ls16x4*)(vst + sl * 16 * C::RB + off.voff[mt][0]));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (ls16x4*)(vst + sl * 16 * C::RB + off.voff[mt][1]));
-      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-      const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
-      st.acc[mt] = mfma32(as_bf16x8(a), as_bf16x8(pf[sl]), st.acc[mt]);
-    }
+    for (int sl = 0; sl < C::NSL; ++sl) vf[sl][mt] = v_frag<C>(vst, sl, mt, off);
+}
+
+template <class C>
+__device__ __forceinline__ void pv_frags(RowState<C::D>& st, const u32x4 (&vf)[C::NSL][C::MT],
+                                         const u32x4 (&pf)[C::NSL]) {
+#pragma unroll
+  for (int sl = 0; sl < C::NSL; ++sl)
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+      st.acc[mt] = mfma32(as_bf16x8(vf[sl][mt]), as_bf16x8(pf[sl]), st.acc[mt]);
+}
+
+// One CK-key chunk from a stage: S^T, softmax update, O^T += V^T P^T.
+// With the two-wave register budget and 32-key chunks (PRE) every LDS
+// fragment is read well before its MFMA; the three-wave budget (and 64-key
+// chunks) leave no room for that, and each fragment is read next to its MFMA.
+template <class C, bool STAGE2>
+__device__ __forceinline__ void chunk(RowState<C::D>& st, const bf16x8 (&qf)[C::KS],
+                                      const char* stage, const Offsets<C>& off, float c2, int hh,
+                                      const unsigned* bits, int jbase, int kvalid = C::CK,
+                                      int jpart = -1, float wmiss = 0.f) {
+  constexpr bool PRE = C::MINB == 2 && C::CK == 32;
+  const char* vst = stage + C::SUBB;
+  f32x16 s[C::NKT];
+  s_tiles<C, PRE>(s, qf, stage, off);
+  u32x4 vf[C::NSL][C::MT];
+  if constexpr (PRE) v_frags<C>(vf, vst, off);
+  mask_keys<C, STAGE2>(s, hh, bits, jbase, kvalid);
+  u32x4 pf[C::NSL];
+  softmax_update<C, STAGE2>(st, s, c2, hh, pf, jpart, wmiss);
+  if constexpr (PRE) {
+    pv_frags<C>(st, vf, pf);
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int sl = 0; sl < C::NSL; ++sl)
+        st.acc[mt] = mfma32(as_bf16x8(v_frag<C>(vst, sl, mt, off)), as_bf16x8(pf[sl]), st.acc[mt]);
+  }
 }
 
 // First-order term of one unselected block j (per-block order): the stage
@@ -552,14 +618,16 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
     }
   };
   if (ntot > 0) issue(0);
+  // keys of exact chunk u inside the sequence (fewer only in a ragged last block)
+  auto keys_of = [&](int u) {
+    return VL ? min(max(block_count(Lv, (int)s_list[u / SPB], BLK) - (u % SPB) * CK, 0), CK) : CK;
+  };
   int t = 0;
   for (; t < nex; ++t) {                    // stage 1: exact blocks
     wait_vm0();
     __syncthreads();
     if (t + 1 < ntot) issue(t + 1);
-    // keys of this chunk inside the sequence (fewer only in a ragged last block)
-    const int kv = VL ? min(max(block_count(Lv, (int)s_list[t / SPB], BLK) - (t % SPB) * CK, 0), CK)
-                      : CK;
+    const int kv = keys_of(t);
     if (VL && kv < CK) {
       // padding values must not reach the MFMA (0 * NaN): zero those V rows
       char* vz = lds + (t & 1) * C::STB + C::SUBB;
