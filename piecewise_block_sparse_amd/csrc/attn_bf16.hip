@@ -623,20 +623,28 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
     return VL ? min(max(block_count(Lv, (int)s_list[u / SPB], BLK) - (u % SPB) * CK, 0), CK) : CK;
   };
   int t = 0;
-  for (; t < nex; ++t) {                    // stage 1: exact blocks
+  // chunk u sits in stage u & 1, passed as `stage`
+  auto exact_step = [&](int u, char* stage) {
     wait_vm0();
     __syncthreads();
-    if (t + 1 < ntot) issue(t + 1);
-    const int kv = keys_of(t);
+    if (u + 1 < ntot) issue(u + 1);
+    const int kv = keys_of(u);
     if (VL && kv < CK) {
       // padding values must not reach the MFMA (0 * NaN): zero those V rows
-      char* vz = lds + (t & 1) * C::STB + C::SUBB;
+      char* vz = stage + C::SUBB;
       for (int e = tid; e < (CK - kv) * C::CPR; e += C::NT)
         st16(vz + (kv + e / C::CPR) * C::RB + 16 * (e % C::CPR), u32x4{0u, 0u, 0u, 0u});
       __syncthreads();
     }
-    chunk<C, false>(st, qf, lds + (t & 1) * C::STB, off, c2, hh, bits, 0, kv);
+    chunk<C, false>(st, qf, stage, off, c2, hh, bits, 0, kv);
+  };
+  // stage 1, two exact chunks per trip (t even), so each stage's offset is a
+  // constant that folds into the LDS reads' immediate offsets
+  for (; t + 1 < nex; t += 2) {
+    exact_step(t, lds);
+    exact_step(t + 1, lds + C::STB);
   }
+  if (t < nex) exact_step(t++, lds);
   // stage 2: the ragged last block (if any) weighs its n_j tokens
   const int jrag = (VL && Lv % BLK != 0) ? nne - 1 : -1;
   const float wmiss = (float)(BLK - (Lv - jrag * BLK));
