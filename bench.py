@@ -10,12 +10,16 @@ Prints ONE JSON line.  `value` is the algorithmic TFLOP/s of the whole step;
 `ms_per_step` its latency; `roofline` describes the fused attention kernel
 (the dominant one) against the bf16 MFMA peak; `phases` splits the step by
 kernel (HIP events on the launch stream); `dense` is the same kernel run with
-every block exact; `orders` times the zeroth-order and the per-block
-first-order treatments of the unselected blocks on the same inputs;
-`cpu_baseline` is the fp64 oracle on a bounded sample.
+every block exact, `sdpa` torch's fused dense attention on the same tensors
+(context only, never part of the library); `density_sweep` re-routes the same
+inputs at top-k 128 / 64 / 32 / 16 of 256 blocks and times both modes; `orders`
+times the zeroth-order and the per-block first-order treatments of the
+unselected blocks on the same inputs; `cpu_baseline` is the fp64 oracle on a
+bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4|3]
-                    [--no-cpu-baseline] [--no-dense] [--no-orders] [--copy-calibration]
+                    [--no-cpu-baseline] [--no-dense] [--no-sweep] [--no-orders]
+                    [--copy-calibration]
 """
 import argparse
 import json
@@ -126,6 +130,27 @@ def time_attention(pisa, torch, Qd, Kd, Vd, idx, st, w, mode, reps):
     return a.elapsed_time(b) / reps
 
 
+def time_sdpa(torch, Qd, Kd, Vd, dense_flops, t_pisa):
+    """torch's fused dense attention (flash or memory-efficient backend only;
+    the math backend would materialise the L x L scores) on the same tensors."""
+    from torch.nn.attention import sdpa_kernel, SDPBackend
+    sdpa = torch.nn.functional.scaled_dot_product_attention
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            o = sdpa(Qd, Kd, Vd)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(torch.cuda.current_stream())
+            for _ in range(3):
+                o = sdpa(Qd, Kd, Vd)
+            b.record(torch.cuda.current_stream())
+            b.synchronize()
+        del o
+    except RuntimeError as ex:
+        return {"unavailable": str(ex)[:200]}
+    ms = a.elapsed_time(b) / 3
+    return {"ms": ms, "tflops": dense_flops / ms / 1e9, "speedup_of_pisa_attention": ms / t_pisa}
+
+
 def cpu_baseline(w, budget_s=20.0):
     """The fp64 oracle on whole heads of the same workload, until ~budget_s."""
     import numpy as np
@@ -163,7 +188,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4, choices=[3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense comparators (all blocks exact; torch SDPA)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the density sweep of the main workload")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-orders", action="store_true",
                     help="skip timing the zeroth-order and per-block first-order modes")
@@ -193,7 +221,7 @@ def main():
         torch.cuda.synchronize()
         del x, y
 
-    def run(wid, steps, warmup, with_dense, split=True, orders=False):
+    def run(wid, steps, warmup, with_dense, split=True, orders=False, sweep=False):
         w = wl.WORKLOADS[wid]
         log(f"{w.name}: generating inputs")
         Q, K, V = wl.make_inputs(w)
@@ -224,6 +252,21 @@ def main():
             fd = flops(w, nb)["exact"]
             res["dense"] = {"ms": t_dense, "tflops": fd / t_dense / 1e9,
                             "speedup_of_pisa_attention": t_dense / ph["attention"]}
+            del dense_idx
+            res["sdpa"] = time_sdpa(torch, Qd, Kd, Vd, fd, ph["attention"])
+        if sweep:
+            log(f"{w.name}: density sweep")
+            rows = []
+            for k in (w.nb // 2, w.nb // 4, w.nb // 8, w.nb // 16):
+                idx_k = pisa.route(Qd, st, k, w.lam, w.block)
+                fk = flops(w, k)
+                t_a = time_attention(pisa, torch, Qd, Kd, Vd, idx_k, st, w, "approx", 5)
+                t_d = time_attention(pisa, torch, Qd, Kd, Vd, idx_k, st, w, "drop", 5)
+                rows.append({"k": k, "density": k / w.nb,
+                             "approx_ms": t_a, "approx_tflops": fk["attention"] / t_a / 1e9,
+                             "drop_ms": t_d, "exact_tflops": fk["exact"] / t_d / 1e9})
+                del idx_k
+            res["density_sweep"] = rows
         if orders:
             # the other treatments of the unselected blocks, same inputs and idx
             log(f"{w.name}: zeroth-order and per-block first-order modes")
@@ -258,7 +301,7 @@ def main():
         return w, res
 
     w, main_res = run(args.workload, args.steps, args.warmup, not args.no_dense,
-                      not args.no_exact_split, not args.no_orders)
+                      not args.no_exact_split, not args.no_orders, not args.no_sweep)
     f = flops(w, w.k)
     ms = main_res["wall_ms_per_step"]
     t_attn = main_res["phases_ms"]["attention"]
