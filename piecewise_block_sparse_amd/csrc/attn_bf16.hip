@@ -28,14 +28,12 @@
 // the same ring (a centroid chunk has the layout of a K / V chunk).
 #include "common.hpp"
 #include "launch.hpp"
+#include "lds_stream.hpp"
 
 namespace pisa {
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) void gvoid;
-typedef __attribute__((address_space(3))) void lvoid;
-typedef __attribute__((address_space(3))) s16x4 ls16x4;
 
 template <int D_, int BLK_, int CK_>
 struct Cfg {
@@ -66,78 +64,6 @@ struct Cfg {
   static constexpr int RP = (2 * CK < D) ? 2 * CK : D;
   static constexpr int HP = D / RP;
 };
-
-// 16-byte slot of logical column chunk c in row r is c ^ swz(r).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  return (D == 128) ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
-}
-
-// Copies global -> LDS with global_load_lds_dwordx4: lane l copies 16 bytes
-// from gbase + voff(l) + imm into LDS at m0 + imm + 16 l (the immediate offset
-// moves both addresses).  Issued from asm so the compiler does not track the
-// copies: it neither orders later LDS reads of the other ring stage behind
-// them nor waits on them; every use of a stage is preceded by wait_vm0() and a
-// workgroup barrier instead.  The instructions have no register result.
-//
-// A stage holds the K chunk (bytes [0, SUBB)) and the V chunk ([SUBB, 2 SUBB));
-// each is NDMA/2 pieces of 1 KB = RPD rows.  Wave w copies pieces
-// w H .. w H + H - 1 of each half (H = DPW / 2), so one scalar base and one M0
-// serve a half and the pieces follow as immediates 0, 1024, ...  Lane l writes
-// slot l % CPR of row RPD n + l / CPR of piece n; that slot holds logical
-// column chunk (l % CPR) ^ swz(row), so the lane's global offset within the
-// wave's piece u is fixed for the whole kernel (H registers per lane).
-template <class C>
-struct DmaOff {
-  unsigned v[C::DPW / 2];
-};
-
-template <class C>
-__device__ __forceinline__ DmaOff<C> dma_lane_offsets(int w, int lane) {
-  DmaOff<C> o;
-#pragma unroll
-  for (int u = 0; u < C::DPW / 2; ++u) {
-    const int r = (w * (C::DPW / 2) + u) * C::RPD + lane / C::CPR;
-    o.v[u] = 2u * ((lane / C::CPR) * C::D + 8 * ((lane % C::CPR) ^ swz<C::D>(r)));
-  }
-  return o;
-}
-
-// H consecutive 1 KB pieces: global gbase + 1024 u, LDS m0v + 1024 u
-template <class C>
-__device__ __forceinline__ void dma_half(const void* gbase, unsigned m0v, const DmaOff<C>& o) {
-  if constexpr (C::DPW / 2 == 4) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "global_load_lds_dwordx4 %1, %5\n\t"
-        "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
-        "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
-        "global_load_lds_dwordx4 %4, %5 offset:3072"
-        :
-        : "s"(m0v), "v"(o.v[0]), "v"(o.v[1]), "v"(o.v[2]), "v"(o.v[3]), "s"(gbase)
-        : "memory", "m0");
-  } else {
-    static_assert(C::DPW / 2 == 2, "2 or 4 pieces per wave and half");
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "global_load_lds_dwordx4 %1, %3\n\t"
-        "global_load_lds_dwordx4 %2, %3 offset:1024"
-        :
-        : "s"(m0v), "v"(o.v[0]), "v"(o.v[1]), "s"(gbase)
-        : "memory", "m0");
-  }
-}
-
-// gK, gV: first byte of the K and V chunk; stage_m0: LDS address of the stage
-template <class C>
-__device__ __forceinline__ void dma_stage(const char* gK, const char* gV, unsigned stage_m0,
-                                          int w, const DmaOff<C>& loff) {
-  const unsigned wo = (unsigned)w * (C::DPW / 2) * 1024u;
-  dma_half<C>(gK + wo, stage_m0 + wo, loff);
-  dma_half<C>(gV + wo, stage_m0 + C::SUBB + wo, loff);
-}
-
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Online-softmax state of one lane (one query row, half of each key tile).
 template <int D>
@@ -176,7 +102,7 @@ __device__ __forceinline__ float row_max(float x) {
 template <class C>
 struct Offsets {
   int koff[C::KS];
-  int voff[C::MT][2];
+  TrOff<C> tr;
 };
 
 template <class C>
@@ -186,28 +112,15 @@ __device__ __forceinline__ Offsets<C> make_offsets(int lane) {
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks)
     o.koff[ks] = q32 * C::RB + (((2 * ks + hh) ^ swz<C::D>(q32)) << 4);
-  const int j = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = 4 * hh + 8 * h + (j >> 2);
-      const int chunk = (32 * mt + 16 * (g & 1)) / 8 + ((j & 3) >> 1);
-      o.voff[mt][h] = row * C::RB + ((chunk ^ swz<C::D>(row)) << 4) + 8 * (j & 1);
-    }
+  o.tr = tr_offsets<C>(lane);
   return o;
 }
 
-// A operand of O^T += V^T P^T for 16-key slab sl and d-tile mt: two
-// transposing reads of 4 keys each.
+// A operand of O^T += V^T P^T for 16-key slab sl and d-tile mt; its key order
+// within the slab is the one the lane's P registers hold.
 template <class C>
 __device__ __forceinline__ u32x4 v_frag(const char* vst, int sl, int mt, const Offsets<C>& off) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (ls16x4*)(vst + sl * 16 * C::RB + off.voff[mt][0]));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (ls16x4*)(vst + sl * 16 * C::RB + off.voff[mt][1]));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  return tr_frag<C>(vst, sl, mt, off.tr);
 }
 
 // exp2 weights -> bf16 MFMA B operands, and the sum of the same bf16 weights.

@@ -16,35 +16,70 @@
 // buffer, reduced to Hbar, then M_j is read off the buffer.
 #include "common.hpp"
 #include "launch.hpp"
+#include "lds_stream.hpp"
 
 namespace pisa {
 namespace {
 
-template <int D, int BLK>
+// Streaming configuration: 32-token chunks of K and V through a four-stage
+// LDS ring (the layout of lds_stream.hpp), four waves, each owning TM x TM
+// 32x32 tiles of the d x d product.
+template <int D_, int BLK_>
 struct SCfg {
-  static constexpr int NT = 256;
-  static constexpr int ROW = BLK + 8;                 // LDS row (tokens) of K^T / V^T, padded
-  static constexpr int SUB = (BLK / 8) * (D / 8);     // 8x8 sub-tiles per tensor
-  static constexpr int PER_T = (2 * SUB + NT - 1) / NT;
+  static constexpr int D = D_, BLK = BLK_;
+  static constexpr int NW = 4, NT = 64 * NW;
+  static constexpr int CK = 32;                       // tokens per chunk
+  static constexpr int CPB = BLK / CK;                // chunks per block
+  static constexpr int NSL = CK / 16;                 // 16-token MFMA k-steps per chunk
+  static constexpr int RB = 2 * D, CPR = D / 8, SUBB = CK * RB, STB = 2 * SUBB;
+  static constexpr int NDMA = STB / 1024, DPW = NDMA / NW, RPD = 1024 / RB;
+  // ring stages: 64-token blocks end every two chunks, and run best at three
+  // workgroups per CU (three 16 KB stages each at d = 128); 128-token blocks
+  // at two workgroups per CU with four stages
+  static constexpr int NS = (BLK == 64) ? 3 : 4;
   static constexpr int TM = (D == 128) ? 2 : 1;       // 32x32 output tiles per wave, per dim
-  static_assert(2 * D <= NT, "column sums use one thread per column");
+  static_assert(BLK % CK == 0 && NDMA % NW == 0 && DPW % 2 == 0, "chunking");
 };
 
-// STORE: pass 2 also writes the optional H_j (fp32) and H_j^T (bf16) outputs;
-// without them pass 2 fits 256 registers and runs two workgroups per CU.
+// Orders one wave's own LDS accesses among its lanes (no workgroup barrier).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Sum of the 8 bf16 values of a fragment, added to acc (v_dot2 against 1;
+// the pairs are taken from the bf16 view of the fragment).
+__device__ __forceinline__ float frag_sum(const u32x4& f, float acc) {
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+  const bf16x8 v = as_bf16x8(f);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+  return acc;
+}
+
+// One workgroup per group of kStatsGroup consecutive blocks of one head.  The
+// group's tokens stream through the ring in 32-token chunks; for each 16-token
+// slab every wave reads its K^T and V fragments with transposing LDS reads
+// (both operands index tokens the same way), accumulates K_j^T V_j on MFMA and
+// the column sums of K and V from the same fragments (lanes l and l + 32 hold
+// the two halves of a column's tokens).  At the end of a block the sums give
+// kbar_j and sigma_j, and H_j = K_j^T V_j - kbar_j^T sigma_j.
+// STORE: pass 2 also writes the optional H_j (fp32) and H_j^T (bf16) outputs.
 template <int D, int BLK, bool PASS2, bool STORE>
-__global__ __launch_bounds__(256, (PASS2 && STORE) ? 1 : 2) void stats_bf16_kernel(
+__global__ __launch_bounds__(256, (PASS2 && STORE) ? 2 : (BLK == 64 ? 3 : 2)) void stats_bf16_kernel(
     const bf16* __restrict__ K, const bf16* __restrict__ V, int nb, float* __restrict__ centroid,
     float* __restrict__ vsum, float* __restrict__ partial, const float* __restrict__ hbar_frag,
     float* __restrict__ M, float* __restrict__ Hout, bf16* __restrict__ pk_cen,
     bf16* __restrict__ pk_vsum, bf16* __restrict__ Ht, const int32_t* __restrict__ lens,
     int heads) {
   using C = SCfg<D, BLK>;
-  __shared__ __attribute__((aligned(16))) bf16 Kt[D * C::ROW];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[D * C::ROW];
-  __shared__ float s_k[D];
-  __shared__ float s_v[D];
-  __shared__ float s_red[4];
+  constexpr int TM = C::TM;
+  __shared__ __attribute__((aligned(1024))) char ring[C::NS * C::STB];
+  __shared__ float s_kv[C::NW][2][TM * 32];              // per wave: its kbar and sigma entries
+  __shared__ float s_sq[kStatsGroup][C::NW];              // per block and wave: part of ||H_j - Hbar||^2
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q32 = lane & 31, hh = lane >> 5;
@@ -53,174 +88,213 @@ __global__ __launch_bounds__(256, (PASS2 && STORE) ? 1 : 2) void stats_bf16_kern
   const int j0 = grp * kStatsGroup;
   const int j1 = min(nb, j0 + kStatsGroup);
   const size_t L = (size_t)nb * BLK;
-  const bf16* Kh = K + (size_t)bh * L * D;
-  const bf16* Vh = V + (size_t)bh * L * D;
-  const int mt0 = (w >> 1) * C::TM, nt0 = (w & 1) * C::TM;
+  const int mt0 = (w >> 1) * TM, nt0 = (w & 1) * TM;
+  const bool kout = nt0 == 0, vout = mt0 == 0;            // waves that write centroid / value sum
   const int Lv = valid_len(lens, bh, heads, (int)L);      // tokens past Lv are not counted
 
-  f32x16 acc[C::TM][C::TM];
+  f32x16 acc[TM][TM];
 #pragma unroll
-  for (int a = 0; a < C::TM; ++a)
+  for (int a = 0; a < TM; ++a)
 #pragma unroll
-    for (int b = 0; b < C::TM; ++b) acc[a][b] = f32x16{};
+    for (int b = 0; b < TM; ++b) acc[a][b] = f32x16{};
 
-  // pass 2: this lane's Hbar entries, stored by the reduction in fragment order
-  // (4 consecutive floats per (tile, row group)); re-read per block from L2
-  // rather than held in 64 registers for the whole loop
-  const float* hbf = PASS2 ? hbar_frag + (size_t)bh * D * D + (size_t)w * C::TM * C::TM * 1024 + 4 * lane
-                           : nullptr;
+  // pass 2: this lane's Hbar entries (stored by the reduction in fragment
+  // order: 4 consecutive floats per tile and row group), held for the whole
+  // group; loaded before the ring starts so no wait for them lands in the loop
+  f32x4 hb[TM][TM][4];
+  if (PASS2) {
+    const float* hbf = hbar_frag + (size_t)bh * D * D + (size_t)w * TM * TM * 1024 + 4 * lane;
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TM; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          hb[a][b][g] = *reinterpret_cast<const f32x4*>(hbf + ((a * TM + b) * 4 + g) * 256);
+  }
 
-  u32x4 regs[C::PER_T][8];
-  auto gload = [&](int j) {
+  const DmaOff<C> loff = dma_lane_offsets<C>(w, lane);
+  const int ws = __builtin_amdgcn_readfirstlane(w);        // wave index as a scalar
+  int ao[TM][2], bo[TM][2];                               // this wave's tiles' read offsets
 #pragma unroll
-    for (int u = 0; u < C::PER_T; ++u) {
-      const int p = tid + u * C::NT;
-      if (p < 2 * C::SUB) {
-        const bf16* X = ((p < C::SUB) ? Kh : Vh) + (size_t)j * BLK * D;
-        const int q = p % C::SUB;
-        const int g = q % (BLK / 8), c = q / (BLK / 8);
+  for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) regs[u][e] = ld16(X + (8 * g + e) * D + 8 * c);
-      }
+    for (int h = 0; h < 2; ++h) {
+      ao[a][h] = tr_lane_offset<C>(lane, mt0 + a, h);
+      bo[a][h] = tr_lane_offset<C>(lane, nt0 + a, h) + C::SUBB;
     }
+  const unsigned ring_m0 = (unsigned)(uintptr_t)(lvoid*)ring;
+  const int nch = (j1 - j0) * C::CPB;                     // the group's tokens are contiguous
+  const char* Kb = reinterpret_cast<const char*>(K + ((size_t)bh * L + (size_t)j0 * BLK) * D);
+  const char* Vb = reinterpret_cast<const char*>(V + ((size_t)bh * L + (size_t)j0 * BLK) * D);
+  auto issue = [&](int u) {                 // copy chunk u into stage u % NS
+    const size_t off = (size_t)u * C::SUBB;
+    dma_stage<C>(Kb + off, Vb + off, ring_m0 + (unsigned)((u % C::NS) * C::STB), ws, loff);
   };
-  auto lstore = [&](int nj) {
-#pragma unroll
-    for (int u = 0; u < C::PER_T; ++u) {
-      const int p = tid + u * C::NT;
-      if (p < 2 * C::SUB) {
-        bf16* Xt = (p < C::SUB) ? Kt : Vt;
-        const int q = p % C::SUB;
-        const int g = q % (BLK / 8), c = q / (BLK / 8);
-        // tokens 8 g + e at or past the block's valid count are stored as zeros
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (8 * g + e >= nj) regs[u][e] = u32x4{0u, 0u, 0u, 0u};
-        u32x4 col[8];
-        transpose8x8(regs[u], col);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) st16(Xt + (8 * c + i) * C::ROW + 8 * g, col[i]);
-      }
-    }
-  };
+  for (int u = 0; u < C::NS - 1 && u < nch; ++u) issue(u);
+  wait_vm0();   // the first chunks and the Hbar entries; no compiler-placed waits in the loop
 
-  gload(j0);
-  for (int j = j0; j < j1; ++j) {
+  float ks[TM], vs[TM];                    // this lane's half of the block's column sums
+#pragma unroll
+  for (int a = 0; a < TM; ++a) ks[a] = vs[a] = 0.f;
+  // Per-block outputs are written after the loop: stores count in vmcnt with
+  // the copies, so a store issued between copies would hold up every later
+  // wait for a chunk.  Pass 1 keeps the lane's centroid / value-sum entries of
+  // the group's blocks in a window shifted by one block at each block end
+  // (entry kStatsGroup - 1 is the newest); pass 2 keeps M_j in LDS.
+  float ocen[TM][kStatsGroup], ovs[TM][kStatsGroup];
+
+  for (int t = 0; t < nch; ++t) {
+    // chunk t: wait for it (chunks t + 1 .. t + NS - 2 may be in flight),
+    // publish it, and refill the stage read in the previous step
+    wait_groups<C>(min(C::NS - 2, nch - 1 - t));
+    __syncthreads();
+    if (t + C::NS - 1 < nch) issue(t + C::NS - 1);
+    const int j = j0 + t / C::CPB, tb = (t % C::CPB) * C::CK;
     const int nj = block_count(Lv, j, BLK);
-    __syncthreads();
-    lstore(nj);
-    __syncthreads();
-    if (j + 1 < j1) gload(j + 1);
-
-    // centroid (mean of keys) and value sum, one thread per column
-    if (tid < 2 * D) {
-      const bf16* rp = (tid < D) ? (Kt + tid * C::ROW) : (Vt + (tid - D) * C::ROW);
-      float s = 0.f;
-#pragma unroll
-      for (int c8 = 0; c8 < BLK / 8; ++c8) {
-        const bf16x8 v = as_bf16x8(ld16(rp + 8 * c8));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s += (float)v[e];
+    char* stage = ring + (t % C::NS) * C::STB;
+    if (nj < tb + C::CK) {
+      // tokens at or past the block's valid count are stored as zeros
+      const int r0 = max(nj - tb, 0);
+      for (int e = tid; e < 2 * (C::CK - r0) * C::CPR; e += C::NT) {
+        const int half = e / ((C::CK - r0) * C::CPR), q = e % ((C::CK - r0) * C::CPR);
+        st16(stage + half * C::SUBB + (r0 + q / C::CPR) * C::RB + 16 * (q % C::CPR),
+             u32x4{0u, 0u, 0u, 0u});
       }
-      const size_t prow = ((size_t)bh * ((nb + BLK - 1) / BLK * BLK) + j) * D;
-      if (tid < D) {
-        const float kbar = (nj == BLK) ? s * (1.f / BLK) : (nj > 0 ? s / (float)nj : 0.f);
-        s_k[tid] = kbar;
-        if (!PASS2) {
-          centroid[((size_t)bh * nb + j) * D + tid] = kbar;
-          if (pk_cen) pk_cen[prow + tid] = (bf16)kbar;
+      __syncthreads();
+    }
+#pragma unroll
+    for (int sl = 0; sl < C::NSL; ++sl) {
+      u32x4 fa[TM], fb[TM];
+#pragma unroll
+      for (int a = 0; a < TM; ++a) fa[a] = tr_read<C>(stage, sl, ao[a][0], ao[a][1]);
+#pragma unroll
+      for (int b = 0; b < TM; ++b) fb[b] = tr_read<C>(stage, sl, bo[b][0], bo[b][1]);
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b) acc[a][b] = mfma32(as_bf16x8(fa[a]), as_bf16x8(fb[b]), acc[a][b]);
+#pragma unroll
+      for (int a = 0; a < TM; ++a) ks[a] = frag_sum(fa[a], ks[a]);
+#pragma unroll
+      for (int b = 0; b < TM; ++b) vs[b] = frag_sum(fb[b], vs[b]);
+    }
+    if (t % C::CPB != C::CPB - 1) continue;
+
+    // ---- end of block j: centroid (mean of keys) and value sum
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+      const float sk = ks[a] + __shfl_xor(ks[a], 32);
+      const float sv = vs[a] + __shfl_xor(vs[a], 32);
+      ks[a] = vs[a] = 0.f;
+      const float kbar = (nj == BLK) ? sk * (1.f / BLK) : (nj > 0 ? sk / (float)nj : 0.f);
+      if (hh == 0) {
+        s_kv[w][0][32 * a + q32] = kbar;
+        s_kv[w][1][32 * a + q32] = sv;
+      }
+      if (!PASS2) {
+#pragma unroll
+        for (int g = 0; g + 1 < kStatsGroup; ++g) {
+          ocen[a][g] = ocen[a][g + 1];
+          ovs[a][g] = ovs[a][g + 1];
         }
-      } else {
-        s_v[tid - D] = s;
-        if (!PASS2) {
-          vsum[((size_t)bh * nb + j) * D + (tid - D)] = s;
-          if (pk_vsum) pk_vsum[prow + (tid - D)] = (bf16)s;
-        }
+        ocen[a][kStatsGroup - 1] = kbar;
+        ovs[a][kStatsGroup - 1] = sv;
       }
     }
+    // every wave summed its own rows and columns, so the exchange stays
+    // inside the wave: no workgroup barrier at the end of a block
+    wave_sync();
 
-    // K_j^T V_j on MFMA: A = K^T rows (key dim), B = V^T rows (value dim), k = tokens
-    if (PASS2) {
+    // H_j = K_j^T V_j - kbar_j^T sigma_j (pass 1: summed over the group)
 #pragma unroll
-      for (int a = 0; a < C::TM; ++a)
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < C::TM; ++b) acc[a][b] = f32x16{};
-    }
-#pragma unroll
-    for (int ks = 0; ks < BLK / 16; ++ks) {
-      bf16x8 A[C::TM], Bv[C::TM];
-#pragma unroll
-      for (int a = 0; a < C::TM; ++a)
-        A[a] = as_bf16x8(ld16(Kt + (32 * (mt0 + a) + q32) * C::ROW + 16 * ks + 8 * hh));
-#pragma unroll
-      for (int b = 0; b < C::TM; ++b)
-        Bv[b] = as_bf16x8(ld16(Vt + (32 * (nt0 + b) + q32) * C::ROW + 16 * ks + 8 * hh));
-#pragma unroll
-      for (int a = 0; a < C::TM; ++a)
-#pragma unroll
-        for (int b = 0; b < C::TM; ++b) acc[a][b] = mfma32(A[a], Bv[b], acc[a][b]);
-    }
-    __syncthreads();
-
-    // H_j = K_j^T V_j - kbar_j^T sigma_j
-#pragma unroll
-    for (int a = 0; a < C::TM; ++a)
-#pragma unroll
-      for (int b = 0; b < C::TM; ++b)
+      for (int b = 0; b < TM; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int ra = 32 * (mt0 + a) + 8 * (r / 4) + 4 * hh + (r % 4);
-          const int cb = 32 * (nt0 + b) + q32;
-          acc[a][b][r] -= s_k[ra] * s_v[cb];
+          const int ra = 32 * a + 8 * (r / 4) + 4 * hh + (r % 4);
+          acc[a][b][r] -= s_kv[w][0][ra] * s_kv[w][1][32 * b + q32];
         }
+    wave_sync();                            // reads done before the next block's writes
 
     if (PASS2) {
       float sq = 0.f;
       float* Hj = (STORE && Hout) ? Hout + ((size_t)bh * nb + j) * D * D : nullptr;
 #pragma unroll
-      for (int a = 0; a < C::TM; ++a)
+      for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < C::TM; ++b)
+        for (int b = 0; b < TM; ++b)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 h4 = *reinterpret_cast<const f32x4*>(hbf + ((a * C::TM + b) * 4 + g) * 256);
+          for (int g = 0; g < 4; ++g)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               const int r = 4 * g + rr;
               const float x = acc[a][b][r];
-              const float dlt = x - h4[rr];
+              const float dlt = x - hb[a][b][g][rr];
               sq += dlt * dlt;
               if (Hj) Hj[(32 * (mt0 + a) + 8 * (r / 4) + 4 * hh + (r % 4)) * D + 32 * (nt0 + b) + q32] = x;
             }
-          }
       if (STORE && Ht) {
         // H_j^T in bf16: row = value dim, 4 consecutive key-dim columns per store
-        bf16* Hj = Ht + ((size_t)bh * nb + j) * D * D;
+        bf16* Hjt = Ht + ((size_t)bh * nb + j) * D * D;
 #pragma unroll
-        for (int a = 0; a < C::TM; ++a)
+        for (int a = 0; a < TM; ++a)
 #pragma unroll
-          for (int b = 0; b < C::TM; ++b)
+          for (int b = 0; b < TM; ++b)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
               const f32x16& x = acc[a][b];
               const u32x2 v = {pack2(x[4 * g4], x[4 * g4 + 1]), pack2(x[4 * g4 + 2], x[4 * g4 + 3])};
-              st8(Hj + (size_t)(32 * (nt0 + b) + q32) * D + 32 * (mt0 + a) + 8 * g4 + 4 * hh, v);
+              st8(Hjt + (size_t)(32 * (nt0 + b) + q32) * D + 32 * (mt0 + a) + 8 * g4 + 4 * hh, v);
             }
       }
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
-      if (lane == 0) s_red[w] = sq;
-      __syncthreads();
-      if (tid == 0) M[(size_t)bh * nb + j] = nj > 0 ? sqrtf(s_red[0] + s_red[1] + s_red[2] + s_red[3]) : 0.f;
+      if (lane == 0) s_sq[j - j0][w] = (nj > 0) ? sq : -1.f;     // -1: empty block
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b) acc[a][b] = f32x16{};
+    }
+  }
+
+  // ---- the group's per-block outputs (the loop ends with a full wait)
+  const int ng = j1 - j0;
+  if (PASS2) {
+    __syncthreads();
+    if (tid < ng) {
+      const float* q = s_sq[tid];
+      M[(size_t)bh * nb + j0 + tid] = q[0] < 0.f ? 0.f : sqrtf(q[0] + q[1] + q[2] + q[3]);
+    }
+  } else {
+    const size_t nbp = (size_t)(nb + BLK - 1) / BLK * BLK;
+#pragma unroll
+    for (int g = 0; g < kStatsGroup; ++g) {
+      const int jj = j0 + g - (kStatsGroup - ng);          // block of window entry g
+      if (g < kStatsGroup - ng || hh != 0) continue;
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        if (kout) {
+          const int dk = 32 * (mt0 + a) + q32;
+          centroid[((size_t)bh * nb + jj) * D + dk] = ocen[a][g];
+          if (pk_cen) pk_cen[((size_t)bh * nbp + jj) * D + dk] = (bf16)ocen[a][g];
+        }
+        if (vout) {
+          const int dv = 32 * (nt0 + a) + q32;
+          vsum[((size_t)bh * nb + jj) * D + dv] = ovs[a][g];
+          if (pk_vsum) pk_vsum[((size_t)bh * nbp + jj) * D + dv] = (bf16)ovs[a][g];
+        }
+      }
     }
   }
 
   if (!PASS2) {
     float* P = partial + ((size_t)bh * ngrp + grp) * D * D;
 #pragma unroll
-    for (int a = 0; a < C::TM; ++a)
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-      for (int b = 0; b < C::TM; ++b)
+      for (int b = 0; b < TM; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           P[(32 * (mt0 + a) + 8 * (r / 4) + 4 * hh + (r % 4)) * D + 32 * (nt0 + b) + q32] = acc[a][b][r];
