@@ -10,8 +10,8 @@
 // j, written in ascending order.
 //
 // One workgroup = R waves = R query blocks of one head (R = 8 when there are at
-// least 512 blocks to score, so every thread owns a centroid, else 4; more rows
-// per workgroup means fewer re-reads of the head's centroids).  Each wave pools its
+// least 256 blocks to score, else 4; each centroid is read from L2 once per
+// workgroup, so more rows per workgroup means fewer re-reads of it).  Each wave pools its
 // block's queries with fully unrolled 16-byte loads (the HBM-bound part); for
 // the scores each thread owns one centroid and forms its dot products with all
 // R pooled queries (broadcast LDS reads); each wave then selects its row's
@@ -174,15 +174,37 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
   // per wave.  Lane l owns candidates j = l + 64 u.  Each pass histograms the
   // next 8-bit digit of the candidates still in play, finds the digit value d*
   // holding the k-th largest, selects the candidates above it and keeps those
-  // equal to it in play.  After 8 passes the ones left tie exactly with the
-  // k-th largest score; the lowest block ids among them fill the rest.
+  // equal to it in play.  After the last pass the ones left tie exactly with
+  // the k-th largest score; the lowest block ids among them fill the rest.
   const int nu = nbp / 64;                                // candidates per lane (<= 32)
   unsigned inplay = 0u, chosen = 0u;
   for (int u = 0; u < nu; ++u)
     if (lane + 64 * u < nne) inplay |= 1u << u;
   const int kk = (ni > 0) ? min(k, nne) : 0;            // blocks this row can hold
   int krem = kk;
-  for (int pass = 7; pass >= 0; --pass) {
+  // Digits above the highest bit in which the candidates' keys differ are the
+  // same for all of them (on these scores: the sign and most of the exponent),
+  // so those passes would split nothing: start below them.
+  int top_pass = 0;
+  {
+    unsigned long long kand = ~0ull, kor = 0ull;
+    for (int u = 0; u < nu; ++u)
+      if ((inplay >> u) & 1u) {
+        const unsigned long long key = order_key(sc[lane + 64 * u]);
+        kand &= key;
+        kor |= key;
+      }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const unsigned alo = __shfl_xor((unsigned)kand, off), ahi = __shfl_xor((unsigned)(kand >> 32), off);
+      const unsigned olo = __shfl_xor((unsigned)kor, off), ohi = __shfl_xor((unsigned)(kor >> 32), off);
+      kand &= ((unsigned long long)ahi << 32) | alo;
+      kor |= ((unsigned long long)ohi << 32) | olo;
+    }
+    const unsigned long long diff = kor & ~kand;          // bits that differ somewhere
+    if (diff != 0ull) top_pass = (63 - __clzll((long long)diff)) / 8;
+  }
+  for (int pass = top_pass; pass >= 0; --pass) {
     // every candidate still in play is needed: take them all and stop early
     int ip = __popc(inplay);
 #pragma unroll
@@ -304,7 +326,7 @@ template <int D, int BLK, typename T>
 hipError_t route_t(const RouteArgs& a) {
   int nbp = 64;
   while (nbp < a.nb) nbp <<= 1;
-  return a.nb >= 512 ? route_launch<D, BLK, T, 8>(a, nbp) : route_launch<D, BLK, T, 4>(a, nbp);
+  return a.nb >= 256 ? route_launch<D, BLK, T, 8>(a, nbp) : route_launch<D, BLK, T, 4>(a, nbp);
 }
 
 template <typename T>
