@@ -70,12 +70,15 @@ def profiled_traffic(workload_name):
     import hashlib
     import re
     path = os.path.join(ROOT, "profiles", f"kernels_{workload_name}.md")
-    src = os.path.join(ROOT, "piecewise_block_sparse_amd", "csrc", "attn_bf16.hip")
     if not os.path.exists(path):
         return None
+    # the stamp covers every source the attention kernel is compiled from
+    stamp = hashlib.sha256()
+    for f in ("attn_bf16.hip", "lds_stream.hpp", "common.hpp"):
+        stamp.update(open(os.path.join(ROOT, "piecewise_block_sparse_amd", "csrc", f), "rb").read())
     m = re.search(r"attn_bf16_kernel traffic_bytes_per_launch=(\d+) read=(\d+) write=(\d+) "
                   r"avg_ns=(\d+) source=([0-9a-f]+)", open(path).read())
-    if not m or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != m.group(5):
+    if not m or stamp.hexdigest()[:16] != m.group(5):
         return None
     return {"total": int(m.group(1)), "read": int(m.group(2)), "write": int(m.group(3)),
             "profiled_avg_ms": int(m.group(4)) / 1e6}
