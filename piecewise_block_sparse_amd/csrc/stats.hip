@@ -301,60 +301,81 @@ __global__ __launch_bounds__(256, (PASS2 && STORE) ? 2 : (BLK == 64 ? 3 : 2)) vo
   }
 }
 
-// Hbar[bh][e] = (1/nb) sum_g parts[bh][g][e], summed in fp64 in group order.
-// With a bf16 pack: also writes Hbar^T in bf16 and zeroes the padding rows
-// (nb .. nbp) of the packed centroids and value sums.
+// Hbar[bh] = (1 / n) sum_g parts[bh][g] (n = the non-empty blocks: all nb
+// without lengths), summed in fp64 in group order (fixed, reproducible).  One
+// workgroup per 32x32 tile of one head; each thread sums 4 adjacent entries of
+// a tile row with 16-byte loads.  The tile is then staged in LDS so that the
+// other layouts are written with whole rows too: Hbar in the fragment order of
+// pass 2 (a tile is one contiguous 4 KB region there) and, with a bf16 pack,
+// Hbar^T in bf16.  The pack's padding rows (nb .. nbp) of the centroids and
+// value sums are zeroed here as well.
+template <int D>
 __global__ __launch_bounds__(256) void hbar_reduce_kernel(const float* __restrict__ parts, int ngrp,
-                                                          int nb, int D, int total,
-                                                          float* __restrict__ hbar,
+                                                          int nb, float* __restrict__ hbar,
                                                           bf16* __restrict__ pk_hbart,
                                                           bf16* __restrict__ pk_cen,
                                                           bf16* __restrict__ pk_vsum, int nbp,
                                                           const int32_t* __restrict__ lens,
                                                           int heads, int BLK,
                                                           float* __restrict__ hbar_frag) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  const int DD = D * D;
-  if (t < total) {
-    const int bh = t / DD, e = t - bh * DD;
-    const float* p = parts + (size_t)bh * ngrp * DD + e;
-    // loads of 8 groups in flight, summed in group order (fixed, reproducible)
-    double s = 0.0;
-    int g = 0;
-    for (; g + 8 <= ngrp; g += 8) {
-      float x[8];
+  constexpr int TT = D / 32, DD = D * D;
+  __shared__ float tile[32][33];
+  const int bh = blockIdx.x / (TT * TT), tix = blockIdx.x - bh * (TT * TT);
+  const int mt = tix / TT, nt = tix - mt * TT;
+  const int t = threadIdx.x, r = t >> 3, c0 = (t & 7) * 4;
+  const size_t e0 = (size_t)(32 * mt + r) * D + 32 * nt + c0;
+  const float* p = parts + (size_t)bh * ngrp * DD + e0;
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+  int g = 0;
+  for (; g + 4 <= ngrp; g += 4) {
+    f32x4 x[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = p[(size_t)(g + u) * DD];
+    for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const f32x4*>(p + (size_t)(g + u) * DD);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += (double)x[u];
-    }
-    for (; g < ngrp; ++g) s += (double)p[(size_t)g * DD];
-    // mean over the non-empty blocks (all nb without lengths)
-    const int nne = (valid_len(lens, bh, heads, nb * BLK) + BLK - 1) / BLK;
-    const float v = nne > 0 ? (float)(s / nne) : 0.f;
-    hbar[t] = v;
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s[q] += (double)x[u][q];
+  }
+  for (; g < ngrp; ++g) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(p + (size_t)g * DD);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s[q] += (double)x[q];
+  }
+  const int nne = (valid_len(lens, bh, heads, nb * BLK) + BLK - 1) / BLK;
+  f32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = nne > 0 ? (float)(s[q] / nne) : 0.f;
+  *reinterpret_cast<f32x4*>(hbar + (size_t)bh * DD + e0) = v;
+  if (hbar_frag || pk_hbart) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tile[r][c0 + q] = v[q];
+    __syncthreads();
     if (hbar_frag) {
-      // fragment order of the statistics kernel's pass 2: wave w = 2 (row tile / TM) +
-      // (column tile / TM) holds tiles (a, b); lane q32 + 32 hh holds rows
-      // 32 mt + 8 g + 4 hh + rr of column 32 nt + q32; 4 rows rr are contiguous
-      const int TM = (D == 128) ? 2 : 1;
-      const int row = e / D, col = e - (e / D) * D;
-      const int mt = row >> 5, rem = row & 31, nt = col >> 5;
+      // pass 2's order: wave w = 2 (row tile / TM) + (column tile / TM) holds
+      // tiles (a, b); within a tile, lane ln = col + 32 hh holds rows
+      // 8 g + 4 hh + rr (rr = 0 .. 3 contiguous), at ((g * 64 + ln) * 4 + rr)
+      constexpr int TM = (D == 128) ? 2 : 1;
       const int wv = 2 * (mt / TM) + nt / TM, a = mt % TM, b = nt % TM;
-      const int g = rem >> 3, hh = (rem >> 2) & 1, rr = rem & 3, ln = (col & 31) + 32 * hh;
-      hbar_frag[(size_t)bh * DD + ((((wv * TM + a) * TM + b) * 4 + g) * 64 + ln) * 4 + rr] = v;
+      float* fr = hbar_frag + (size_t)bh * DD + (size_t)((wv * TM + a) * TM + b) * 1024;
+      const int fg = t >> 6, ln = t & 63, hh = ln >> 5, col = ln & 31;
+      f32x4 o;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) o[rr] = tile[8 * fg + 4 * hh + rr][col];
+      *reinterpret_cast<f32x4*>(fr + 4 * t) = o;
     }
     if (pk_hbart) {
-      const int a = e / D, c = e - a * D;
-      pk_hbart[(size_t)bh * DD + (size_t)c * D + a] = (bf16)v;
+      // Hbar^T: row 32 nt + rt holds column 32 nt + rt of the tile
+      const int rt = t >> 3, cc = (t & 7) * 4;
+      const u32x2 pk = {pack2(tile[cc][rt], tile[cc + 1][rt]), pack2(tile[cc + 2][rt], tile[cc + 3][rt])};
+      st8(pk_hbart + (size_t)bh * DD + (size_t)(32 * nt + rt) * D + 32 * mt + cc, pk);
     }
   }
   if (pk_cen && nbp > nb) {
     const int per = (nbp - nb) * D;
-    const int npad = (total / DD) * per;
-    for (int u = t; u < npad; u += gridDim.x * 256) {
-      const int bh = u / per, r = u - bh * per;
-      const size_t o = ((size_t)bh * nbp + nb) * D + r;
+    const int npad = (int)(gridDim.x / (TT * TT)) * per;
+    for (int u = blockIdx.x * 256 + t; u < npad; u += gridDim.x * 256) {
+      const int b2 = u / per, rr = u - b2 * per;
+      const size_t o = ((size_t)b2 * nbp + nb) * D + rr;
       pk_cen[o] = (bf16)0.f;
       pk_vsum[o] = (bf16)0.f;
     }
@@ -617,10 +638,9 @@ hipError_t stats_bf16_t(const StatsArgs& a) {
                      (bf16*)nullptr, a.lens, a.heads);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int total = a.bh * D * D;
-  hipLaunchKernelGGL(hbar_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, a.stream,
-                     (const float*)parts, ngrp, a.nb, D, total, a.hbar, pk_hbart, pk_cen, pk_vsum,
-                     nbp, a.lens, a.heads, BLK, frag);
+  hipLaunchKernelGGL(hbar_reduce_kernel<D>, dim3(a.bh * (D / 32) * (D / 32)), dim3(256), 0, a.stream,
+                     (const float*)parts, ngrp, a.nb, a.hbar, pk_hbart, pk_cen, pk_vsum, nbp,
+                     a.lens, a.heads, BLK, frag);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   auto pass2 = (a.H || a.ht) ? stats_bf16_kernel<D, BLK, true, true> : stats_bf16_kernel<D, BLK, true, false>;
@@ -642,10 +662,9 @@ hipError_t stats_f32_t(const StatsArgs& a) {
                      a.lens, a.heads);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int total = a.bh * D * D;
-  hipLaunchKernelGGL(hbar_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, a.stream,
-                     (const float*)Hbuf, a.nb, a.nb, D, total, a.hbar, (bf16*)nullptr,
-                     (bf16*)nullptr, (bf16*)nullptr, a.nb, a.lens, a.heads, a.BLK, (float*)nullptr);
+  hipLaunchKernelGGL(hbar_reduce_kernel<D>, dim3(a.bh * (D / 32) * (D / 32)), dim3(256), 0, a.stream,
+                     (const float*)Hbuf, a.nb, a.nb, a.hbar, (bf16*)nullptr, (bf16*)nullptr,
+                     (bf16*)nullptr, a.nb, a.lens, a.heads, a.BLK, (float*)nullptr);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (a.spectral) return launch_spectral<D>(Hbuf, a.hbar, a.bh, a.nb, a.M, a);
