@@ -45,18 +45,6 @@ __device__ __forceinline__ unsigned pack2(float lo, float hi) {
   return __builtin_bit_cast(unsigned, v);
 }
 
-// Transpose an 8x8 tile of bf16 held as 8 rows of 16 bytes: out[i] is column i,
-// element e of out[i] = element i of row e.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&row)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      out[i][q] = __builtin_amdgcn_perm(row[2 * q + 1][i >> 1], row[2 * q][i >> 1], sel);
-  }
-}
-
 // Workgroups are dealt round-robin over the 8 XCDs (id % 8).  Map them so that
 // every XCD walks one contiguous range of logical ids; neighbouring query
 // blocks of a head then share that XCD's L2.  Bijective for any grid size.
