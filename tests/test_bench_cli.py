@@ -1,0 +1,50 @@
+"""Host-side checks of bench.py's command line (no GPU needed)."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    # one process drives one GPU; N > 1 must stop before touching a device
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr
+    assert p.stdout == ""
+
+
+def test_profiled_traffic_is_read_only_for_the_profiled_kernel_source(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    # the committed summaries carry a stamp of the attention sources they were taken with
+    for name in ("video-dit-L", "video-dit-S"):
+        t = bench.profiled_traffic(name)
+        if t is not None:
+            assert t["total"] == t["read"] + t["write"] > 0
+    # a summary whose stamp does not match the sources yields no traffic figure
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "kernels_x.md").write_text(
+        "attn_bf16_kernel traffic_bytes_per_launch=3 read=2 write=1 avg_ns=5 source=0000000000000000\n")
+    csrc = tmp_path / "piecewise_block_sparse_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for f in ("attn_bf16.hip", "lds_stream.hpp", "common.hpp"):
+        (csrc / f).write_text("x")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.profiled_traffic("x") is None
+    assert bench.profiled_traffic("missing") is None
+
+
+def test_flops_model_matches_the_stated_algorithmic_work():
+    sys.path.insert(0, ROOT)
+    import bench
+    from piecewise_block_sparse_amd import workloads as wl
+    w = wl.WORKLOADS[4]                       # video-DiT-L: 40 heads, 32K, d 128, B 128, k 32
+    f = bench.flops(w, w.k)
+    assert f["exact"] == 40 * 256 * 4 * 128 * (32 * 128) * 128          # 2748.8 GFLOP
+    assert round(f["exact"] / 1e9, 1) == 2748.8
+    assert f["step"] == f["exact"] + f["approx"] + f["stats"] + f["route"]
+    json.dumps(f)
