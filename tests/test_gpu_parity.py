@@ -429,6 +429,42 @@ def test_runs_are_bitwise_reproducible(torch):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("wid", [2, 4])
+def test_step_replays_in_a_captured_graph(torch, wid):
+    """The library's calls only enqueue kernels on the caller's stream (no host
+    synchronisation, allocation or memset inside it; the binding's output
+    tensors come from torch's graph pool), so a whole step can be captured in a
+    HIP graph.  Every replay, with eager steps in between, equals the eager step
+    bit for bit."""
+    pisa = pisa_mod()
+    w, Q, K, V, Qd, Kd, Vd = inputs(wid)
+    ws = torch.empty(pisa.workspace_size(Kd, w.block), dtype=torch.uint8, device="cuda")
+
+    def step():
+        st = pisa.precompute(Kd, Vd, w.block, workspace=ws)
+        idx = pisa.route(Qd, st, w.k, w.lam, w.block)
+        return idx, pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode="approx")
+
+    ref_idx, ref = step()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        g_idx, g_out = step()
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(g_idx, ref_idx)
+        assert torch.equal(g_out, ref)
+        step()                                # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_end_to_end_routing_diagnostic(torch):
     """Each side routes with its own statistics; reported, not gated (fp32 vs
     fp64 M differs by ~1e-7 relative, which can flip near-ties)."""
