@@ -333,7 +333,12 @@ def main():
                      "traffic": traffic["total"] if traffic else None,
                      "traffic_detail": dict(traffic, algorithmic_min=min_bytes) if traffic else None,
                      "kernel": f"attn_bf16_kernel (d={w.head_dim}, block={w.block})",
-                     "avg_launch_ms": t_attn},
+                     "avg_launch_ms": t_attn,
+                     # the metric's MFMA utilisation: algorithmic bf16 rate over the peak
+                     "mfma_util": {
+                         "attention": achieved / MFMA_BF16_PEAK_TFLOPS,
+                         "exact_phase": (main_res["tflops"]["exact_phase"] / MFMA_BF16_PEAK_TFLOPS
+                                         if "exact_phase" in main_res["tflops"] else None)}},
         "phases": main_res,
     }
     if not args.no_secondary:
