@@ -492,11 +492,13 @@ def test_route_max_blocks(torch):
     check_route(idx.cpu().numpy(), scores, k, name="nb2048")
 
 
-def test_attention_max_blocks_all_modes(torch):
-    """nb = 2048 (the largest supported block count) with a large k: every mode
-    against the oracle on sampled query blocks (first, middle, last)."""
+@pytest.mark.parametrize("B", [64, 128])
+def test_attention_max_blocks_all_modes(torch, B):
+    """nb = 2048 (the largest supported block count) with a large k: the
+    statistics, and every mode against the oracle on sampled query blocks
+    (first, middle, last), for both block sizes' kernels."""
     pisa = pisa_mod()
-    B, L, d, k = 64, 2048 * 64, 128, 300
+    L, d, k = 2048 * B, 128, 300
     Q, K, V = (_rand(torch, (1, 1, L, d), "bf16", s) for s in (14, 15, 16))
     K = wl.round_bf16(K + np.repeat(_rand(torch, (1, 1, L // B, d), "fp32", 17) * 0.5, B, axis=2))
     Qd, Kd, Vd = (to_dev(x, "bf16") for x in (Q, K, V))
@@ -505,12 +507,13 @@ def test_attention_max_blocks_all_modes(torch):
     outs = {m: to_np(pisa.attention(Qd, Kd, Vd, idx, st, B, mode=m)) for m in VL_MODES}
     torch.cuda.synchronize()
     ref_st = oracle.precompute(K, V, B)
+    check_stats(st, ref_st, name=f"nb2048/B{B}")
     qb = [(0, 0, i) for i in (0, 1024, 2047)]
     for m, code in VL_MODES.items():
         ref = oracle.attention(Q, K, V, idx.cpu().numpy(), ref_st["centroid"], ref_st["vsum"],
                                ref_st["Hbar"], code, 1 / math.sqrt(d), B, qblocks=qb, H=ref_st["H"])
-        err, mab = check_attention(outs[m], ref, "bf16", name=f"nb2048/{m}")
-        print(f"nb2048 {m}: rel-L2 {err:.3e} max-abs {mab:.3e}")
+        err, mab = check_attention(outs[m], ref, "bf16", name=f"nb2048/B{B}/{m}")
+        print(f"nb2048 B{B} {m}: rel-L2 {err:.3e} max-abs {mab:.3e}")
 
 
 @pytest.mark.parametrize("wid", [2, 5])
