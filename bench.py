@@ -14,12 +14,14 @@ every block exact, `sdpa` torch's fused dense attention on the same tensors
 (context only, never part of the library); `density_sweep` re-routes the same
 inputs at top-k 128 / 64 / 32 / 16 of 256 blocks and times both modes; `orders`
 times the zeroth-order and the per-block first-order treatments of the
-unselected blocks on the same inputs; `cpu_baseline` is the fp64 oracle on a
-bounded sample.
+unselected blocks on the same inputs; `roofline.attainable` is the MFMA rate
+the chip sustains for the exact phase's per-chunk instruction mix on random
+operands (libpisa_probe), beside the published peak; `cpu_baseline` is the
+fp64 oracle on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4|3]
                     [--no-cpu-baseline] [--no-dense] [--no-sweep] [--no-orders]
-                    [--copy-calibration]
+                    [--no-probe] [--copy-calibration]
 """
 import argparse
 import json
@@ -184,6 +186,25 @@ def cpu_baseline(w, budget_s=20.0):
             "seconds_per_step_extrapolated": spent * w.heads / done}
 
 
+def attainable_rates(pisa):
+    """The bf16 MFMA rate gfx950 sustains for the exact phase's per-chunk
+    instruction mix at the attention kernel's occupancy (libpisa_probe):
+    MFMAs alone and the full chunk step, on N(0, 1)-like operands, and the
+    full step on zeros (the same instructions without operand toggling)."""
+    import ctypes
+    probe = pisa._lib.load_probe()
+    out = {"unit": "TFLOP/s", "data": "N(0,1)-like bf16 operands (zeros where named)",
+           "probe": "pisa_probe_chunk_rate (include/pisa_probe.h)"}
+    for name, mix, zeros in (("mfma_only", 0, 0), ("chunk_mix", 1, 0), ("chunk_mix_zeros", 1, 1)):
+        r = ctypes.c_double(0.0)
+        rc = probe.pisa_probe_chunk_rate(mix, zeros, 2000, 5, ctypes.byref(r))
+        if rc != 0:
+            raise RuntimeError(f"pisa_probe_chunk_rate({mix}, {zeros}) failed with HIP error {rc}")
+        out[name] = r.value
+    log(f"attainable MFMA rates: {out}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +221,8 @@ def main():
                     help="skip timing the zeroth-order and per-block first-order modes")
     ap.add_argument("--no-exact-split", action="store_true",
                     help="skip the keep-or-drop timing that splits exact / approximate phases")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip measuring the attainable MFMA rate of the kernel's chunk mix")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args()
@@ -341,6 +364,11 @@ def main():
                                          if "exact_phase" in main_res["tflops"] else None)}},
         "phases": main_res,
     }
+    if not args.no_probe:
+        att = attainable_rates(pisa)
+        if "exact_phase" in main_res["tflops"]:
+            att["exact_phase_frac_of_chunk_mix"] = main_res["tflops"]["exact_phase"] / att["chunk_mix"]
+        line["roofline"]["attainable"] = att
     if not args.no_secondary:
         other = 3 if args.workload == 4 else 4
         _, res2 = run(other, max(5, args.steps // 2), 2, False)

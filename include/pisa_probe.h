@@ -1,0 +1,35 @@
+/* libpisa_probe: measurement helper, not part of the attention library.
+ *
+ * Measures the bf16 MFMA rate that gfx950 sustains for the per-chunk
+ * instruction mix of libpisa's attention kernel (exact phase, d = 128,
+ * 32-key chunks, three 4-wave workgroups per CU), on operands that toggle like
+ * real activations.  The published dense peak assumes the nominal clock; under
+ * sustained MFMA work on random data the chip holds a lower one, so this rate
+ * is the attainable ceiling the kernel is compared with.
+ */
+#ifndef PISA_PROBE_H
+#define PISA_PROBE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* mix    0: MFMAs only (S^T = K Q^T as 8 dependent 32x32x16 MFMAs, then
+ *           O^T += V^T P^T as 8 MFMAs; P is S truncated to bf16);
+ *        1: the full chunk step (the same MFMAs plus the softmax weights, one
+ *           workgroup barrier and the global -> LDS copy of the next chunk).
+ * zeros  0: N(0, 1)-like bf16 operands; 1: all operands zero.
+ * iters  chunks per wave per launch (>= 1); reps timed launches (>= 1) after
+ *        one warm-up launch.
+ * tflops out: algorithmic MFMA rate, TFLOP/s (host pointer).
+ * Runs on the current device and the null stream, allocates and frees its
+ * own 2 MB source and output buffers, and synchronizes before returning.
+ * Returns 0 (hipSuccess) or the first HIP error code; invalid arguments give
+ * hipErrorInvalidValue and launch nothing. */
+int pisa_probe_chunk_rate(int mix, int zeros, int iters, int reps, double* tflops);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -9,6 +9,7 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpisa.so")
+PROBE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpisa_probe.so")
 
 PISA_OK = 0
 STATUS_NAMES = {0: "PISA_OK", 1: "PISA_ERR_NULL", 2: "PISA_ERR_SHAPE", 3: "PISA_ERR_ARG",
@@ -25,6 +26,8 @@ NORM_SPECTRAL = 1
 # every symbol the header declares
 EXPORTS = ("pisa_version", "pisa_status_string", "pisa_last_error", "pisa_workspace_size",
            "pisa_packed_size", "pisa_precompute", "pisa_route", "pisa_attention")
+# ... and every symbol include/pisa_probe.h declares (libpisa_probe.so)
+PROBE_EXPORTS = ("pisa_probe_chunk_rate",)
 
 
 class PisaShape(ctypes.Structure):
@@ -81,3 +84,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
 def check(fn: str, status: int) -> None:
     if status != PISA_OK:
         raise PisaError(fn, status, load().pisa_last_error().decode())
+
+
+def load_probe(path: str = PROBE_PATH) -> ctypes.CDLL:
+    """Load the measurement probe library (include/pisa_probe.h)."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m piecewise_block_sparse_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.pisa_probe_chunk_rate.restype = ctypes.c_int
+    lib.pisa_probe_chunk_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.POINTER(ctypes.c_double)]
+    return lib

@@ -3,8 +3,10 @@
     python -m piecewise_block_sparse_amd.build          # or build() from Python
 
 Each HIP source is compiled to an object with hipcc for gfx950 and the objects
-are linked into piecewise_block_sparse_amd/libpisa.so.  The compile always runs
-(no up-to-date check), so a call after editing a source rebuilds it.
+are linked into piecewise_block_sparse_amd/libpisa.so; the measurement probe
+(csrc/probe_rate.hip, include/pisa_probe.h) becomes libpisa_probe.so.  The
+compile always runs (no up-to-date check), so a call after editing a source
+rebuilds it.
 """
 from __future__ import annotations
 
@@ -19,7 +21,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpisa.so")
+PROBE_LIB = os.path.join(PKG, "libpisa_probe.so")
 SOURCES = ["api.hip", "attn_bf16.hip", "attn_f32.hip", "stats.hip", "route.hip"]
+PROBE_SOURCES = ["probe_rate.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -48,13 +52,15 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         return obj, out
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(compile_one, SOURCES))
+        results = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
     for _, out in results:
         if verbose and out.strip():
             print(out)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]])
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        objs = [o for (o, _), src in zip(results, SOURCES + PROBE_SOURCES) if src in srcs]
+        tmp = lib + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+        os.replace(tmp, lib)
     return LIB
 
 

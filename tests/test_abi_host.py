@@ -42,6 +42,22 @@ def test_exports_every_declared_symbol(lib):
     assert lib.pisa_version() == 100
 
 
+def test_probe_library_exports_its_declared_symbol():
+    if not os.path.exists(_lib.PROBE_PATH):
+        pytest.fail("libpisa_probe.so is not built (run python -m piecewise_block_sparse_amd.build)")
+    header = open(os.path.join(ROOT, "include", "pisa_probe.h")).read()
+    declared = set(re.findall(r"\b(pisa_\w+)\s*\(", header))
+    assert declared == set(_lib.PROBE_EXPORTS)
+    probe = _lib.load_probe()
+    for name in declared:
+        assert hasattr(probe, name), name
+    # invalid arguments are rejected on the host (hipErrorInvalidValue = 1), nothing launched
+    out = ctypes.c_double(0.0)
+    assert probe.pisa_probe_chunk_rate(2, 0, 10, 1, ctypes.byref(out)) == 1
+    assert probe.pisa_probe_chunk_rate(0, 0, 0, 1, ctypes.byref(out)) == 1
+    assert probe.pisa_probe_chunk_rate(0, 0, 10, 1, None) == 1
+
+
 def test_status_strings(lib):
     for code in range(7):
         assert lib.pisa_status_string(code)
