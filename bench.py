@@ -11,7 +11,9 @@ Prints ONE JSON line.  `value` is the algorithmic TFLOP/s of the whole step;
 (the dominant one) against the bf16 MFMA peak; `phases` splits the step by
 kernel (HIP events on the launch stream); `dense` is the same kernel run with
 every block exact, `sdpa` torch's fused dense attention on the same tensors
-(context only, never part of the library); `density_sweep` re-routes the same
+(context only, never part of the library); `step_event_ms` gives p10 / p50 /
+p90 of the timed steps (HIP events) and `cold_step_ms` the same for steps run
+after a 512 MB scratch write (caches flushed); `density_sweep` re-routes the same
 inputs at top-k 128 / 64 / 32 / 16 of 256 blocks and times both modes; `orders`
 times the zeroth-order and the per-block first-order treatments of the
 unselected blocks on the same inputs; `roofline.attainable` is the MFMA rate
@@ -115,11 +117,43 @@ def timed_phases(pisa, torch, Qd, Kd, Vd, w, k, steps, warmup, mode="approx"):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     ph = {"precompute": 0.0, "route": 0.0, "attention": 0.0}
+    per_step = []
     for e in evs:
         ph["precompute"] += e[0].elapsed_time(e[1])
         ph["route"] += e[1].elapsed_time(e[2])
         ph["attention"] += e[2].elapsed_time(e[3])
-    return wall_ms, {n: v / steps for n, v in ph.items()}, (st, idx, out)
+        per_step.append(e[0].elapsed_time(e[3]))
+    ph = {n: v / steps for n, v in ph.items()}
+    ph["step_event_ms"] = percentiles(per_step)
+    return wall_ms, ph, (st, idx, out)
+
+
+def percentiles(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def cold_steps(pisa, torch, Qd, Kd, Vd, w, reps=10):
+    """Whole steps with the caches flushed first: a 512 MB scratch write (more
+    than the 256 MB MALL and every L2) before each timed step."""
+    stream = torch.cuda.current_stream()
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    times = []
+    for r in range(reps + 1):
+        scratch.fill_(r & 255)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        st = pisa.precompute(Kd, Vd, w.block)
+        idx = pisa.route(Qd, st, w.k, w.lam, w.block)
+        pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode="approx")
+        b.record(stream)
+        b.synchronize()
+        if r > 0:                                   # the first one warms the allocator
+            times.append(a.elapsed_time(b))
+    del scratch
+    return percentiles(times)
 
 
 def time_attention(pisa, torch, Qd, Kd, Vd, idx, st, w, mode, reps):
@@ -256,7 +290,10 @@ def main():
         log(f"{w.name}: timing {steps} steps")
         wall_ms, ph, (st, idx, _) = timed_phases(pisa, torch, Qd, Kd, Vd, w, w.k, steps, warmup)
         f, by = flops(w, w.k), bytes_moved(w)
-        res = {"wall_ms_per_step": wall_ms / steps, "phases_ms": ph}
+        step_pct = ph.pop("step_event_ms")
+        res = {"wall_ms_per_step": wall_ms / steps, "phases_ms": ph, "step_event_ms": step_pct}
+        log(f"{w.name}: cold-cache steps")
+        res["cold_step_ms"] = cold_steps(pisa, torch, Qd, Kd, Vd, w)
         res["tflops"] = {
             "step": f["step"] / (wall_ms / steps) / 1e9,
             "attention": f["attention"] / ph["attention"] / 1e9,
