@@ -63,6 +63,7 @@ struct Cfg {
   // per-block first order: H_j^T (D rows) streams as HP ring chunks of RP rows
   static constexpr int RP = (2 * CK < D) ? 2 * CK : D;
   static constexpr int HP = D / RP;
+  static_assert(HP <= 2, "Hbar^T streams in at most two parts");
 };
 
 // Online-softmax state of one lane (one query row, half of each key tile).
@@ -327,6 +328,25 @@ __device__ __forceinline__ void first_order_part(RowState<C::D>& st, const bf16x
   for (int mt = 0; mt < C::MT; ++mt) st.acc[mt] += (mt / MTP == part ? f : 0.f) * hq[mt % MTP];
 }
 
+// Global first-order term, part PART: the stage holds RP rows (value dims
+// PART * RP ..) of Hbar^T in the K-chunk layout; acc[d] += f * (q Hbar)[d] for
+// those dims, q Hbar as MFMAs (A = Hbar^T rows from LDS, B = query fragments).
+template <class C, int PART>
+__device__ __forceinline__ void hbar_part(RowState<C::D>& st, const bf16x8 (&qf)[C::KS],
+                                          const char* stage, const Offsets<C>& off, float f) {
+  constexpr int MTP = C::RP / 32;                     // 32-row tiles per part
+#pragma unroll
+  for (int mtl = 0; mtl < MTP; ++mtl) {
+    if constexpr (PART * MTP + MTP <= C::MT) {
+      f32x16 hq = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        hq = mfma32(as_bf16x8(ld16(stage + mtl * 32 * C::RB + off.koff[ks])), qf[ks], hq);
+      st.acc[PART * MTP + mtl] += f * hq;
+    }
+  }
+}
+
 // fp32 statistics -> bf16 chunk of CK centroids / value sums in the stage
 // layout (used when no bf16 pack was supplied); rows past nb are zero.
 template <class C>
@@ -503,7 +523,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   }
   __syncthreads();
   const int ncnt = s_cnt[0];
-  const int nex = ncnt * SPB, ncen = nex + s_cnt[1], ntot = ncen + s_cnt[2] * C::HP;
+  // mixed order with the bf16 pack: Hbar^T streams as HP ring chunks after stage 2
+  const int nhb = (packed && order == kOrderMixed) ? C::HP : 0;
+  const int nex = ncnt * SPB, ncen = nex + s_cnt[1], nhbe = ncen + nhb, ntot = nhbe + s_cnt[2] * C::HP;
   const int ws = __builtin_amdgcn_readfirstlane(w);
   const unsigned lds_m0 = (unsigned)(uintptr_t)(lvoid*)lds;
   const char* Kb = reinterpret_cast<const char*>(Kh);
@@ -511,6 +533,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   const char* Cb = packed ? reinterpret_cast<const char*>(p.pk_cen + (size_t)bh * nbp * D) : nullptr;
   const char* Sb = packed ? reinterpret_cast<const char*>(p.pk_vsum + (size_t)bh * nbp * D) : nullptr;
   const char* Hb = first ? reinterpret_cast<const char*>(p.ht + (size_t)bh * nb * D * D) : nullptr;
+  const char* Hbt = nhb ? reinterpret_cast<const char*>(p.pk_hbart + (size_t)bh * D * D) : nullptr;
   // copy chunk t into stage t & 1
   auto issue = [&](int t) {
     const unsigned m0 = lds_m0 + (unsigned)((t & 1) * C::STB);
@@ -522,9 +545,13 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       const int tcv = __builtin_amdgcn_readfirstlane((int)s_clist[t - nex]);
       const size_t off = (size_t)tcv * CK * C::RB;
       dma_stage<C>(Cb + off, Sb + off, m0, ws, loff);
+    } else if (t < nhbe) {
+      // rows part * RP .. of Hbar^T (same layout as the H_j^T parts below)
+      const char* g = Hbt + (size_t)(t - ncen) * C::RP * C::RB;
+      dma_stage<C>(g, (2 * CK <= D) ? g + CK * C::RB : g, m0, ws, loff);
     } else {
       // rows part * RP .. of H_j^T; with RP = D < 2 CK the second half repeats them
-      const int hc = t - ncen;
+      const int hc = t - nhbe;
       const int j = __builtin_amdgcn_readfirstlane((int)s_list[ncnt + hc / C::HP]);
       const char* g = Hb + ((size_t)j * D + (size_t)(hc % C::HP) * C::RP) * C::RB;
       dma_stage<C>(g, (2 * CK <= D) ? g + CK * C::RB : g, m0, ws, loff);
@@ -574,7 +601,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       wait_vm0();
       __syncthreads();
       if (t + 1 < ntot) issue(t + 1);
-      const int hc = t - ncen;
+      const int hc = t - nhbe;
       const int j = (int)s_list[ncnt + hc / C::HP];
       first_order_part<C>(st, qf, lds + (t & 1) * C::STB, off, c2, scale,
                           p.pk_cen + ((size_t)bh * nbp + j) * D, hc % C::HP, hh);
@@ -597,24 +624,26 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   }
   if (approx && order == kOrderMixed) {
     // ---- stage 3: global first-order correction, acc += scale * (q Hbar) * sum alpha
+    // (sum alpha is complete once stage 2 is done; m does not move from here on)
     const float atot = row_sum(st.a);
     const float f = scale * atot;
     if (packed) {
-      // A operand (Hbar^T rows) straight from the bf16 pack, two d-tiles at a time
-      const bf16* hb = p.pk_hbart + ((size_t)bh * D + q32) * D + 8 * hh;
-#pragma unroll
-      for (int m0 = 0; m0 < C::MT; m0 += 2) {
-        u32x4 ha[2][C::KS];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks) ha[u][ks] = ld16(hb + (size_t)(32 * (m0 + u)) * D + 16 * ks);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          f32x16 hq = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks) hq = mfma32(as_bf16x8(ha[u][ks]), qf[ks], hq);
-          st.acc[m0 + u] += f * hq;
+      // the Hbar^T parts (HP <= 2), streamed through the ring behind the
+      // centroid chunks; each part owns compile-time accumulator tiles
+      if (t < nhbe) {
+        wait_vm0();
+        __syncthreads();
+        if (t + 1 < ntot) issue(t + 1);
+        hbar_part<C, 0>(st, qf, lds + (t & 1) * C::STB, off, f);
+        ++t;
+      }
+      if constexpr (C::HP > 1) {
+        if (t < nhbe) {
+          wait_vm0();
+          __syncthreads();
+          if (t + 1 < ntot) issue(t + 1);
+          hbar_part<C, 1>(st, qf, lds + (t & 1) * C::STB, off, f);
+          ++t;
         }
       }
     } else {
