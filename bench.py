@@ -23,7 +23,7 @@ fp64 oracle on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4|3]
                     [--no-cpu-baseline] [--no-dense] [--no-sweep] [--no-orders]
-                    [--no-probe] [--copy-calibration]
+                    [--no-cold] [--no-probe] [--copy-calibration]
 """
 import argparse
 import json
@@ -255,6 +255,8 @@ def main():
                     help="skip timing the zeroth-order and per-block first-order modes")
     ap.add_argument("--no-exact-split", action="store_true",
                     help="skip the keep-or-drop timing that splits exact / approximate phases")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache steps (e.g. under a counter profiler)")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip measuring the attainable MFMA rate of the kernel's chunk mix")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -281,7 +283,7 @@ def main():
         torch.cuda.synchronize()
         del x, y
 
-    def run(wid, steps, warmup, with_dense, split=True, orders=False, sweep=False):
+    def run(wid, steps, warmup, with_dense, split=True, orders=False, sweep=False, cold=True):
         w = wl.WORKLOADS[wid]
         log(f"{w.name}: generating inputs")
         Q, K, V = wl.make_inputs(w)
@@ -292,8 +294,9 @@ def main():
         f, by = flops(w, w.k), bytes_moved(w)
         step_pct = ph.pop("step_event_ms")
         res = {"wall_ms_per_step": wall_ms / steps, "phases_ms": ph, "step_event_ms": step_pct}
-        log(f"{w.name}: cold-cache steps")
-        res["cold_step_ms"] = cold_steps(pisa, torch, Qd, Kd, Vd, w)
+        if cold:
+            log(f"{w.name}: cold-cache steps")
+            res["cold_step_ms"] = cold_steps(pisa, torch, Qd, Kd, Vd, w)
         res["tflops"] = {
             "step": f["step"] / (wall_ms / steps) / 1e9,
             "attention": f["attention"] / ph["attention"] / 1e9,
@@ -364,7 +367,7 @@ def main():
         return w, res
 
     w, main_res = run(args.workload, args.steps, args.warmup, not args.no_dense,
-                      not args.no_exact_split, not args.no_orders, not args.no_sweep)
+                      not args.no_exact_split, not args.no_orders, not args.no_sweep, not args.no_cold)
     f = flops(w, w.k)
     ms = main_res["wall_ms_per_step"]
     t_attn = main_res["phases_ms"]["attention"]
@@ -408,7 +411,7 @@ def main():
         line["roofline"]["attainable"] = att
     if not args.no_secondary:
         other = 3 if args.workload == 4 else 4
-        _, res2 = run(other, max(5, args.steps // 2), 2, False)
+        _, res2 = run(other, max(5, args.steps // 2), 2, False, cold=not args.no_cold)
         line["secondary"] = {wl.WORKLOADS[other].name: res2}
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
