@@ -18,7 +18,8 @@ inputs at top-k 128 / 64 / 32 / 16 of 256 blocks and times both modes; `orders`
 times the zeroth-order and the per-block first-order treatments of the
 unselected blocks on the same inputs; `roofline.attainable` is the MFMA rate
 the chip sustains for the exact phase's per-chunk instruction mix on random
-operands (libpisa_probe), beside the published peak; `cpu_baseline` is the
+operands, and its streaming HBM read rate (libpisa_probe), beside the published
+peaks; `cpu_baseline` is the
 fp64 oracle on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4|3]
@@ -221,20 +222,28 @@ def cpu_baseline(w, budget_s=20.0):
 
 
 def attainable_rates(pisa):
-    """The bf16 MFMA rate gfx950 sustains for the exact phase's per-chunk
-    instruction mix at the attention kernel's occupancy (libpisa_probe):
-    MFMAs alone and the full chunk step, on N(0, 1)-like operands, and the
-    full step on zeros (the same instructions without operand toggling)."""
+    """What the chip sustains on this machine (libpisa_probe): the bf16 MFMA rate
+    of the exact phase's per-chunk instruction mix at the attention kernel's
+    occupancy (MFMAs alone and the full chunk step on N(0, 1)-like operands,
+    and the full step on zeros: the same instructions without operand
+    toggling), and the HBM rate of a plain 2 GiB streaming read."""
     import ctypes
     probe = pisa._lib.load_probe()
-    out = {"unit": "TFLOP/s", "data": "N(0,1)-like bf16 operands (zeros where named)",
-           "probe": "pisa_probe_chunk_rate (include/pisa_probe.h)"}
+    out = {"unit": "TFLOP/s (MFMA rates), GB/s (hbm_read_gbs)",
+           "data": "N(0,1)-like bf16 operands (zeros where named)",
+           "probe": "pisa_probe_chunk_rate, pisa_probe_read_rate (include/pisa_probe.h)"}
     for name, mix, zeros in (("mfma_only", 0, 0), ("chunk_mix", 1, 0), ("chunk_mix_zeros", 1, 1)):
         r = ctypes.c_double(0.0)
         rc = probe.pisa_probe_chunk_rate(mix, zeros, 2000, 5, ctypes.byref(r))
         if rc != 0:
             raise RuntimeError(f"pisa_probe_chunk_rate({mix}, {zeros}) failed with HIP error {rc}")
         out[name] = r.value
+    # the streaming kernels' yardstick: a plain 2 GiB streaming read
+    r = ctypes.c_double(0.0)
+    rc = probe.pisa_probe_read_rate(2 << 30, 5, ctypes.byref(r))
+    if rc != 0:
+        raise RuntimeError(f"pisa_probe_read_rate failed with HIP error {rc}")
+    out["hbm_read_gbs"] = r.value
     log(f"attainable MFMA rates: {out}")
     return out
 
@@ -408,6 +417,8 @@ def main():
         att = attainable_rates(pisa)
         if "exact_phase" in main_res["tflops"]:
             att["exact_phase_frac_of_chunk_mix"] = main_res["tflops"]["exact_phase"] / att["chunk_mix"]
+        att["precompute_frac_of_read"] = main_res["gbs"]["precompute"] / att["hbm_read_gbs"]
+        att["route_frac_of_read"] = main_res["gbs"]["route"] / att["hbm_read_gbs"]
         line["roofline"]["attainable"] = att
     if not args.no_secondary:
         other = 3 if args.workload == 4 else 4

@@ -1,6 +1,6 @@
-/* libpisa_probe: measurement helper, not part of the attention library.
+/* libpisa_probe: measurement helpers, not part of the attention library.
  *
- * Measures the bf16 MFMA rate that gfx950 sustains for the per-chunk
+ * Measures the HBM streaming-read rate, and the bf16 MFMA rate that gfx950 sustains for the per-chunk
  * instruction mix of libpisa's attention kernel (exact phase, d = 128,
  * 32-key chunks, three 4-wave workgroups per CU), on operands that toggle like
  * real activations.  The published dense peak assumes the nominal clock; under
@@ -10,9 +10,20 @@
 #ifndef PISA_PROBE_H
 #define PISA_PROBE_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Streaming read of a `bytes`-byte device buffer (a multiple of 16, at least
+ * 32 MiB; use far more than the 256 MB of on-chip caches, e.g. 2 GiB) by 8192
+ * workgroups of 256 threads with 16-byte loads, timed over `reps` (>= 1)
+ * launches after one warm-up.  gbs out: bytes read / time, GB/s (host
+ * pointer).  Current device, null stream; allocates and frees the buffer;
+ * synchronizes before returning.  Returns 0 (hipSuccess) or the first HIP
+ * error code; invalid arguments give hipErrorInvalidValue and launch nothing. */
+int pisa_probe_read_rate(size_t bytes, int reps, double* gbs);
 
 /* mix    0: MFMAs only (S^T = K Q^T as 8 dependent 32x32x16 MFMAs, then
  *           O^T += V^T P^T as 8 MFMAs; P is S truncated to bf16);

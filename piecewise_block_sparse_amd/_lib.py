@@ -27,7 +27,7 @@ NORM_SPECTRAL = 1
 EXPORTS = ("pisa_version", "pisa_status_string", "pisa_last_error", "pisa_workspace_size",
            "pisa_packed_size", "pisa_precompute", "pisa_route", "pisa_attention")
 # ... and every symbol include/pisa_probe.h declares (libpisa_probe.so)
-PROBE_EXPORTS = ("pisa_probe_chunk_rate",)
+PROBE_EXPORTS = ("pisa_probe_chunk_rate", "pisa_probe_read_rate")
 
 
 class PisaShape(ctypes.Structure):
@@ -94,4 +94,6 @@ def load_probe(path: str = PROBE_PATH) -> ctypes.CDLL:
     lib.pisa_probe_chunk_rate.restype = ctypes.c_int
     lib.pisa_probe_chunk_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.POINTER(ctypes.c_double)]
+    lib.pisa_probe_read_rate.restype = ctypes.c_int
+    lib.pisa_probe_read_rate.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
     return lib

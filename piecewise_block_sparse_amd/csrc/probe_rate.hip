@@ -19,6 +19,10 @@
 // Operands: Q in registers, K / V chunks copied from a 2 MB buffer (L2
 // resident) of N(0, 1)-like bf16 values; `zeros` = 1 fills everything with
 // zeros instead (the same instructions on operands that do not toggle).
+//
+// pisa_probe_read_rate measures the other roofline the library's streaming
+// kernels (statistics, routing) are held to: the HBM read rate of a plain
+// streaming reduction over a buffer much larger than the caches.
 #include "common.hpp"
 #include "lds_stream.hpp"
 #include "pisa_probe.h"
@@ -136,8 +140,66 @@ __global__ __launch_bounds__(256, 3) void probe_kernel(const char* src, float* o
   out[(size_t)blockIdx.x * 256 + tid] = r;
 }
 
+// Streaming read: workgroup b sums words [b * per, (b + 1) * per) of the buffer
+// with 16-byte loads, eight per lane in flight; the sum is written only if it
+// hits a sentinel, so the loads cannot be dropped.
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ p, size_t n16,
+                                                   unsigned* out, int per) {
+  constexpr int U = 8;
+  const size_t base = (size_t)blockIdx.x * per;
+  unsigned acc = 0u;
+  for (int i = threadIdx.x; i < per; i += 256 * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t e = base + i + u * 256;
+      v[u] = (i + u * 256 < per && e < n16) ? p[e] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u][0] + v[u][1] + v[u][2] + v[u][3];
+  }
+  if (acc == 0x9e3779b9u) out[blockIdx.x] = acc;
+}
+
 }  // namespace
 }  // namespace pisa
+
+extern "C" int pisa_probe_read_rate(size_t bytes, int reps, double* gbs) {
+  using namespace pisa;
+  constexpr int kGrid = 8192;
+  if (!gbs || reps < 1 || bytes < (size_t)kGrid * 4096 || bytes % 16 != 0) return (int)hipErrorInvalidValue;
+  const size_t n16 = bytes / 16;
+  const int per = (int)(n16 / kGrid);
+  char* buf = nullptr;
+  unsigned* out = nullptr;
+  hipEvent_t t0 = nullptr, t1 = nullptr;
+  hipError_t e = hipMalloc(&buf, bytes);
+  if (e == hipSuccess) e = hipMalloc(&out, kGrid * sizeof(unsigned));
+  if (e == hipSuccess) e = hipEventCreate(&t0);
+  if (e == hipSuccess) e = hipEventCreate(&t1);
+  if (e == hipSuccess) {
+    const int nwords = (int)(bytes / 4 < (size_t)INT32_MAX ? bytes / 4 : INT32_MAX);
+    fill_kernel<<<(nwords + 255) / 256, 256>>>(reinterpret_cast<unsigned*>(buf), nwords, 0);
+    auto launch = [&]() {
+      read_kernel<<<kGrid, 256>>>(reinterpret_cast<const u32x4*>(buf), n16, out, per);
+    };
+    launch();                                // warm-up
+    e = hipEventRecord(t0);
+    for (int r = 0; r < reps && e == hipSuccess; ++r) launch();
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess) e = hipEventRecord(t1);
+    if (e == hipSuccess) e = hipEventSynchronize(t1);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t0, t1);
+    const double read = (double)per * kGrid * 16.0 * reps;   // bytes the kernels read
+    if (e == hipSuccess) *gbs = read / (ms * 1e-3) * 1e-9;
+  }
+  if (t0) (void)hipEventDestroy(t0);
+  if (t1) (void)hipEventDestroy(t1);
+  if (out) (void)hipFree(out);
+  if (buf) (void)hipFree(buf);
+  return (int)e;
+}
 
 extern "C" int pisa_probe_chunk_rate(int mix, int zeros, int iters, int reps, double* tflops) {
   using namespace pisa;

@@ -56,6 +56,9 @@ def test_probe_library_exports_its_declared_symbol():
     assert probe.pisa_probe_chunk_rate(2, 0, 10, 1, ctypes.byref(out)) == 1
     assert probe.pisa_probe_chunk_rate(0, 0, 0, 1, ctypes.byref(out)) == 1
     assert probe.pisa_probe_chunk_rate(0, 0, 10, 1, None) == 1
+    assert probe.pisa_probe_read_rate(1 << 20, 1, ctypes.byref(out)) == 1      # below 32 MiB
+    assert probe.pisa_probe_read_rate((1 << 30) + 8, 1, ctypes.byref(out)) == 1  # not 16-byte
+    assert probe.pisa_probe_read_rate(1 << 30, 0, ctypes.byref(out)) == 1
 
 
 def test_status_strings(lib):

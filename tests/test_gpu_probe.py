@@ -21,3 +21,12 @@ def test_probe_rates_are_below_the_published_peak():
         rates[(mix, zeros)] = r.value
     # the softmax work can only slow the same MFMAs down (small launches are noisy)
     assert rates[(1, 0)] < 1.1 * rates[(0, 0)]
+
+
+def test_read_probe_is_below_the_published_hbm_peak():
+    import torch
+    torch.cuda.set_device(0)
+    probe = _lib.load_probe()
+    r = ctypes.c_double(0.0)
+    assert probe.pisa_probe_read_rate(1 << 30, 2, ctypes.byref(r)) == 0
+    assert math.isfinite(r.value) and 1000.0 < r.value < 8000.0 * 1.05, r.value
