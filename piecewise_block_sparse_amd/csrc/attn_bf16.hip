@@ -9,8 +9,13 @@
 // notes, section 3.3) runs stage 1 only.
 //
 // Work decomposition: one workgroup per (batch*head, query block); BLK/32
-// waves, each owning 32 query rows.  Everything is computed transposed so
-// that a lane owns one query row:
+// waves, each owning 32 query rows.  With 64-token blocks a workgroup takes
+// two neighbouring query blocks (four waves): their chunk stream is the union
+// of the two routed lists, in ascending block order, and each wave computes
+// only the blocks of its own query block, so every row sees the same sequence
+// of terms as alone, while each chunk copied to LDS serves four waves and the
+// register budget allows three waves per SIMD.  Everything is computed
+// transposed so that a lane owns one query row:
 //   S^T[key][query]  = K_chunk . Q^T      (A = K rows from LDS, B = Q fragments in VGPRs)
 //   O^T[d][query]   += V_chunk^T . P^T    (A = V read transposed from LDS, B = P from S^T)
 // The 32x32x16 result layout gives lane l the 16 keys {8(r/4) + 4(l/32) + r%4}
@@ -35,10 +40,16 @@ namespace {
 
 typedef __attribute__((address_space(1))) void gvoid;
 
-template <int D_, int BLK_, int CK_>
+// QB_: query blocks per workgroup.  With 64-token blocks two neighbouring
+// query blocks share one workgroup (QB = 2): the chunk stream is the union of
+// their routed KV blocks, and each wave computes only the blocks routed to its
+// own query block.  Four waves then share every chunk copied to LDS, as with
+// 128-token blocks.
+template <int D_, int BLK_, int CK_, int QB_ = 1>
 struct Cfg {
-  static constexpr int D = D_, BLK = BLK_, CK = CK_;
-  static constexpr int NW = BLK / 32;            // waves per workgroup
+  static constexpr int D = D_, BLK = BLK_, CK = CK_, QB = QB_;
+  static constexpr int WPQ = BLK / 32;           // waves per query block
+  static constexpr int NW = QB * WPQ;            // waves per workgroup
   static constexpr int NT = 64 * NW;             // threads
   static constexpr int RB = 2 * D;               // bytes per row
   static constexpr int CPR = D / 8;              // 16-byte slots per row
@@ -53,9 +64,10 @@ struct Cfg {
   static constexpr int DPW = NDMA / NW;          // ... per wave
   static constexpr int RPD = 1024 / RB;          // rows per 1 KB copy
   // waves per SIMD the register budget is sized for: three (<= 168 VGPRs)
-  // for d = 128, block 128 with 32-key chunks (three 4-wave groups per CU,
-  // 37 KB of LDS each); two otherwise
-  static constexpr int MINB = (D == 128 && BLK == 128 && CK == 32) ? 3 : 2;
+  // for d = 128 with 128 query rows per workgroup and 32-key chunks (three
+  // 4-wave groups per CU, 37 KB of LDS each); two otherwise
+  static constexpr int MINB = (D == 128 && QB * BLK == 128 && CK == 32) ? 3 : 2;
+  static_assert(QB == 1 || (QB == 2 && BLK == 64), "query-block pairs are for 64-token blocks");
   static_assert(NDMA % NW == 0, "copies split evenly over waves");
   static_assert(DPW % 2 == 0, "per-wave copies: half K, half V");
   static_assert(D * RB <= LDSB && (D / 2) * RB <= STB, "Hbar^T (fallback) halves fit the stages");
@@ -402,6 +414,8 @@ struct AttnPtrs {
 };
 
 constexpr int kBitWords = (kMaxBlocks + 128) / 32;
+constexpr int kIdMask = 0xfff;                  // block id bits of a list entry (ids < 4096)
+static_assert(kMaxBlocks <= kIdMask + 1, "block ids fit below the pair flags");
 
 // VL: sequences have valid lengths (lens); without, the length code compiles away.
 // FO: the per-block first order (its stage lives only in these instantiations,
@@ -412,46 +426,77 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
                                                              const int32_t* lens, int heads) {
   constexpr int D = C::D, BLK = C::BLK, CK = C::CK;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDSB];
-  __shared__ unsigned bits[kBitWords];
+  constexpr int QB = C::QB;
+  static_assert(QB == 1 || !FO, "the per-block first order runs one query block per workgroup");
+  __shared__ unsigned bits[QB][kBitWords];
+  __shared__ unsigned exb[QB == 2 ? 2 : 1][QB == 2 ? kBitWords : 1];   // pairs: exact blocks
   __shared__ short s_list[kMaxBlocks];                 // exact block ids of S_i, in order;
-                                                       // then (per-block first order) U_i
+                                                       // then (per-block first order) U_i.
+                                                       // Pairs: the union, ascending, with
+                                                       // bit 12 + q set if query block q
+                                                       // routes the block
   __shared__ short s_clist[kBitWords];                 // centroid chunks to sweep
   __shared__ int s_cnt[3];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q32 = lane & 31, hh = lane >> 5;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = logical / nb, i = logical - bh * nb;
+  const int ngrp = (nb + QB - 1) / QB;                 // workgroups per (batch, head)
+  const int bh = logical / ngrp, i0 = (logical - bh * ngrp) * QB;
+  const int qb = w / C::WPQ, wq = w - qb * C::WPQ;     // this wave: query block i0 + qb, rows 32 wq ..
+  const int i = i0 + qb;
+  const bool qvalid = i < nb;                          // (odd nb: the last pair has one block)
   const size_t L = (size_t)nb * BLK;
   const int nbp = (nb + BLK - 1) / BLK * BLK;
   const bf16* Kh = p.K + (size_t)bh * L * D;
   const bf16* Vh = p.V + (size_t)bh * L * D;
-  const int32_t* row = p.idx + ((size_t)bh * nb + i) * kmax;
   const bool packed = approx && p.pk_cen != nullptr;
   // valid tokens: blocks j < nne are non-empty; query block i holds ni queries
   const int Lv = VL ? valid_len(lens, bh, heads, (int)L) : (int)L;
   const int nne = VL ? (Lv + BLK - 1) / BLK : nb;
-  const int ni = VL ? block_count(Lv, i, BLK) : BLK;
-  if (VL && ni == 0) {
-    // a query block past the sequence: its rows are 0
-    bf16* ob = p.O + ((size_t)bh * L + (size_t)i * BLK) * D;
-    for (int e = tid; e < BLK * D / 8; e += C::NT) st16(ob + 8 * e, u32x4{0u, 0u, 0u, 0u});
+  const int ni = !qvalid ? 0 : (VL ? block_count(Lv, i, BLK) : BLK);
+  // the workgroup's query blocks past the sequence (or past nb) have no work
+  int nlive = 0;
+#pragma unroll
+  for (int q = 0; q < QB; ++q)
+    nlive += (i0 + q < nb) && (!VL || block_count(Lv, i0 + q, BLK) > 0);
+  if (nlive == 0) {
+    // query blocks past the sequence: their rows are 0
+    for (int q = 0; q < QB; ++q) {
+      if (i0 + q >= nb) break;
+      bf16* ob = p.O + ((size_t)bh * L + (size_t)(i0 + q) * BLK) * D;
+      for (int e = tid; e < BLK * D / 8; e += C::NT) st16(ob + 8 * e, u32x4{0u, 0u, 0u, 0u});
+    }
     return;
   }
+  const bool alive = ni > 0;                           // wave-uniform
   const bool first = FO && approx && order == kOrderFirst && packed && p.ht != nullptr;
 
-  if (approx) {
-    // bit j set: block j is exact (in S_i) or padding (j >= nb)
+  if (approx || QB == 2) {
+    // bits[q]: bit j set when block j is exact for query block i0 + q (in its
+    // S_i) or padding (j >= nne); exb[q] (pairs): the exact blocks alone
     for (int e = tid; e < nbp / 32; e += C::NT) {
       const int lo = 32 * e;
       unsigned pad = 0u;                                 // padding and empty blocks: j >= nne
       if (lo + 32 > nne) pad = (lo >= nne) ? ~0u : (~0u << (nne - lo));
-      bits[e] = pad;
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        bits[q][e] = pad;
+        if constexpr (QB == 2) exb[q][e] = 0u;
+      }
     }
     __syncthreads();
-    for (int e = tid; e < kmax; e += C::NT) {
-      const int j = row[e];
-      if (j >= 0 && j < nne) atomicOr(&bits[j >> 5], 1u << (j & 31));
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      if (i0 + q >= nb) break;
+      const int32_t* rq = p.idx + ((size_t)bh * nb + i0 + q) * kmax;
+      for (int e = tid; e < kmax; e += C::NT) {
+        const int j = rq[e];
+        if (j >= 0 && j < nne) {
+          atomicOr(&bits[q][j >> 5], 1u << (j & 31));
+          if constexpr (QB == 2) atomicOr(&exb[q][j >> 5], 1u << (j & 31));
+        }
+      }
     }
     __syncthreads();
   }
@@ -459,10 +504,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   // this lane's query row as 16-byte B-operand fragments (d = 16 ks + 8 hh + 0..7)
   bf16x8 qf[C::KS];
   {
-    const bf16* qrow = p.Q + ((size_t)bh * L + (size_t)i * BLK + 32 * w + q32) * D + 8 * hh;
+    const bf16* qrow = p.Q + ((size_t)bh * L + (size_t)(qvalid ? i : i0) * BLK + 32 * wq + q32) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_bf16x8(ld16(qrow + 16 * ks));
-    if (VL && 32 * w + q32 >= ni)                        // padding query: a zero row
+    if ((VL || QB == 2) && 32 * wq + q32 >= ni)          // padding query: a zero row
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
@@ -483,20 +528,42 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   const int nctile = packed ? nbp / CK : 0;
   if (w == 0) {
     int cnt = 0;
-    for (int e0 = 0; e0 < kmax; e0 += 64) {
-      const int e = e0 + lane;
-      const int j = (e < kmax) ? row[e] : -1;
-      const bool ok = j >= 0 && j < nne;
-      const unsigned long long m = __ballot(ok);
-      if (ok) s_list[cnt + __popcll(m & ((1ull << lane) - 1))] = (short)j;
-      cnt += __popcll(m);
+    if constexpr (QB == 1) {
+      const int32_t* row = p.idx + ((size_t)bh * nb + i) * kmax;
+      for (int e0 = 0; e0 < kmax; e0 += 64) {
+        const int e = e0 + lane;
+        const int j = (e < kmax) ? row[e] : -1;
+        const bool ok = j >= 0 && j < nne;
+        const unsigned long long m = __ballot(ok);
+        if (ok) s_list[cnt + __popcll(m & ((1ull << lane) - 1))] = (short)j;
+        cnt += __popcll(m);
+      }
+    } else {
+      // the union of the two rows, ascending (lane = bitmap word: nbp <= 2048)
+      const unsigned a = (lane < nbp / 32) ? exb[0][lane] : 0u;
+      const unsigned b = (lane < nbp / 32) ? exb[1][lane] : 0u;
+      const unsigned u = a | b;
+      const int n = __popc(u);
+      int pre = n;                                       // inclusive prefix over lanes
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(pre, o);
+        if (lane >= o) pre += y;
+      }
+      int pos = pre - n;
+      for (unsigned r = u; r; r &= r - 1) {
+        const int bit = __ffs(r) - 1;
+        s_list[pos++] = (short)((32 * lane + bit) | (((a >> bit) & 1u) << 12) | (((b >> bit) & 1u) << 13));
+      }
+      cnt = __shfl(pre, 63);
     }
     int ccnt = 0;
     for (int c0 = 0; c0 < nctile; c0 += 64) {
       const int tcv = c0 + lane;
       bool need = false;
       if (tcv < nctile)
-        for (int u = 0; u < CK / 32; ++u) need = need || (bits[tcv * (CK / 32) + u] != ~0u);
+        for (int q = 0; q < QB; ++q)
+          for (int u = 0; u < CK / 32; ++u) need = need || (bits[q][tcv * (CK / 32) + u] != ~0u);
       const unsigned long long m = __ballot(need);
       if (need) s_clist[ccnt + __popcll(m & ((1ull << lane) - 1))] = (short)tcv;
       ccnt += __popcll(m);
@@ -506,7 +573,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       // unselected blocks (bit clear), ascending, after the exact ids
       for (int c0 = 0; c0 < nb; c0 += 64) {
         const int j = c0 + lane;
-        const bool u = j < nb && !((bits[j >> 5] >> (j & 31)) & 1u);
+        const bool u = j < nb && !((bits[0][j >> 5] >> (j & 31)) & 1u);
         const unsigned long long m = __ballot(u);
         // exact ids plus U_i fill at most nb <= kMaxBlocks slots (more only for
         // an idx row with duplicate ids, whose excess is dropped)
@@ -538,7 +605,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   auto issue = [&](int t) {
     const unsigned m0 = lds_m0 + (unsigned)((t & 1) * C::STB);
     if (t < nex) {
-      const int j = __builtin_amdgcn_readfirstlane((int)s_list[t / SPB]);
+      const int j = __builtin_amdgcn_readfirstlane((int)s_list[t / SPB] & kIdMask);
       const size_t off = ((size_t)j * BLK + (size_t)(t % SPB) * CK) * C::RB;
       dma_stage<C>(Kb + off, Vb + off, m0, ws, loff);
     } else if (t < ncen) {
@@ -560,7 +627,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   if (ntot > 0) issue(0);
   // keys of exact chunk u inside the sequence (fewer only in a ragged last block)
   auto keys_of = [&](int u) {
-    return VL ? min(max(block_count(Lv, (int)s_list[u / SPB], BLK) - (u % SPB) * CK, 0), CK) : CK;
+    return VL ? min(max(block_count(Lv, (int)s_list[u / SPB] & kIdMask, BLK) - (u % SPB) * CK, 0), CK) : CK;
   };
   int t = 0;
   // chunk u sits in stage u & 1, passed as `stage`
@@ -576,7 +643,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
         st16(vz + (kv + e / C::CPR) * C::RB + 16 * (e % C::CPR), u32x4{0u, 0u, 0u, 0u});
       __syncthreads();
     }
-    chunk<C, false>(st, qf, stage, off, c2, hh, bits, 0, kv);
+    // pairs: only the waves of a query block that routes this block compute it
+    const bool mine = QB == 1 || (alive && (((int)s_list[u / SPB] >> (12 + qb)) & 1));
+    if (mine) chunk<C, false>(st, qf, stage, off, c2, hh, bits[qb], 0, kv);
   };
   // stage 1, two exact chunks per trip (t even), so each stage's offset is a
   // constant that folds into the LDS reads' immediate offsets
@@ -594,7 +663,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
     if (t + 1 < ntot) issue(t + 1);
     const int jbase = (int)s_clist[t - nex] * CK;
     const int jp = (VL && jrag >= jbase && jrag < jbase + CK) ? jrag - jbase : -1;
-    chunk<C, true>(st, qf, lds + (t & 1) * C::STB, off, c2, hh, bits, jbase, CK, jp, wmiss);
+    if (alive) chunk<C, true>(st, qf, lds + (t & 1) * C::STB, off, c2, hh, bits[qb], jbase, CK, jp, wmiss);
   }
   if (FO) {
     for (; t < ntot; ++t) {                 // per-block first order: H_j^T parts
@@ -618,7 +687,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
         stage_centroids<C>(cen, vs, j0, nb, lds, tid);
         __syncthreads();
         const int jp = (VL && jrag >= j0 && jrag < j0 + CK) ? jrag - j0 : -1;
-        chunk<C, true>(st, qf, lds, off, c2, hh, bits, j0, CK, jp, wmiss);
+        if (alive) chunk<C, true>(st, qf, lds, off, c2, hh, bits[qb], j0, CK, jp, wmiss);
       }
     }
   }
@@ -634,7 +703,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
         wait_vm0();
         __syncthreads();
         if (t + 1 < ntot) issue(t + 1);
-        hbar_part<C, 0>(st, qf, lds + (t & 1) * C::STB, off, f);
+        if (alive) hbar_part<C, 0>(st, qf, lds + (t & 1) * C::STB, off, f);
         ++t;
       }
       if constexpr (C::HP > 1) {
@@ -642,7 +711,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
           wait_vm0();
           __syncthreads();
           if (t + 1 < ntot) issue(t + 1);
-          hbar_part<C, 1>(st, qf, lds + (t & 1) * C::STB, off, f);
+          if (alive) hbar_part<C, 1>(st, qf, lds + (t & 1) * C::STB, off, f);
           ++t;
         }
       }
@@ -664,8 +733,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   // ---- epilogue: o = N / D (0 when nothing was attended in keep-or-drop)
   const float ltot = row_sum(st.l);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  const bool live = !VL || 32 * w + q32 < ni;            // padding query rows are written 0
-  bf16* orow = p.O + ((size_t)bh * L + (size_t)i * BLK + 32 * w + q32) * D;
+  if (!qvalid) return;                                  // (odd nb: no second query block)
+  const bool live = 32 * wq + q32 < ni;                 // padding query rows are written 0
+  bf16* orow = p.O + ((size_t)bh * L + (size_t)i * BLK + 32 * wq + q32) * D;
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
@@ -679,30 +749,39 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
 
 template <class C>
 hipError_t launch_t(const AttnArgs& a) {
-  const int grid = a.bh * a.nb;
+  const int grid = a.bh * ((a.nb + C::QB - 1) / C::QB);
   const int nbp = (a.nb + C::BLK - 1) / C::BLK * C::BLK;
   const bf16* pk = static_cast<const bf16*>(a.packed);
   AttnPtrs p{(const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.idx, a.centroid, a.vsum,
              a.hbar, pk, pk ? pk + (size_t)a.bh * nbp * C::D : nullptr,
              pk ? pk + (size_t)2 * a.bh * nbp * C::D : nullptr, (const bf16*)a.ht, (bf16*)a.O};
   const bool fo = a.approx && a.order == kOrderFirst;
-  auto kern = a.lens ? (fo ? attn_bf16_kernel<C, true, true> : attn_bf16_kernel<C, true, false>)
-                     : (fo ? attn_bf16_kernel<C, false, true> : attn_bf16_kernel<C, false, false>);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax, a.approx, a.order,
-                     a.scale, a.nb, a.lens, a.heads);
+  if constexpr (C::QB == 1) {
+    auto kern = a.lens ? (fo ? attn_bf16_kernel<C, true, true> : attn_bf16_kernel<C, true, false>)
+                       : (fo ? attn_bf16_kernel<C, false, true> : attn_bf16_kernel<C, false, false>);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax, a.approx, a.order,
+                       a.scale, a.nb, a.lens, a.heads);
+  } else {
+    if (fo) return hipErrorInvalidValue;        // the launcher sends this order to QB = 1
+    auto kern = a.lens ? attn_bf16_kernel<C, true, false> : attn_bf16_kernel<C, false, false>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax, a.approx, a.order,
+                       a.scale, a.nb, a.lens, a.heads);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a) {
-  if (a.D == 128 && a.BLK == 64) return launch_t<Cfg<128, 64, 32>>(a);
+  // 64-token blocks: query blocks in pairs, except for the per-block first order
+  const bool fo = a.approx && a.order == kOrderFirst;
+  if (a.D == 128 && a.BLK == 64) return fo ? launch_t<Cfg<128, 64, 32>>(a) : launch_t<Cfg<128, 64, 32, 2>>(a);
   if (a.D == 128 && a.BLK == 128) {
     // the per-block first order streams whole 128-row H_j^T matrices: 64-key chunks
-    if (a.approx && a.order == kOrderFirst) return launch_t<Cfg<128, 128, 64>>(a);
+    if (fo) return launch_t<Cfg<128, 128, 64>>(a);
     return launch_t<Cfg<128, 128, 32>>(a);
   }
-  if (a.D == 64 && a.BLK == 64) return launch_t<Cfg<64, 64, 32>>(a);
+  if (a.D == 64 && a.BLK == 64) return fo ? launch_t<Cfg<64, 64, 32>>(a) : launch_t<Cfg<64, 64, 32, 2>>(a);
   if (a.D == 64 && a.BLK == 128) return launch_t<Cfg<64, 128, 64>>(a);
   return hipErrorInvalidValue;
 }

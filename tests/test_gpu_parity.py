@@ -242,6 +242,8 @@ VL_MODES = {"approx": oracle.MODE_APPROX, "drop": oracle.MODE_DROP, **ORDER_MODE
     ("bf16", 128, 128, 1024, 3, [1024, 700, 130]),
     ("bf16", 64, 64, 1024, 4, [999, 64, 1]),
     ("bf16", 64, 128, 1024, 2, [1024, 129, 0]),          # an empty sequence
+    ("bf16", 128, 64, 1024, 4, [320, 1024, 577]),        # a live and an empty block share a pair
+    ("bf16", 64, 64, 1344, 3, [1344, 700, 64]),          # odd block count
     ("fp32", 128, 64, 512, 3, [512, 300, 65]),
     ("fp32", 64, 128, 512, 2, [257, 128, 5]),
 ])
@@ -413,6 +415,37 @@ def test_padding_empty_rows_and_out_of_range_ids(torch):
                                code, 1 / math.sqrt(d), B, H=ref_st["H"])
         check_attention(outs[m], ref, "bf16", f"padding/{m}")
     assert np.all(outs["drop"][0, 0, B:2 * B] == 0.0)
+
+
+@pytest.mark.parametrize("d,L,k", [(128, 64 * 21, 6), (64, 64 * 21, 5), (128, 64 * 40, 9)])
+def test_query_block_pairs_with_unrelated_rows(torch, d, L, k):
+    """With 64-token blocks two neighbouring query blocks share a workgroup and
+    stream the union of their routed blocks; here every row routes its own
+    random set (with -1 padding in some rows and one empty row), so most
+    blocks of the union belong to one query block only.  Odd block counts leave
+    the last pair with a single query block."""
+    pisa = pisa_mod()
+    B, h = 64, 2
+    nb = L // B
+    Q, K, V = (_rand(torch, (1, h, L, d), "bf16", s) for s in (41, 42, 43))
+    g = np.random.default_rng(nb * 1000 + k)
+    rows = np.full((1, h, nb, k), -1, dtype=np.int32)
+    for hh in range(h):
+        for i in range(nb):
+            n = 0 if (hh, i) == (1, 3) else (k if i % 5 else k - 2)
+            rows[0, hh, i, :n] = np.sort(g.choice(nb, size=n, replace=False))
+    idx = torch.from_numpy(rows).cuda()
+    st = pisa.precompute(Kd := to_dev(K, "bf16"), Vd := to_dev(V, "bf16"), B, store_Ht=True)
+    Qd = to_dev(Q, "bf16")
+    modes = {"approx": oracle.MODE_APPROX, "drop": oracle.MODE_DROP, **ORDER_MODES}
+    outs = {m: to_np(pisa.attention(Qd, Kd, Vd, idx, st, B, mode=m)) for m in modes}
+    torch.cuda.synchronize()
+    ref_st = oracle.precompute(K, V, B)
+    for m, code in modes.items():
+        ref = oracle.attention(Q, K, V, rows, ref_st["centroid"], ref_st["vsum"], ref_st["Hbar"],
+                               code, 1 / math.sqrt(d), B, H=ref_st["H"])
+        check_attention(outs[m], ref, "bf16", f"pairs/{m}")
+    assert np.all(outs["drop"][0, 1, 3 * B:4 * B] == 0.0)
 
 
 def test_runs_are_bitwise_reproducible(torch):
