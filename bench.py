@@ -90,7 +90,12 @@ def profiled_traffic(workload_name):
 
 
 def timed_phases(pisa, torch, Qd, Kd, Vd, w, k, steps, warmup, mode="approx"):
-    """Run `steps` full steps; return total wall ms and per-phase event ms."""
+    """Run `steps` full steps back to back with nothing recorded between them
+    (host clock around the loop, synchronized on both sides: the headline),
+    then the same number again with one HIP event pair per step (latency
+    percentiles) and again with an event between the calls (phase split; each
+    event costs the GPU some microseconds, so these passes run apart from the
+    headline).  Returns total wall ms and the per-phase event ms."""
     stream = torch.cuda.current_stream()
     ws = torch.empty(pisa.workspace_size(Kd, w.block), dtype=torch.uint8, device="cuda")
 
@@ -111,19 +116,30 @@ def timed_phases(pisa, torch, Qd, Kd, Vd, w, k, steps, warmup, mode="approx"):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     t0 = time.perf_counter()
+    for _ in range(steps):
+        st, idx, out = step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    # per-step latency: one event pair per step
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    for a, b in pairs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_step = [a.elapsed_time(b) for a, b in pairs]
+    # phase split: an event between the calls
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(steps):
         st, idx, out = step(evs[i])
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
     ph = {"precompute": 0.0, "route": 0.0, "attention": 0.0}
-    per_step = []
     for e in evs:
         ph["precompute"] += e[0].elapsed_time(e[1])
         ph["route"] += e[1].elapsed_time(e[2])
         ph["attention"] += e[2].elapsed_time(e[3])
-        per_step.append(e[0].elapsed_time(e[3]))
     ph = {n: v / steps for n, v in ph.items()}
     ph["step_event_ms"] = percentiles(per_step)
     return wall_ms, ph, (st, idx, out)
@@ -422,7 +438,7 @@ def main():
         line["roofline"]["attainable"] = att
     if not args.no_secondary:
         other = 3 if args.workload == 4 else 4
-        _, res2 = run(other, max(5, args.steps // 2), 2, False, cold=not args.no_cold)
+        _, res2 = run(other, args.steps, max(3, args.warmup), False, cold=not args.no_cold)
         line["secondary"] = {wl.WORKLOADS[other].name: res2}
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
