@@ -283,6 +283,55 @@ def test_varlen_pipeline_parity(torch, dtype, d, B, L, k, lens):
             assert np.all(got[bi, :, n:] == 0.0), f"varlen/{m}: padding rows of entry {bi}"
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_random_small_configurations(torch, seed):
+    """Seeded random small problems across the supported space: element type,
+    head dim, block size, 1 to 24 blocks (one block, odd counts: query-block
+    pairs with a missing second block), batch and heads, k, and with half the
+    seeds variable lengths including empty and one-token sequences; the whole
+    pipeline and every attention mode against the oracle."""
+    pisa = pisa_mod()
+    g = np.random.default_rng(7000 + seed)
+    dtype = "fp32" if seed % 4 == 3 else "bf16"
+    d, B = int(g.choice([64, 128])), int(g.choice([64, 128]))
+    nb, b, h = int(g.integers(1, 25)), int(g.integers(1, 3)), int(g.integers(1, 4))
+    k = int(g.integers(1, nb + 1))
+    L = nb * B
+    lens = None
+    if seed % 2 == 1:
+        lens = [int(x) for x in g.choice([0, 1, L, int(g.integers(1, L + 1))], size=b)]
+    Q, K, V = (_rand(torch, (b, h, L, d), dtype, 100 * seed + s) for s in (1, 2, 3))
+    K = K + np.repeat(_rand(torch, (b, h, nb, d), "fp32", 100 * seed + 4) * 0.5, B, axis=2)
+    if dtype == "bf16":
+        K = wl.round_bf16(K)
+    Qn, Kn, Vn = Q.copy(), K.copy(), V.copy()
+    if lens is not None:
+        for bi, n in enumerate(lens):
+            for X in (Qn, Kn, Vn):
+                X[bi, :, n:] = np.nan
+    Qd, Kd, Vd = (to_dev(x, dtype) for x in (Qn, Kn, Vn))
+    sl = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+    st = pisa.precompute(Kd, Vd, B, store_H=True, store_Ht=dtype == "bf16", seq_lens=sl)
+    idx = pisa.route(Qd, st, k, 0.05, B, seq_lens=sl)
+    outs = {m: pisa.attention(Qd, Kd, Vd, idx, st, B, mode=m, seq_lens=sl) for m in VL_MODES}
+    torch.cuda.synchronize()
+    name = f"random{seed}({dtype}, d={d}, B={B}, nb={nb}, b={b}, h={h}, k={k}, lens={lens})"
+    ref_st = oracle.precompute(K, V, B, seq_lens=lens)
+    check_stats(st, ref_st, name=name)
+    scale = 1 / math.sqrt(d)
+    scores = oracle.route_scores(Q, to_np(st["centroid"]), to_np(st["M"]), 0.05, B, scale,
+                                 seq_lens=lens)
+    check_route(idx.cpu().numpy(), scores, k, name=name)
+    for m, code in VL_MODES.items():
+        ref = oracle.attention(Q, K, V, idx.cpu().numpy(), ref_st["centroid"], ref_st["vsum"],
+                               ref_st["Hbar"], code, scale, B, H=ref_st["H"], seq_lens=lens)
+        got = to_np(outs[m])
+        check_attention(got, ref, dtype, name=f"{name}/{m}")
+        if lens is not None:
+            for bi, n in enumerate(lens):
+                assert np.all(got[bi, :, n:] == 0.0), f"{name}/{m}: padding rows of entry {bi}"
+
+
 def test_varlen_full_lengths_match_the_plain_call(torch):
     """Lengths equal to the buffer length reproduce the call without lengths."""
     pisa = pisa_mod()
