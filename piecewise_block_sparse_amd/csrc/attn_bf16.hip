@@ -443,7 +443,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int ngrp = (nb + QB - 1) / QB;                 // workgroups per (batch, head)
   const int bh = logical / ngrp, i0 = (logical - bh * ngrp) * QB;
-  const int qb = w / C::WPQ, wq = w - qb * C::WPQ;     // this wave: query block i0 + qb, rows 32 wq ..
+  // this wave: query block i0 + qb, rows 32 wq .. (qb as a scalar, so that
+  // branches on the wave's query block are uniform)
+  const int qb = __builtin_amdgcn_readfirstlane(w / C::WPQ), wq = w - qb * C::WPQ;
   const int i = i0 + qb;
   const bool qvalid = i < nb;                          // (odd nb: the last pair has one block)
   const size_t L = (size_t)nb * BLK;
@@ -644,7 +646,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       __syncthreads();
     }
     // pairs: only the waves of a query block that routes this block compute it
-    const bool mine = QB == 1 || (alive && (((int)s_list[u / SPB] >> (12 + qb)) & 1));
+    const bool mine =
+        QB == 1 || (alive && ((__builtin_amdgcn_readfirstlane((int)s_list[u / SPB]) >> (12 + qb)) & 1));
     if (mine) chunk<C, false>(st, qf, stage, off, c2, hh, bits[qb], 0, kv);
   };
   // stage 1, two exact chunks per trip (t even), so each stage's offset is a
