@@ -16,7 +16,9 @@ p90 of the timed steps (HIP events) and `cold_step_ms` the same for steps run
 after a 512 MB scratch write (caches flushed); `density_sweep` re-routes the same
 inputs at top-k 128 / 64 / 32 / 16 of 256 blocks and times both modes; `orders`
 times the zeroth-order and the per-block first-order treatments of the
-unselected blocks on the same inputs; `roofline.attainable` is the MFMA rate
+unselected blocks on the same inputs; `route_attention_fused` times the
+single-launch routing-and-attention call against the two calls it replaces;
+`roofline.attainable` is the MFMA rate
 the chip sustains for the exact phase's per-chunk instruction mix on random
 operands, and its streaming HBM read rate (libpisa_probe), beside the published
 peaks; `cpu_baseline` is the
@@ -79,7 +81,7 @@ def profiled_traffic(workload_name):
         return None
     # the stamp covers every source the attention kernel is compiled from
     stamp = hashlib.sha256()
-    for f in ("attn_bf16.hip", "lds_stream.hpp", "common.hpp"):
+    for f in ("attn_bf16.hip", "lds_stream.hpp", "common.hpp", "topk.hpp"):
         stamp.update(open(os.path.join(ROOT, "piecewise_block_sparse_amd", "csrc", f), "rb").read())
     m = re.search(r"attn_bf16_kernel traffic_bytes_per_launch=(\d+) read=(\d+) write=(\d+) "
                   r"avg_ns=(\d+) source=([0-9a-f]+)", open(path).read())
@@ -181,6 +183,20 @@ def time_attention(pisa, torch, Qd, Kd, Vd, idx, st, w, mode, reps):
     a.record(stream)
     for _ in range(reps):
         pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode=mode)
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def time_route_attention(pisa, torch, Qd, Kd, Vd, st, w, reps):
+    """The in-kernel routing call (route and attention in one launch), event-timed."""
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        pisa.route_attention(Qd, Kd, Vd, st, w.k, w.lam, w.block, mode="approx")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        pisa.route_attention(Qd, Kd, Vd, st, w.k, w.lam, w.block, mode="approx")
     b.record(stream)
     b.synchronize()
     return a.elapsed_time(b) / reps
@@ -331,6 +347,10 @@ def main():
             res["exact_phase_ms"] = t_drop
             res["approx_phase_ms"] = ph["attention"] - t_drop
             res["tflops"]["exact_phase"] = f["exact"] / t_drop / 1e9
+            t_fused = time_route_attention(pisa, torch, Qd, Kd, Vd, st, w, max(5, steps // 2))
+            res["route_attention_fused"] = {
+                "ms": t_fused, "route_plus_attention_ms": ph["route"] + ph["attention"],
+                "step_ms_with_fused": ph["precompute"] + t_fused}
         res["gbs"] = {"precompute": by["stats"] / ph["precompute"] / 1e6,
                       "route": by["route"] / ph["route"] / 1e6}
         res["gflop"] = {n: v / 1e9 for n, v in f.items()}

@@ -223,6 +223,36 @@ pisa_status pisa_attention(const pisa_shape* shape, const void* Q, const void* K
                            const pisa_stats* stats, int32_t mode, float scale, void* O,
                            void* stream);
 
+/*
+ * pisa_route_attention -- routing and attention in one kernel (PISA summary,
+ * section 2, "Covariance-aware routing" for the selection and "Hardware
+ * implementation" for the stages).  Each workgroup routes its own query
+ * block(s) exactly as pisa_route does (same fp64 pooled query, scores and
+ * top-k, so the selection is identical bit for bit) and then runs the
+ * attention of pisa_attention on that selection; no idx round trip through
+ * memory and no separate routing launch.
+ *
+ *   Q, K, V   [b,h,L,d] bf16 (device)
+ *   stats     centroid and M (routing), plus what pisa_attention reads in `mode`
+ *   k         blocks per query block, 1 <= k <= nb
+ *   lambda    weight of M_j, finite
+ *   mode      PISA_MODE_APPROX, PISA_MODE_DROP or PISA_MODE_ZEROTH
+ *   scale     the routing score uses it as given (float64); the attention uses
+ *             (float)scale, as pisa_attention with that value
+ *   idx       NULLABLE out: int32 [b,h,nb,k], the selection, as pisa_route
+ *             writes it (ascending, -1 after fewer than k candidates)
+ *   O         out: [b,h,L,d] bf16 (device)
+ *
+ * Errors as pisa_route and pisa_attention, and: PISA_ERR_DTYPE for fp32
+ * inputs, PISA_ERR_ARG for PISA_MODE_FIRST, PISA_ERR_SHAPE for nb above what
+ * the kernel's LDS holds for the score rows (d = 128: nb <= 2048 with
+ * 128-token blocks, nb <= 1792 with 64-token blocks; d = 64: nb <= 2048 and
+ * 832); the caller then uses pisa_route and pisa_attention.
+ */
+pisa_status pisa_route_attention(const pisa_shape* shape, const void* Q, const void* K,
+                                 const void* V, const pisa_stats* stats, int32_t k, double lambda,
+                                 int32_t mode, double scale, int32_t* idx, void* O, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

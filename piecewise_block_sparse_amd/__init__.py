@@ -25,7 +25,7 @@ import math
 
 from . import _lib
 
-__all__ = ["precompute", "route", "attention", "workspace_size", "version", "MODE_APPROX",
+__all__ = ["precompute", "route", "attention", "route_attention", "workspace_size", "version", "MODE_APPROX",
            "MODE_DROP", "MODE_ZEROTH", "MODE_FIRST"]
 
 MODE_APPROX = _lib.MODE_APPROX
@@ -196,3 +196,39 @@ def attention(Q, K, V, idx, stats: dict | None, block: int, mode: int | str = "a
         ctypes.byref(shp), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), int(idx.shape[-1]),
         ctypes.byref(st) if st is not None else None, int(mode), scale, _ptr(O), _stream(Q)))
     return O
+
+
+def route_attention(Q, K, V, stats: dict, k: int, lam: float, block: int,
+                    mode: int | str = "approx", scale: float | None = None, out=None,
+                    seq_lens=None, return_idx: bool = False):
+    """Routing and attention in one kernel (bf16): the selection of route()
+    (bit for bit) followed by attention() on it, without the idx round trip.
+    Modes "approx", "zeroth" and "drop".  With return_idx, returns (O, idx)."""
+    torch = _torch()
+    lib = _lib.load()
+    _same(Q, K, V)
+    if isinstance(mode, str):
+        mode = _MODES[mode]
+    shp = _shape(Q, block, seq_lens)
+    b, h, L, d = Q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nb = L // block if L % block == 0 else 0
+    _expect(stats["centroid"], (b, h, nb, d), torch.float32, "stats['centroid']")
+    _expect(stats["M"], (b, h, nb), torch.float32, "stats['M']")
+    if mode != MODE_DROP:
+        _expect(stats["vsum"], (b, h, nb, d), torch.float32, "stats['vsum']")
+    if mode == MODE_APPROX:
+        _expect(stats["Hbar"], (b, h, d, d), torch.float32, "stats['Hbar']")
+    pk = stats.get("packed")
+    if pk is not None and pk.numel() != lib.pisa_packed_size(ctypes.byref(shp)):
+        raise ValueError("stats['packed'] does not match this shape")
+    idx = (torch.empty((b, h, nb, max(k, 0)), dtype=torch.int32, device=Q.device)
+           if return_idx else None)
+    O = torch.empty_like(Q) if out is None else out
+    _same(Q, O)
+    st = _lib.PisaStats(_ptr(stats["centroid"]), _ptr(stats.get("vsum")), None,
+                        _ptr(stats.get("Hbar")), _ptr(stats["M"]), _ptr(pk), None)
+    _lib.check("pisa_route_attention", lib.pisa_route_attention(
+        ctypes.byref(shp), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(st), int(k), float(lam),
+        int(mode), scale, _ptr(idx), _ptr(O), _stream(Q)))
+    return (O, idx) if return_idx else O

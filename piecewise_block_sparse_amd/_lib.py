@@ -25,7 +25,7 @@ NORM_SPECTRAL = 1
 
 # every symbol the header declares
 EXPORTS = ("pisa_version", "pisa_status_string", "pisa_last_error", "pisa_workspace_size",
-           "pisa_packed_size", "pisa_precompute", "pisa_route", "pisa_attention")
+           "pisa_packed_size", "pisa_precompute", "pisa_route", "pisa_attention", "pisa_route_attention")
 # ... and every symbol include/pisa_probe.h declares (libpisa_probe.so)
 PROBE_EXPORTS = ("pisa_probe_chunk_rate", "pisa_probe_read_rate")
 
@@ -77,6 +77,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_route.argtypes = [sp, vp, vp, vp, i32, ctypes.c_double, ctypes.c_double, vp, vp]
     lib.pisa_attention.restype = i32
     lib.pisa_attention.argtypes = [sp, vp, vp, vp, vp, i32, stp, i32, ctypes.c_float, vp, vp]
+    lib.pisa_route_attention.restype = i32
+    lib.pisa_route_attention.argtypes = [sp, vp, vp, vp, stp, i32, ctypes.c_double, i32,
+                                         ctypes.c_double, vp, vp, vp]
     _lib = lib
     return lib
 

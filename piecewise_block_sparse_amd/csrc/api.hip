@@ -172,4 +172,42 @@ pisa_status pisa_attention(const pisa_shape* shape, const void* Q, const void* K
   return hip_status(bf ? pisa::launch_attn_bf16(a) : pisa::launch_attn_f32(a), "pisa_attention");
 }
 
+pisa_status pisa_route_attention(const pisa_shape* shape, const void* Q, const void* K,
+                                 const void* V, const pisa_stats* stats, int32_t k, double lambda,
+                                 int32_t mode, double scale, int32_t* idx, void* O, void* stream) {
+  g_err[0] = 0;
+  int bh = 0, nb = 0;
+  pisa_status st = check_shape(shape, &bh, &nb);
+  if (st != PISA_OK) return st;
+  if (!Q || !K || !V || !O || !stats || !stats->centroid || !stats->M)
+    return fail(PISA_ERR_NULL, "Q, K, V, O and stats centroid and M are required");
+  if (shape->dtype != PISA_DTYPE_BF16)
+    return fail(PISA_ERR_DTYPE, "in-kernel routing is built for bf16 inputs");
+  if (mode == PISA_MODE_FIRST)
+    return fail(PISA_ERR_ARG, "FIRST mode: use pisa_route, then pisa_attention");
+  if (mode != PISA_MODE_APPROX && mode != PISA_MODE_DROP && mode != PISA_MODE_ZEROTH)
+    return fail(PISA_ERR_ARG, "unknown mode %d", mode);
+  if (k < 1 || k > nb) return fail(PISA_ERR_ARG, "k=%d outside [1, %d]", k, nb);
+  if (!std::isfinite(scale) || !(scale > 0.0) || !((float)scale > 0.f) || !std::isfinite((float)scale))
+    return fail(PISA_ERR_ARG, "scale must be finite and positive");
+  if (!std::isfinite(lambda)) return fail(PISA_ERR_ARG, "lambda must be finite");
+  const int maxnb = pisa::fused_route_max_blocks(shape->head_dim, shape->block);
+  if (nb > maxnb)
+    return fail(PISA_ERR_SHAPE, "nb=%d above %d for in-kernel routing at d=%d, block=%d: "
+                "use pisa_route, then pisa_attention", nb, maxnb, shape->head_dim, shape->block);
+  const bool approx = mode != PISA_MODE_DROP;
+  if (approx && !stats->vsum) return fail(PISA_ERR_NULL, "modes other than DROP need stats vsum");
+  if (mode == PISA_MODE_APPROX && !stats->Hbar)
+    return fail(PISA_ERR_NULL, "APPROX mode needs stats Hbar");
+  const int order = mode == PISA_MODE_ZEROTH ? pisa::kOrderZeroth : pisa::kOrderMixed;
+  pisa::AttnArgs a{Q, K, V, nullptr, k,
+                   stats->centroid, approx ? stats->vsum : nullptr,
+                   mode == PISA_MODE_APPROX ? stats->Hbar : nullptr,
+                   approx ? stats->packed : nullptr, nullptr, nullptr,
+                   approx ? 1 : 0, order, (float)scale, O, bh, nb, shape->head_dim, shape->block,
+                   shape->seq_lens, shape->heads, (hipStream_t)stream,
+                   stats->M, k, scale, lambda, idx};
+  return hip_status(pisa::launch_attn_bf16(a), "pisa_route_attention");
+}
+
 }  // extern "C"

@@ -34,6 +34,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_stream.hpp"
+#include "topk.hpp"
 
 namespace pisa {
 namespace {
@@ -411,25 +412,53 @@ struct AttnPtrs {
   const bf16* pk_hbart;
   const bf16* ht;        // H_j^T per block, bf16 [bh][nb][D][D] (per-block first order)
   bf16* O;
+  const float* M;        // in-kernel routing: M_j [bh][nb]
+  int32_t* idx_out;      // in-kernel routing: the selection written out (nullable)
+};
+
+// In-kernel routing (workgroup-local copy of the route kernel's selection):
+// rk blocks per query block, score = rscale * qbar . kbar_j + rlam * M_j in fp64.
+struct RouteIn {
+  int rk;
+  double rscale;
+  double rlam;
 };
 
 constexpr int kBitWords = (kMaxBlocks + 128) / 32;
 constexpr int kIdMask = 0xfff;                  // block id bits of a list entry (ids < 4096)
 static_assert(kMaxBlocks <= kIdMask + 1, "block ids fit below the pair flags");
 
+// The lane's query row (32 wq + q32 of block qblk) as MFMA B-operand fragments;
+// padding queries (row >= ni) are zero rows.
+template <class C, bool VL>
+__device__ __forceinline__ void load_q_frags(bf16x8 (&qf)[C::KS], const bf16* Q, int bh, size_t L,
+                                             int qblk, int wq, int q32, int hh, int ni) {
+  const bf16* qrow = Q + ((size_t)bh * L + (size_t)qblk * C::BLK + 32 * wq + q32) * C::D + 8 * hh;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_bf16x8(ld16(qrow + 16 * ks));
+  if ((VL || C::QB == 2) && 32 * wq + q32 >= ni)
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+}
+
 // VL: sequences have valid lengths (lens); without, the length code compiles away.
 // FO: the per-block first order (its stage lives only in these instantiations,
 // so the other modes keep their register budget).
-template <class C, bool VL, bool FO>
+// FR: the workgroup routes its own query blocks (pooled query, fp64 scores
+// against every centroid, top-k) instead of reading idx; the selection is the
+// route kernel's, bit for bit.
+template <class C, bool VL, bool FO, bool FR = false>
 __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, int kmax, int approx,
                                                              int order, float scale, int nb,
-                                                             const int32_t* lens, int heads) {
+                                                             const int32_t* lens, int heads,
+                                                             RouteIn ri) {
   constexpr int D = C::D, BLK = C::BLK, CK = C::CK;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDSB];
   constexpr int QB = C::QB;
   static_assert(QB == 1 || !FO, "the per-block first order runs one query block per workgroup");
   __shared__ unsigned bits[QB][kBitWords];
-  __shared__ unsigned exb[QB == 2 ? 2 : 1][QB == 2 ? kBitWords : 1];   // pairs: exact blocks
+  static_assert(!(FR && FO), "in-kernel routing runs with the other orders");
+  __shared__ unsigned exb[QB == 2 ? 2 : 1][(QB == 2 || FR) ? kBitWords : 1];   // exact blocks
   __shared__ short s_list[kMaxBlocks];                 // exact block ids of S_i, in order;
                                                        // then (per-block first order) U_i.
                                                        // Pairs: the union, ascending, with
@@ -468,13 +497,118 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       if (i0 + q >= nb) break;
       bf16* ob = p.O + ((size_t)bh * L + (size_t)(i0 + q) * BLK) * D;
       for (int e = tid; e < BLK * D / 8; e += C::NT) st16(ob + 8 * e, u32x4{0u, 0u, 0u, 0u});
+      if (FR && p.idx_out)
+        for (int e = tid; e < ri.rk; e += C::NT) p.idx_out[((size_t)bh * nb + i0 + q) * ri.rk + e] = -1;
     }
     return;
   }
   const bool alive = ni > 0;                           // wave-uniform
   const bool first = FO && approx && order == kOrderFirst && packed && p.ht != nullptr;
 
-  if (approx || QB == 2) {
+  if constexpr (FR) {
+    // ---- in-kernel routing.  LDS (the ring, idle until the chunk stream
+    // starts): qbar [QB][D] f64 | pooling partials [QB][WPQ][D] f64, then the
+    // scores [QB][ncol] f64 in their place | at the end, the select
+    // histograms [QB][256] u32 (the launcher checks that the scores fit).
+    double* s_qbar = reinterpret_cast<double*>(lds);
+    double* s_part = s_qbar + QB * D;
+    double* s_sc = s_qbar + QB * D;
+    unsigned* s_hist = reinterpret_cast<unsigned*>(lds + C::LDSB) - QB * 256;
+    const int ncol = (nb + 63) / 64 * 64;
+    for (int e = tid; e < kBitWords; e += C::NT) {
+      const int lo = 32 * e;
+      unsigned pad = 0u;                                 // padding and empty blocks: j >= nne
+      if (lo + 32 > nne) pad = (lo >= nne) ? ~0u : (~0u << (nne - lo));
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        bits[q][e] = pad;
+        exb[q][e] = 0u;
+      }
+    }
+    // pooled query of block i: exact fp64 sums of its ni valid queries.  The
+    // query rows, already in registers as MFMA fragments (padding queries are
+    // zero rows), are staged row-major in the ring; the waves of each query
+    // block then sum its columns with 16-byte LDS reads and times 1 / ni below.
+    {
+      bf16x8 qt[C::KS];                                  // (loaded again from L2 below)
+      load_q_frags<C, VL>(qt, p.Q, bh, L, qvalid ? i : i0, wq, q32, hh, ni);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        st16(lds + (size_t)(qb * BLK + 32 * wq + q32) * C::RB + 32 * ks + 16 * hh,
+             __builtin_bit_cast(u32x4, qt[ks]));
+    }
+    __syncthreads();
+    {
+      constexpr int CPR = D / 8, TPQ = 64 * C::WPQ, RPI = TPQ / CPR, NR = BLK / RPI;
+      const int tq = tid - qb * TPQ, c = tq % CPR, rs = tq / CPR;
+      double x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int n = 0; n < NR; ++n) {
+        const bf16x8 v = as_bf16x8(ld16(lds + (size_t)(qb * BLK + rs + n * RPI) * C::RB + 16 * c));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] += (double)(float)v[e];
+      }
+#pragma unroll
+      for (int o = CPR; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] += __shfl_xor(x[e], o);
+      __syncthreads();                                   // staged rows read before the partials
+      if (lane < CPR)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_part[(qb * C::WPQ + wq) * D + 8 * c + e] = x[e];
+    }
+    __syncthreads();
+    for (int e = tid; e < QB * D; e += C::NT) {
+      const int q = e / D;
+      double sum = 0.0;
+#pragma unroll
+      for (int u = 0; u < C::WPQ; ++u) sum += s_part[(q * C::WPQ + u) * D + (e - q * D)];
+      const int nq = (i0 + q < nb) ? (VL ? block_count(Lv, i0 + q, BLK) : BLK) : 0;
+      s_qbar[e] = sum * ((nq == BLK) ? 1.0 / BLK : 1.0 / (double)(nq > 0 ? nq : 1));
+    }
+    __syncthreads();
+    // scores of the candidates j < nne against the QB pooled queries: fp64
+    // FMAs over d in order, then scale * dot + lambda * M_j as one FMA (the
+    // route kernel's arithmetic)
+    {
+      const float* cen = p.centroid + (size_t)bh * nb * D;
+      const float* Mh = p.M + (size_t)bh * nb;
+      for (int j = tid; j < nne; j += C::NT) {
+        const float* cj = cen + (size_t)j * D;
+        double acc[QB];
+#pragma unroll
+        for (int q = 0; q < QB; ++q) acc[q] = 0.0;
+#pragma unroll 4
+        for (int a = 0; a < D; a += 4) {
+          const f32x4 kv = *reinterpret_cast<const f32x4*>(cj + a);
+#pragma unroll
+          for (int q = 0; q < QB; ++q) {
+            const double* qq = s_qbar + q * D + a;
+            acc[q] = fma(qq[0], (double)kv[0], acc[q]);
+            acc[q] = fma(qq[1], (double)kv[1], acc[q]);
+            acc[q] = fma(qq[2], (double)kv[2], acc[q]);
+            acc[q] = fma(qq[3], (double)kv[3], acc[q]);
+          }
+        }
+        const double mj = ri.rlam * (double)Mh[j];
+#pragma unroll
+        for (int q = 0; q < QB; ++q) s_sc[q * ncol + j] = fma(ri.rscale, acc[q], mj);
+      }
+    }
+    __syncthreads();
+    // top-k of each query block by its first wave; the ids go out when asked
+    if (wq == 0 && qvalid) {
+      const int kk = (ni > 0) ? min(ri.rk, nne) : 0;
+      select_top_k(s_sc + qb * ncol, s_hist + qb * 256, exb[qb], ncol / 64, nne, kk, lane);
+      if (p.idx_out) write_ids_ascending(exb[qb], ncol / 32, kk, ri.rk, p.idx_out + ((size_t)bh * nb + i) * ri.rk, lane);
+    }
+    __syncthreads();
+    for (int e = tid; e < nbp / 32; e += C::NT)
+#pragma unroll
+      for (int q = 0; q < QB; ++q) bits[q][e] |= exb[q][e];
+    __syncthreads();
+  }
+  if (!FR && (approx || QB == 2)) {
     // bits[q]: bit j set when block j is exact for query block i0 + q (in its
     // S_i) or padding (j >= nne); exb[q] (pairs): the exact blocks alone
     for (int e = tid; e < nbp / 32; e += C::NT) {
@@ -505,14 +639,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
 
   // this lane's query row as 16-byte B-operand fragments (d = 16 ks + 8 hh + 0..7)
   bf16x8 qf[C::KS];
-  {
-    const bf16* qrow = p.Q + ((size_t)bh * L + (size_t)(qvalid ? i : i0) * BLK + 32 * wq + q32) * D + 8 * hh;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_bf16x8(ld16(qrow + 16 * ks));
-    if ((VL || QB == 2) && 32 * wq + q32 >= ni)          // padding query: a zero row
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) qf[ks] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-  }
+  load_q_frags<C, VL>(qf, p.Q, bh, L, qvalid ? i : i0, wq, q32, hh, ni);
   const Offsets<C> off = make_offsets<C>(lane);
   const DmaOff<C> loff = dma_lane_offsets<C>(w, lane);
   RowState<D> st;
@@ -530,7 +657,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   const int nctile = packed ? nbp / CK : 0;
   if (w == 0) {
     int cnt = 0;
-    if constexpr (QB == 1) {
+    if constexpr (QB == 1 && !FR) {
       const int32_t* row = p.idx + ((size_t)bh * nb + i) * kmax;
       for (int e0 = 0; e0 < kmax; e0 += 64) {
         const int e = e0 + lane;
@@ -543,7 +670,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
     } else {
       // the union of the two rows, ascending (lane = bitmap word: nbp <= 2048)
       const unsigned a = (lane < nbp / 32) ? exb[0][lane] : 0u;
-      const unsigned b = (lane < nbp / 32) ? exb[1][lane] : 0u;
+      const unsigned b = (QB == 2 && lane < nbp / 32) ? exb[QB - 1][lane] : 0u;
       const unsigned u = a | b;
       const int n = __popc(u);
       int pre = n;                                       // inclusive prefix over lanes
@@ -750,41 +877,80 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
     }
 }
 
+// In-kernel routing keeps the pooled queries, the score rows and the select
+// histograms in the ring's LDS.
 template <class C>
+constexpr bool fused_route_fits(int nb) {
+  const int ncol = (nb + 63) / 64 * 64;
+  return nb <= kMaxBlocks &&
+         (size_t)C::QB * (C::D * 8 + ncol * 8 + 1024) <= (size_t)C::LDSB &&
+         (size_t)C::QB * (C::D * 8 + C::WPQ * C::D * 8) <= (size_t)C::LDSB;
+}
+
+// FR_: this configuration also serves in-kernel routing (the ones the
+// per-block first order alone uses do not)
+template <class C, bool FR_ = true>
 hipError_t launch_t(const AttnArgs& a) {
   const int grid = a.bh * ((a.nb + C::QB - 1) / C::QB);
   const int nbp = (a.nb + C::BLK - 1) / C::BLK * C::BLK;
   const bf16* pk = static_cast<const bf16*>(a.packed);
   AttnPtrs p{(const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.idx, a.centroid, a.vsum,
              a.hbar, pk, pk ? pk + (size_t)a.bh * nbp * C::D : nullptr,
-             pk ? pk + (size_t)2 * a.bh * nbp * C::D : nullptr, (const bf16*)a.ht, (bf16*)a.O};
+             pk ? pk + (size_t)2 * a.bh * nbp * C::D : nullptr, (const bf16*)a.ht, (bf16*)a.O,
+             a.M, a.idx_out};
+  const RouteIn ri{a.route_k, a.route_scale, a.route_lam};
   const bool fo = a.approx && a.order == kOrderFirst;
-  if constexpr (C::QB == 1) {
+  const bool fr = a.route_k > 0;
+  if (fr) {
+    if constexpr (FR_) {
+      if (fo || !fused_route_fits<C>(a.nb)) return hipErrorInvalidValue;
+      auto kern = a.lens ? attn_bf16_kernel<C, true, false, true> : attn_bf16_kernel<C, false, false, true>;
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax, a.approx, a.order,
+                         a.scale, a.nb, a.lens, a.heads, ri);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if constexpr (C::QB == 1) {
     auto kern = a.lens ? (fo ? attn_bf16_kernel<C, true, true> : attn_bf16_kernel<C, true, false>)
                        : (fo ? attn_bf16_kernel<C, false, true> : attn_bf16_kernel<C, false, false>);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax, a.approx, a.order,
-                       a.scale, a.nb, a.lens, a.heads);
+                       a.scale, a.nb, a.lens, a.heads, ri);
   } else {
     if (fo) return hipErrorInvalidValue;        // the launcher sends this order to QB = 1
     auto kern = a.lens ? attn_bf16_kernel<C, true, false> : attn_bf16_kernel<C, false, false>;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax, a.approx, a.order,
-                       a.scale, a.nb, a.lens, a.heads);
+                       a.scale, a.nb, a.lens, a.heads, ri);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
+int fused_route_max_blocks(int D, int BLK) {
+  int best = 0;
+  for (int nb = 1; nb <= kMaxBlocks; ++nb) {
+    bool ok = false;
+    if (D == 128 && BLK == 64) ok = fused_route_fits<Cfg<128, 64, 32, 2>>(nb);
+    if (D == 128 && BLK == 128) ok = fused_route_fits<Cfg<128, 128, 32>>(nb);
+    if (D == 64 && BLK == 64) ok = fused_route_fits<Cfg<64, 64, 32, 2>>(nb);
+    if (D == 64 && BLK == 128) ok = fused_route_fits<Cfg<64, 128, 64>>(nb);
+    if (ok) best = nb;
+  }
+  return best;
+}
+
 hipError_t launch_attn_bf16(const AttnArgs& a) {
   // 64-token blocks: query blocks in pairs, except for the per-block first order
   const bool fo = a.approx && a.order == kOrderFirst;
-  if (a.D == 128 && a.BLK == 64) return fo ? launch_t<Cfg<128, 64, 32>>(a) : launch_t<Cfg<128, 64, 32, 2>>(a);
+  if (a.D == 128 && a.BLK == 64)
+    return fo ? launch_t<Cfg<128, 64, 32>, false>(a) : launch_t<Cfg<128, 64, 32, 2>>(a);
   if (a.D == 128 && a.BLK == 128) {
     // the per-block first order streams whole 128-row H_j^T matrices: 64-key chunks
-    if (fo) return launch_t<Cfg<128, 128, 64>>(a);
+    if (fo) return launch_t<Cfg<128, 128, 64>, false>(a);
     return launch_t<Cfg<128, 128, 32>>(a);
   }
-  if (a.D == 64 && a.BLK == 64) return fo ? launch_t<Cfg<64, 64, 32>>(a) : launch_t<Cfg<64, 64, 32, 2>>(a);
+  if (a.D == 64 && a.BLK == 64)
+    return fo ? launch_t<Cfg<64, 64, 32>, false>(a) : launch_t<Cfg<64, 64, 32, 2>>(a);
   if (a.D == 64 && a.BLK == 128) return launch_t<Cfg<64, 128, 64>>(a);
   return hipErrorInvalidValue;
 }

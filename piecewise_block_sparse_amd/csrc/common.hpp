@@ -53,6 +53,13 @@ __device__ __forceinline__ int xcd_remap(int wg, int grid) {
   return x * q + (x < r ? x : r) + slot;
 }
 
+// Orders one wave's own LDS accesses among its lanes (no workgroup barrier).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Valid length of the sequence of (batch * heads) row bh: lens[bh / heads]

@@ -30,6 +30,13 @@ struct AttnArgs {
   const int32_t* lens;  // nullable device [batch]: valid length of each sequence
   int heads;
   hipStream_t stream;
+  // in-kernel routing (bf16): route_k > 0 selects each query block's route_k
+  // blocks inside the attention kernel (idx unused); idx_out receives them
+  const float* M;
+  int route_k;
+  double route_scale;
+  double route_lam;
+  int32_t* idx_out;     // nullable
 };
 
 struct StatsArgs {
@@ -86,6 +93,8 @@ size_t stats_workspace_f32(int bh, int nb, int D);
 size_t stats_packed_bytes(int bh, int nb, int D, int BLK);
 
 hipError_t launch_attn_bf16(const AttnArgs& a);
+// largest nb whose in-kernel routing fits the attention kernel's LDS (bf16)
+int fused_route_max_blocks(int D, int BLK);
 hipError_t launch_attn_f32(const AttnArgs& a);
 hipError_t launch_stats_bf16(const StatsArgs& a);
 hipError_t launch_stats_f32(const StatsArgs& a);

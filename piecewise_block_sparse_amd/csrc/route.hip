@@ -25,6 +25,7 @@
 // k candidates ends in -1, and an empty query block gets an all -1 row.
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk.hpp"
 
 namespace pisa {
 namespace {
@@ -63,21 +64,6 @@ template <int D, int R>
 __host__ __device__ constexpr size_t route_lds_bytes(int nbp) {
   return (size_t)R * D * 8 + (size_t)R * nbp * 8 + (size_t)R * 256 * 4 +
          (size_t)R * (nbp / 32) * 4;
-}
-
-// Ordering of one wave's LDS accesses among its own lanes (each row's histogram
-// and selection bitmap belong to one wave, so no workgroup barrier is needed).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// fp64 score -> unsigned key with the same order (larger score, larger key);
-// -0.0 becomes +0.0 first so that equal scores give equal keys
-__device__ __forceinline__ unsigned long long order_key(double x) {
-  const unsigned long long b = __builtin_bit_cast(unsigned long long, x + 0.0);
-  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
 template <int D, int BLK, typename T, int kRows>
@@ -161,7 +147,7 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
       }
       const double mj = lam * (double)Mh[j];
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) s_sc[r * nbp + j] = scale * acc[r] + mj;
+      for (int r = 0; r < kRows; ++r) s_sc[r * nbp + j] = fma(scale, acc[r], mj);
     }
   }
   double* sc = s_sc + w * nbp;
@@ -170,141 +156,13 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
   for (int t = lane; t < nbp / 32; t += 64) sel[t] = 0u;
   __syncthreads();
 
-  // ---- top-k by radix select on the order-preserving 64-bit keys, one row
-  // per wave.  Lane l owns candidates j = l + 64 u.  Each pass histograms the
-  // next 8-bit digit of the candidates still in play, finds the digit value d*
-  // holding the k-th largest, selects the candidates above it and keeps those
-  // equal to it in play.  After the last pass the ones left tie exactly with
-  // the k-th largest score; the lowest block ids among them fill the rest.
-  const int nu = nbp / 64;                                // candidates per lane (<= 32)
-  unsigned inplay = 0u, chosen = 0u;
-  for (int u = 0; u < nu; ++u)
-    if (lane + 64 * u < nne) inplay |= 1u << u;
+  // ---- top-k of this wave's row (ties to the lower block ids)
   const int kk = (ni > 0) ? min(k, nne) : 0;            // blocks this row can hold
-  int krem = kk;
-  // Digits above the highest bit in which the candidates' keys differ are the
-  // same for all of them (on these scores: the sign and most of the exponent),
-  // so those passes would split nothing: start below them.
-  int top_pass = 0;
-  {
-    unsigned long long kand = ~0ull, kor = 0ull;
-    for (int u = 0; u < nu; ++u)
-      if ((inplay >> u) & 1u) {
-        const unsigned long long key = order_key(sc[lane + 64 * u]);
-        kand &= key;
-        kor |= key;
-      }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const unsigned alo = __shfl_xor((unsigned)kand, off), ahi = __shfl_xor((unsigned)(kand >> 32), off);
-      const unsigned olo = __shfl_xor((unsigned)kor, off), ohi = __shfl_xor((unsigned)(kor >> 32), off);
-      kand &= ((unsigned long long)ahi << 32) | alo;
-      kor |= ((unsigned long long)ohi << 32) | olo;
-    }
-    const unsigned long long diff = kor & ~kand;          // bits that differ somewhere
-    if (diff != 0ull) top_pass = (63 - __clzll((long long)diff)) / 8;
-  }
-  for (int pass = top_pass; pass >= 0; --pass) {
-    // every candidate still in play is needed: take them all and stop early
-    int ip = __popc(inplay);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ip += __shfl_xor(ip, off);
-    if (ip == krem) {
-      chosen |= inplay;
-      inplay = 0u;
-      krem = 0;
-      break;
-    }
-    const int shift = 8 * pass;
-    for (int b = lane; b < 256; b += 64) hist[b] = 0u;
-    wave_sync();
-    for (int u = 0; u < nu; ++u)
-      if ((inplay >> u) & 1u) atomicAdd(&hist[(order_key(sc[lane + 64 * u]) >> shift) & 255u], 1u);
-    wave_sync();
-    // this lane holds histogram bins 4l .. 4l + 3
-    unsigned h[4], own = 0u;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      h[e] = hist[4 * lane + e];
-      own += h[e];
-    }
-    // exclusive suffix sum over lanes: above = sum of `own` over lanes > this lane
-    unsigned above;
-    {
-      unsigned incl = own;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const unsigned y = __shfl_down(incl, off);
-        if (lane + off < 64) incl += y;
-      }
-      above = incl - own;
-    }
-    int dstar = -1;
-    unsigned cnt_above = 0u;
-    {
-      unsigned acc = above;                               // count of bins > 4l + 3
-#pragma unroll
-      for (int e = 3; e >= 0; --e) {
-        if (dstar < 0 && acc < (unsigned)krem && acc + h[e] >= (unsigned)krem) {
-          dstar = 4 * lane + e;
-          cnt_above = acc;
-        }
-        acc += h[e];
-      }
-    }
-    const unsigned long long who = __ballot(dstar >= 0);
-    if (who == 0ull) {                                    // krem == 0: nothing left to pick
-      dstar = 256;
-      cnt_above = 0u;
-    } else {
-      const int src = __ffsll(who) - 1;
-      dstar = __shfl(dstar, src);
-      cnt_above = __shfl(cnt_above, src);
-    }
-    krem -= (int)cnt_above;
-    for (int u = 0; u < nu; ++u)
-      if ((inplay >> u) & 1u) {
-        const int dg = (int)((order_key(sc[lane + 64 * u]) >> shift) & 255u);
-        if (dg > dstar) {
-          chosen |= 1u << u;
-          inplay &= ~(1u << u);
-        } else if (dg < dstar) {
-          inplay &= ~(1u << u);
-        }
-      }
-    wave_sync();
-  }
-  // exact ties with the k-th largest: lowest block ids first
-  for (int u = 0; u < nu && krem > 0; ++u) {
-    const bool tie = (inplay >> u) & 1u;
-    const unsigned long long m = __ballot(tie);
-    const int before_me = __popcll(m & ((1ull << lane) - 1));
-    if (tie && before_me < krem) chosen |= 1u << u;
-    krem -= min(krem, __popcll(m));
-  }
-  for (int u = 0; u < nu; ++u)
-    if ((chosen >> u) & 1u) atomicOr(&sel[(lane + 64 * u) >> 5], 1u << ((lane + 64 * u) & 31));
-  wave_sync();
+  select_top_k(sc, hist, sel, nbp / 64, nne, kk, lane);
 
   // ---- the selected ids, written in ascending order
   if (!active) return;
-  int32_t* out = idx + ((size_t)bh * nb + i) * k;
-  const int nw = nbp / 32;                                   // <= 64 words
-  const unsigned word = (lane < nw) ? sel[lane] : 0u;
-  int cnt = __popc(word), pre = cnt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(pre, off);
-    if (lane >= off) pre += y;
-  }
-  int pos = pre - cnt;
-  unsigned wv = word;
-  while (wv) {
-    const int b = __ffs(wv) - 1;
-    out[pos++] = 32 * lane + b;
-    wv &= wv - 1;
-  }
-  for (int e = kk + lane; e < k; e += 64) out[e] = -1;   // fewer candidates than k
+  write_ids_ascending(sel, nbp / 32, kk, k, idx + ((size_t)bh * nb + i) * k, lane);
 }
 
 template <int D, int BLK, typename T, int R>

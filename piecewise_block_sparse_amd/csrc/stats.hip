@@ -41,13 +41,6 @@ struct SCfg {
   static_assert(BLK % CK == 0 && NDMA % NW == 0 && DPW % 2 == 0, "chunking");
 };
 
-// Orders one wave's own LDS accesses among its lanes (no workgroup barrier).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Sum of the 8 bf16 values of a fragment, added to acc (v_dot2 against 1;
 // the pairs are taken from the bf16 view of the fragment).
 __device__ __forceinline__ float frag_sum(const u32x4& f, float acc) {

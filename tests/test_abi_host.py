@@ -164,3 +164,32 @@ def test_precompute_Ht_is_bf16_only(lib):
     out = _lib.PisaStats(p, p, None, p, p, None, p)
     assert pre(lib, shape(dtype=_lib.DTYPE_FP32), out=out) == 3
     assert b"Ht" in lib.pisa_last_error()
+
+
+def ra(lib, shp, k=4, lam=0.1, mode=0, scale=0.1, st=None, O=FAKE):
+    st = stats() if st is None else st
+    return lib.pisa_route_attention(ctypes.byref(shp), FAKE, FAKE, FAKE, ctypes.byref(st), k, lam,
+                                    mode, scale, None, O, None)
+
+
+def test_route_attention_arguments(lib):
+    s = shape()                                                     # nb = 16
+    assert ra(lib, shape(L=1000)) == 2
+    assert ra(lib, s, k=0) == 3
+    assert ra(lib, s, k=17) == 3
+    assert ra(lib, s, lam=float("nan")) == 3
+    assert ra(lib, s, scale=float("inf")) == 3
+    assert ra(lib, s, scale=1e-300) == 3                            # zero as a float
+    assert ra(lib, s, mode=9) == 3
+    assert ra(lib, s, mode=_lib.MODE_FIRST) == 3
+    assert b"pisa_route" in lib.pisa_last_error()
+    assert ra(lib, s, O=None) == 1
+    p = FAKE.value
+    assert ra(lib, s, st=_lib.PisaStats(p, p, None, p, None, None)) == 1    # routing reads M
+    assert ra(lib, s, st=_lib.PisaStats(p, p, None, None, p, None)) == 1    # APPROX reads Hbar
+    assert ra(lib, s, mode=_lib.MODE_ZEROTH, st=_lib.PisaStats(p, None, None, None, p, None)) == 1
+    assert ra(lib, shape(dtype=_lib.DTYPE_FP32)) == 4
+    # score rows that do not fit the kernel's LDS: 64-token blocks, d = 128, nb = 1856
+    assert ra(lib, shape(L=64 * 1856)) == 2
+    assert b"pisa_route, then pisa_attention" in lib.pisa_last_error()
+    assert ra(lib, shape(L=64 * 896, d=64)) == 2                    # d = 64: nb <= 832

@@ -31,7 +31,7 @@ def test_profiled_traffic_is_read_only_for_the_profiled_kernel_source(tmp_path, 
         "attn_bf16_kernel traffic_bytes_per_launch=3 read=2 write=1 avg_ns=5 source=0000000000000000\n")
     csrc = tmp_path / "piecewise_block_sparse_amd" / "csrc"
     csrc.mkdir(parents=True)
-    for f in ("attn_bf16.hip", "lds_stream.hpp", "common.hpp"):
+    for f in ("attn_bf16.hip", "lds_stream.hpp", "common.hpp", "topk.hpp"):
         (csrc / f).write_text("x")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.profiled_traffic("x") is None
