@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PISA_VERSION 100 /* major * 100 + minor */
+#define PISA_VERSION 101 /* major * 100 + minor; 1.01 adds pisa_route_attention */
 
 typedef enum {
   PISA_OK = 0,

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.pisa_version() == 100
+    assert lib.pisa_version() == 101
 
 
 def test_probe_library_exports_its_declared_symbol():
