@@ -133,17 +133,22 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
       double acc[kRows];
 #pragma unroll
       for (int r = 0; r < kRows; ++r) acc[r] = 0.0;
-#pragma unroll 4
-      for (int a = 0; a < D; a += 4) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(cj + a);
+      // the centroid row in batches of eight 16-byte loads in flight (the
+      // scoring waits on L2 latency, not on the FMAs)
+      for (int a0 = 0; a0 < D; a0 += 32) {
+        f32x4 kv[8];
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-          const double* q = s_q + r * D + a;
-          acc[r] = fma(q[0], (double)kv[0], acc[r]);
-          acc[r] = fma(q[1], (double)kv[1], acc[r]);
-          acc[r] = fma(q[2], (double)kv[2], acc[r]);
-          acc[r] = fma(q[3], (double)kv[3], acc[r]);
-        }
+        for (int u = 0; u < 8; ++u) kv[u] = *reinterpret_cast<const f32x4*>(cj + a0 + 4 * u);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int r = 0; r < kRows; ++r) {
+            const double* q = s_q + r * D + a0 + 4 * u;
+            acc[r] = fma(q[0], (double)kv[u][0], acc[r]);
+            acc[r] = fma(q[1], (double)kv[u][1], acc[r]);
+            acc[r] = fma(q[2], (double)kv[u][2], acc[r]);
+            acc[r] = fma(q[3], (double)kv[u][3], acc[r]);
+          }
       }
       const double mj = lam * (double)Mh[j];
 #pragma unroll
