@@ -458,6 +458,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   static_assert(QB == 1 || !FO, "the per-block first order runs one query block per workgroup");
   __shared__ unsigned bits[QB][kBitWords];
   static_assert(!(FR && FO), "in-kernel routing runs with the other orders");
+  static_assert(!FR || QB * BLK * C::RB <= C::LDSB, "in-kernel routing stages the query rows in the ring");
   __shared__ unsigned exb[QB == 2 ? 2 : 1][(QB == 2 || FR) ? kBitWords : 1];   // exact blocks
   __shared__ short s_list[kMaxBlocks];                 // exact block ids of S_i, in order;
                                                        // then (per-block first order) U_i.
