@@ -17,7 +17,8 @@ after a 512 MB scratch write (caches flushed); `density_sweep` re-routes the sam
 inputs at top-k 128 / 64 / 32 / 16 of 256 blocks and times both modes; `orders`
 times the zeroth-order and the per-block first-order treatments of the
 unselected blocks on the same inputs; `route_attention_fused` times the
-single-launch routing-and-attention call against the two calls it replaces;
+single-launch routing-and-attention call against the two calls it replaces
+(also on the short image-DiT workload, under `secondary`);
 `roofline.attainable` is the MFMA rate
 the chip sustains for the exact phase's per-chunk instruction mix on random
 operands, and its streaming HBM read rate (libpisa_probe), beside the published
@@ -200,6 +201,42 @@ def time_route_attention(pisa, torch, Qd, Kd, Vd, st, w, reps):
     b.record(stream)
     b.synchronize()
     return a.elapsed_time(b) / reps
+
+
+def short_sequence(pisa, torch, reps):
+    """The image-DiT workload (24 heads x 4096 tokens, 64-token blocks): routing
+    then attention as two calls, and as the single-launch routing call."""
+    from piecewise_block_sparse_amd import workloads as wl
+    w = wl.WORKLOADS[2]
+    log(f"{w.name}: route + attention against the single-launch call")
+    Q, K, V = wl.make_inputs(w)
+    Qd, Kd, Vd = (torch.from_numpy(a).to("cuda", torch.bfloat16) for a in (Q, K, V))
+    st = pisa.precompute(Kd, Vd, w.block)
+    stream = torch.cuda.current_stream()
+
+    def split():
+        idx = pisa.route(Qd, st, w.k, w.lam, w.block)
+        pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode="approx")
+
+    def fused():
+        pisa.route_attention(Qd, Kd, Vd, st, w.k, w.lam, w.block, mode="approx")
+
+    out = {}
+    for name, fn in (("route_plus_attention_ms", split), ("fused_ms", fused),
+                     ("route_plus_attention_ms_again", split), ("fused_ms_again", fused)):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        out[name] = a.elapsed_time(b) / reps
+    return {"route_attention_fused": {
+        "ms": min(out["fused_ms"], out["fused_ms_again"]),
+        "route_plus_attention_ms": min(out["route_plus_attention_ms"],
+                                       out["route_plus_attention_ms_again"])}}
 
 
 def time_sdpa(torch, Qd, Kd, Vd, dense_flops, t_pisa):
@@ -460,6 +497,8 @@ def main():
         other = 3 if args.workload == 4 else 4
         _, res2 = run(other, args.steps, max(3, args.warmup), False, cold=not args.no_cold)
         line["secondary"] = {wl.WORKLOADS[other].name: res2}
+        if not args.no_exact_split:
+            line["secondary"][wl.WORKLOADS[2].name] = short_sequence(pisa, torch, max(5, args.steps // 2))
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         line["cpu_baseline"] = cpu_baseline(w)
