@@ -508,7 +508,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
 
   if constexpr (FR) {
     // ---- in-kernel routing.  LDS (the ring, idle until the chunk stream
-    // starts): qbar [QB][D] f64 | pooling partials [QB][WPQ][D] f64, then the
+    // starts): first the query rows, staged for pooling over the whole ring;
+    // then qbar [QB][D] f64 | pooling partials [QB][WPQ][D] f64, then the
     // scores [QB][ncol] f64 in their place | at the end, the select
     // histograms [QB][256] u32 (the launcher checks that the scores fit).
     double* s_qbar = reinterpret_cast<double*>(lds);
