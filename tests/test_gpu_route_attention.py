@@ -167,3 +167,17 @@ def test_fp32_and_first_order_are_refused(torch):
     stb = pisa.precompute(Xb, Xb, 64)
     with pytest.raises(pisa._lib.PisaError):
         pisa.route_attention(Xb, Xb, Xb, stb, 2, 0.1, 64, mode="first")
+
+
+@pytest.mark.parametrize("wid", [2, 5])
+def test_without_the_statistics_pack(torch, wid):
+    """Without the bf16 pack the kernel converts the fp32 statistics itself,
+    staging them in the ring that the routing prologue used first: same
+    selection and outputs as the split path without the pack."""
+    pisa = pisa_mod()
+    w = wl.WORKLOADS[wid]
+    Q, K, V = wl.make_inputs(w)
+    Qd, Kd, Vd = (to_dev(x, w.dtype) for x in (Q, K, V))
+    st = dict(pisa.precompute(Kd, Vd, w.block), packed=None)
+    k = w.k if w.k > 0 else 8
+    _fused_vs_split(torch, pisa, Qd, Kd, Vd, st, k, 0.1, w.block, name=f"{w.name}/no-pack")
