@@ -291,17 +291,20 @@ def cpu_baseline(w, budget_s=20.0):
 
 
 def attainable_rates(pisa):
-    """What the chip sustains on this machine (libpisa_probe): the bf16 MFMA rate
-    of the exact phase's per-chunk instruction mix at the attention kernel's
-    occupancy (MFMAs alone and the full chunk step on N(0, 1)-like operands,
-    and the full step on zeros: the same instructions without operand
-    toggling), and the HBM rate of a plain 2 GiB streaming read."""
+    """MFMA and HBM rates measured on this machine (libpisa_probe), at the
+    attention kernel's occupancy: the bf16 MFMA stream alone with every operand
+    in registers (N(0, 1)-like and all-zero operands: the clock the chip holds
+    under MFMA work with and without operand toggling), the same MFMAs fed
+    from LDS as the exact phase feeds them, the full per-chunk step of the
+    exact phase (with and without toggling), and the HBM rate of a plain
+    2 GiB streaming read."""
     import ctypes
     probe = pisa._lib.load_probe()
     out = {"unit": "TFLOP/s (MFMA rates), GB/s (hbm_read_gbs)",
            "data": "N(0,1)-like bf16 operands (zeros where named)",
            "probe": "pisa_probe_chunk_rate, pisa_probe_read_rate (include/pisa_probe.h)"}
-    for name, mix, zeros in (("mfma_only", 0, 0), ("chunk_mix", 1, 0), ("chunk_mix_zeros", 1, 1)):
+    for name, mix, zeros in (("mfma_regs", 2, 0), ("mfma_regs_zeros", 2, 1), ("mfma_only", 0, 0),
+                             ("chunk_mix", 1, 0), ("chunk_mix_zeros", 1, 1)):
         r = ctypes.c_double(0.0)
         rc = probe.pisa_probe_chunk_rate(mix, zeros, 2000, 5, ctypes.byref(r))
         if rc != 0:

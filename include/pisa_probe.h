@@ -28,7 +28,10 @@ int pisa_probe_read_rate(size_t bytes, int reps, double* gbs);
 /* mix    0: MFMAs only (S^T = K Q^T as 8 dependent 32x32x16 MFMAs, then
  *           O^T += V^T P^T as 8 MFMAs; P is S truncated to bf16);
  *        1: the full chunk step (the same MFMAs plus the softmax weights, one
- *           workgroup barrier and the global -> LDS copy of the next chunk).
+ *           workgroup barrier and the global -> LDS copy of the next chunk);
+ *        2: the 16 MFMAs per chunk alone with every operand in registers
+ *           (eight A and eight B fragments cycled, four independent
+ *           accumulators; no LDS, no barrier, no copies).
  * zeros  0: N(0, 1)-like bf16 operands; 1: all operands zero.
  * iters  chunks per wave per launch (>= 1); reps timed launches (>= 1) after
  *        one warm-up launch.

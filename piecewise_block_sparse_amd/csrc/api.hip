@@ -75,7 +75,7 @@ const char* pisa_last_error(void) { return g_err; }
 size_t pisa_workspace_size(const pisa_shape* shape) {
   int bh = 0, nb = 0;
   if (check_shape(shape, &bh, &nb) != PISA_OK) return 0;
-  return shape->dtype == PISA_DTYPE_BF16 ? pisa::stats_workspace_bf16(bh, nb, shape->head_dim)
+  return shape->dtype == PISA_DTYPE_BF16 ? pisa::stats_workspace_bf16(bh, nb, shape->head_dim, shape->block)
                                          : pisa::stats_workspace_f32(bh, nb, shape->head_dim);
 }
 

@@ -85,10 +85,7 @@ constexpr int kOrderFirst = 2;    // per-block H_j
 // largest nb (= L / block) the kernels accept
 constexpr int kMaxBlocks = 2048;
 
-// blocks of one head handled by one statistics workgroup (bf16 path)
-constexpr int kStatsGroup = 8;
-
-size_t stats_workspace_bf16(int bh, int nb, int D);
+size_t stats_workspace_bf16(int bh, int nb, int D, int BLK);
 size_t stats_workspace_f32(int bh, int nb, int D);
 size_t stats_packed_bytes(int bh, int nb, int D, int BLK);
 

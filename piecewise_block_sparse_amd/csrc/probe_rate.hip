@@ -15,6 +15,12 @@
 //   mix = 1  the full chunk step: the same MFMAs plus the softmax weights
 //            (16 exp2, 8 bf16 packs, 8 dot2 sums), a workgroup barrier per
 //            chunk and the two-stage global -> LDS copy ring of the next chunk.
+//   mix = 2  registers only: the same 16 MFMAs per wave and chunk with every
+//            operand in VGPRs (eight A and eight B fragments, cycled so that
+//            consecutive MFMAs see different random operands) into four
+//            independent accumulators; no LDS, no barrier, no copies.  This
+//            separates the clock the chip holds under MFMA work on toggling
+//            operands from the cost of feeding the MFMAs from LDS.
 //
 // Operands: Q in registers, K / V chunks copied from a 2 MB buffer (L2
 // resident) of N(0, 1)-like bf16 values; `zeros` = 1 fills everything with
@@ -140,6 +146,35 @@ __global__ __launch_bounds__(256, 3) void probe_kernel(const char* src, float* o
   out[(size_t)blockIdx.x * 256 + tid] = r;
 }
 
+// mix = 2: the MFMA stream alone, operands in registers.  Same grid and
+// occupancy as probe_kernel (three 4-wave workgroups per CU).
+__global__ __launch_bounds__(256, 3) void probe_regs_kernel(float* out, int iters, int zeros) {
+  const int tid = threadIdx.x;
+  bf16x8 af[8], bfr[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const unsigned e = 64u * (unsigned)(blockIdx.x * 256 + tid) + 8u * (unsigned)u;
+    af[u] = as_bf16x8(u32x4{pair_at(e, zeros), pair_at(e + 1, zeros), pair_at(e + 2, zeros), pair_at(e + 3, zeros)});
+    bfr[u] = as_bf16x8(u32x4{pair_at(e + 4, zeros), pair_at(e + 5, zeros), pair_at(e + 6, zeros), pair_at(e + 7, zeros)});
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) acc[a] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+    // 16 MFMAs per chunk, as in the exact phase; accumulator a % 4, A fragment
+    // u, B fragment (u + 3 (u / 8) + 1) % 8: no two consecutive MFMAs share an operand
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      acc[u % 4] = mfma32(af[u % 8], bfr[(u + 3 * (u / 8) + 1) % 8], acc[u % 4]);
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) r += acc[a][e];
+  out[(size_t)blockIdx.x * 256 + tid] = r;
+}
+
 // Streaming read: workgroup b sums words [b * per, (b + 1) * per) of the buffer
 // with 16-byte loads, eight per lane in flight; the sum is written only if it
 // hits a sentinel, so the loads cannot be dropped.
@@ -203,7 +238,7 @@ extern "C" int pisa_probe_read_rate(size_t bytes, int reps, double* gbs) {
 
 extern "C" int pisa_probe_chunk_rate(int mix, int zeros, int iters, int reps, double* tflops) {
   using namespace pisa;
-  if (!tflops || (mix != 0 && mix != 1) || iters < 1 || reps < 1) return (int)hipErrorInvalidValue;
+  if (!tflops || mix < 0 || mix > 2 || iters < 1 || reps < 1) return (int)hipErrorInvalidValue;
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -220,7 +255,8 @@ extern "C" int pisa_probe_chunk_rate(int mix, int zeros, int iters, int reps, do
   if (e == hipSuccess) {
     fill_kernel<<<(nwords + 255) / 256, 256>>>(reinterpret_cast<unsigned*>(src), nwords, zeros);
     auto launch = [&]() {
-      if (mix) probe_kernel<1><<<grid, 256>>>(src, out, iters, zeros);
+      if (mix == 2) probe_regs_kernel<<<grid, 256>>>(out, iters, zeros);
+      else if (mix == 1) probe_kernel<1><<<grid, 256>>>(src, out, iters, zeros);
       else probe_kernel<0><<<grid, 256>>>(src, out, iters, zeros);
     };
     launch();                                // warm-up

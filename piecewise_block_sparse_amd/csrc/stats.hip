@@ -7,8 +7,8 @@
 //
 // bf16 path: H_j = K_j^T V_j - kbar_j^T sigma_j, with K_j^T V_j on bf16 MFMA
 // (products of bf16 values are exact in the fp32 accumulator).  Pass 1 streams
-// K and V once and writes one fp32 partial sum of H_j per group of
-// kStatsGroup blocks; a fixed-order fp64 reduction gives Hbar; pass 2 streams K
+// K and V once and writes one fp32 partial sum of H_j per workgroup range of
+// blocks; a fixed-order fp64 reduction gives Hbar; pass 2 streams K
 // and V again, recomputes each H_j and writes M_j (and H_j when asked).  No
 // atomics: results are bitwise reproducible.
 //
@@ -38,8 +38,29 @@ struct SCfg {
   // at two workgroups per CU with four stages
   static constexpr int NS = (BLK == 64) ? 3 : 4;
   static constexpr int TM = (D == 128) ? 2 : 1;       // 32x32 output tiles per wave, per dim
+  // blocks per workgroup range: at most PMAX (the pass-1 register window of
+  // per-block outputs), at least PMIN, else enough for one round of GT
+  // workgroups (two or three per CU on 256 CUs)
+  static constexpr int PMAX = (BLK == 128) ? 24 : 8;
+  static constexpr int PMIN = 4;
+  static constexpr int GT = (BLK == 64) ? 768 : 512;
   static_assert(BLK % CK == 0 && NDMA % NW == 0 && DPW % 2 == 0, "chunking");
 };
+
+// Ranges per head (bf16 path): enough workgroups for one round of GT (b*h*R
+// <= GT), ranges of at most PMAX blocks and, where the head allows, at least
+// PMIN.  Depends on the shape only, so results are reproducible.
+template <int D, int BLK>
+int stats_ranges(int bh, int nb) {
+  using C = SCfg<D, BLK>;
+  long long r = C::GT / bh;                                  // one round of GT workgroups
+  const long long rmin = (nb + C::PMAX - 1) / C::PMAX;       // the window holds PMAX blocks
+  const long long rmax = nb / C::PMIN > 0 ? nb / C::PMIN : 1;
+  if (r > rmax) r = rmax;
+  if (r < rmin) r = rmin;
+  if (r < 1) r = 1;
+  return (int)r;
+}
 
 // Sum of the 8 bf16 values of a fragment, added to acc (v_dot2 against 1;
 // the pairs are taken from the bf16 view of the fragment).
@@ -53,33 +74,43 @@ __device__ __forceinline__ float frag_sum(const u32x4& f, float acc) {
   return acc;
 }
 
-// One workgroup per group of kStatsGroup consecutive blocks of one head.  The
-// group's tokens stream through the ring in 32-token chunks; for each 16-token
-// slab every wave reads its K^T and V fragments with transposing LDS reads
-// (both operands index tokens the same way), accumulates K_j^T V_j on MFMA and
-// the column sums of K and V from the same fragments (lanes l and l + 32 hold
-// the two halves of a column's tokens).  At the end of a block the sums give
-// kbar_j and sigma_j, and H_j = K_j^T V_j - kbar_j^T sigma_j.
+// Work split.  Each head's nb blocks are dealt in R near-equal contiguous
+// ranges, one per workgroup: range r covers blocks r*nb/R .. (r+1)*nb/R - 1
+// (stats_ranges picks R so that the b*h*R workgroups fill one round on a
+// 256-CU MI355X and a range holds at most PMAX blocks).  Pass 1 writes the
+// range's sum of H_j to partial slot bh*R + r; the reduction sums a head's R
+// slots in order (a fixed order: bitwise reproducible).  Pass 2 walks its range
+// backwards, last block first: the blocks pass 1 read last are the ones most
+// likely still held by the memory-side cache.
+//
+// Per 16-token slab every wave reads its K^T and V fragments with transposing
+// LDS reads (both operands index tokens the same way), accumulates K_j^T V_j
+// on MFMA and the column sums of K and V from the same fragments (lanes l and
+// l + 32 hold the two halves of a column's tokens).  At the end of a block the
+// sums give kbar_j and sigma_j, and H_j = K_j^T V_j - kbar_j^T sigma_j.
 // STORE: pass 2 also writes the optional H_j (fp32) and H_j^T (bf16) outputs.
 template <int D, int BLK, bool PASS2, bool STORE>
 __global__ __launch_bounds__(256, (PASS2 && STORE) ? 2 : (BLK == 64 ? 3 : 2)) void stats_bf16_kernel(
-    const bf16* __restrict__ K, const bf16* __restrict__ V, int nb, float* __restrict__ centroid,
-    float* __restrict__ vsum, float* __restrict__ partial, const float* __restrict__ hbar_frag,
-    float* __restrict__ M, float* __restrict__ Hout, bf16* __restrict__ pk_cen,
-    bf16* __restrict__ pk_vsum, bf16* __restrict__ Ht, const int32_t* __restrict__ lens,
-    int heads) {
+    const bf16* __restrict__ K, const bf16* __restrict__ V, int nb, int R,
+    float* __restrict__ centroid, float* __restrict__ vsum, float* __restrict__ partial,
+    const float* __restrict__ hbar_frag, float* __restrict__ M, float* __restrict__ Hout,
+    bf16* __restrict__ pk_cen, bf16* __restrict__ pk_vsum, bf16* __restrict__ Ht,
+    const int32_t* __restrict__ lens, int heads) {
   using C = SCfg<D, BLK>;
-  constexpr int TM = C::TM;
+  constexpr int TM = C::TM, PM = C::PMAX;
   __shared__ __attribute__((aligned(1024))) char ring[C::NS * C::STB];
   __shared__ float s_kv[C::NW][2][TM * 32];              // per wave: its kbar and sigma entries
-  __shared__ float s_sq[kStatsGroup][C::NW];              // per block and wave: part of ||H_j - Hbar||^2
+  __shared__ float s_sq[PM][C::NW];                       // per block and wave: part of ||H_j - Hbar||^2
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q32 = lane & 31, hh = lane >> 5;
-  const int ngrp = (nb + kStatsGroup - 1) / kStatsGroup;
-  const int bh = blockIdx.x / ngrp, grp = blockIdx.x - bh * ngrp;
-  const int j0 = grp * kStatsGroup;
-  const int j1 = min(nb, j0 + kStatsGroup);
+  const int bh = blockIdx.x / R, rg = blockIdx.x - bh * R;
+  // (scalars: the copies take their global base from scalar registers)
+  const int j0 = __builtin_amdgcn_readfirstlane((int)((long long)rg * nb / R));
+  const int j1 = __builtin_amdgcn_readfirstlane((int)((long long)(rg + 1) * nb / R));
+  const int ng = j1 - j0;                                 // 1 .. PMAX blocks
+  // block at walk position u (pass 2 walks backwards)
+  auto block_at = [&](int u) { return PASS2 ? j1 - 1 - u : j0 + u; };
   const size_t L = (size_t)nb * BLK;
   const int mt0 = (w >> 1) * TM, nt0 = (w & 1) * TM;
   const bool kout = nt0 == 0, vout = mt0 == 0;            // waves that write centroid / value sum
@@ -93,7 +124,7 @@ __global__ __launch_bounds__(256, (PASS2 && STORE) ? 2 : (BLK == 64 ? 3 : 2)) vo
 
   // pass 2: this lane's Hbar entries (stored by the reduction in fragment
   // order: 4 consecutive floats per tile and row group), held for the whole
-  // group; loaded before the ring starts so no wait for them lands in the loop
+  // range; loaded before the ring starts so no wait for them lands in the loop
   f32x4 hb[TM][TM][4];
   if (PASS2) {
     const float* hbf = hbar_frag + (size_t)bh * D * D + (size_t)w * TM * TM * 1024 + 4 * lane;
@@ -117,11 +148,11 @@ __global__ __launch_bounds__(256, (PASS2 && STORE) ? 2 : (BLK == 64 ? 3 : 2)) vo
       bo[a][h] = tr_lane_offset<C>(lane, nt0 + a, h) + C::SUBB;
     }
   const unsigned ring_m0 = (unsigned)(uintptr_t)(lvoid*)ring;
-  const int nch = (j1 - j0) * C::CPB;                     // the group's tokens are contiguous
-  const char* Kb = reinterpret_cast<const char*>(K + ((size_t)bh * L + (size_t)j0 * BLK) * D);
-  const char* Vb = reinterpret_cast<const char*>(V + ((size_t)bh * L + (size_t)j0 * BLK) * D);
+  const int nch = ng * C::CPB;
+  const char* Kb = reinterpret_cast<const char*>(K + (size_t)bh * L * D);
+  const char* Vb = reinterpret_cast<const char*>(V + (size_t)bh * L * D);
   auto issue = [&](int u) {                 // copy chunk u into stage u % NS
-    const size_t off = (size_t)u * C::SUBB;
+    const size_t off = ((size_t)block_at(u / C::CPB) * BLK + (size_t)(u % C::CPB) * C::CK) * C::RB;
     dma_stage<C>(Kb + off, Vb + off, ring_m0 + (unsigned)((u % C::NS) * C::STB), ws, loff);
   };
   for (int u = 0; u < C::NS - 1 && u < nch; ++u) issue(u);
@@ -133,9 +164,9 @@ __global__ __launch_bounds__(256, (PASS2 && STORE) ? 2 : (BLK == 64 ? 3 : 2)) vo
   // Per-block outputs are written after the loop: stores count in vmcnt with
   // the copies, so a store issued between copies would hold up every later
   // wait for a chunk.  Pass 1 keeps the lane's centroid / value-sum entries of
-  // the group's blocks in a window shifted by one block at each block end
-  // (entry kStatsGroup - 1 is the newest); pass 2 keeps M_j in LDS.
-  float ocen[TM][kStatsGroup], ovs[TM][kStatsGroup];
+  // the range's blocks in a window shifted by one block at each block end
+  // (entry PM - 1 is the newest); pass 2 keeps M_j in LDS.
+  float ocen[TM][PM], ovs[TM][PM];
 
   for (int t = 0; t < nch; ++t) {
     // chunk t: wait for it (chunks t + 1 .. t + NS - 2 may be in flight),
@@ -143,7 +174,7 @@ __global__ __launch_bounds__(256, (PASS2 && STORE) ? 2 : (BLK == 64 ? 3 : 2)) vo
     wait_groups<C>(min(C::NS - 2, nch - 1 - t));
     __syncthreads();
     if (t + C::NS - 1 < nch) issue(t + C::NS - 1);
-    const int j = j0 + t / C::CPB, tb = (t % C::CPB) * C::CK;
+    const int u = t / C::CPB, j = block_at(u), tb = (t % C::CPB) * C::CK;
     const int nj = block_count(Lv, j, BLK);
     char* stage = ring + (t % C::NS) * C::STB;
     if (nj < tb + C::CK) {
@@ -187,19 +218,19 @@ __global__ __launch_bounds__(256, (PASS2 && STORE) ? 2 : (BLK == 64 ? 3 : 2)) vo
       }
       if (!PASS2) {
 #pragma unroll
-        for (int g = 0; g + 1 < kStatsGroup; ++g) {
+        for (int g = 0; g + 1 < PM; ++g) {
           ocen[a][g] = ocen[a][g + 1];
           ovs[a][g] = ovs[a][g + 1];
         }
-        ocen[a][kStatsGroup - 1] = kbar;
-        ovs[a][kStatsGroup - 1] = sv;
+        ocen[a][PM - 1] = kbar;
+        ovs[a][PM - 1] = sv;
       }
     }
     // every wave summed its own rows and columns, so the exchange stays
     // inside the wave: no workgroup barrier at the end of a block
     wave_sync();
 
-    // H_j = K_j^T V_j - kbar_j^T sigma_j (pass 1: summed over the group)
+    // H_j = K_j^T V_j - kbar_j^T sigma_j (pass 1: summed over the range)
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -223,10 +254,10 @@ __global__ __launch_bounds__(256, (PASS2 && STORE) ? 2 : (BLK == 64 ? 3 : 2)) vo
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               const int r = 4 * g + rr;
-              const float x = acc[a][b][r];
-              const float dlt = x - hb[a][b][g][rr];
+              const float xv = acc[a][b][r];
+              const float dlt = xv - hb[a][b][g][rr];
               sq += dlt * dlt;
-              if (Hj) Hj[(32 * (mt0 + a) + 8 * (r / 4) + 4 * hh + (r % 4)) * D + 32 * (nt0 + b) + q32] = x;
+              if (Hj) Hj[(32 * (mt0 + a) + 8 * (r / 4) + 4 * hh + (r % 4)) * D + 32 * (nt0 + b) + q32] = xv;
             }
       if (STORE && Ht) {
         // H_j^T in bf16: row = value dim, 4 consecutive key-dim columns per store
@@ -237,14 +268,14 @@ __global__ __launch_bounds__(256, (PASS2 && STORE) ? 2 : (BLK == 64 ? 3 : 2)) vo
           for (int b = 0; b < TM; ++b)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-              const f32x16& x = acc[a][b];
-              const u32x2 v = {pack2(x[4 * g4], x[4 * g4 + 1]), pack2(x[4 * g4 + 2], x[4 * g4 + 3])};
+              const f32x16& xa = acc[a][b];
+              const u32x2 v = {pack2(xa[4 * g4], xa[4 * g4 + 1]), pack2(xa[4 * g4 + 2], xa[4 * g4 + 3])};
               st8(Hjt + (size_t)(32 * (nt0 + b) + q32) * D + 32 * (mt0 + a) + 8 * g4 + 4 * hh, v);
             }
       }
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
-      if (lane == 0) s_sq[j - j0][w] = (nj > 0) ? sq : -1.f;     // -1: empty block
+      if (lane == 0) s_sq[u][w] = (nj > 0) ? sq : -1.f;        // -1: empty block
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -252,20 +283,19 @@ __global__ __launch_bounds__(256, (PASS2 && STORE) ? 2 : (BLK == 64 ? 3 : 2)) vo
     }
   }
 
-  // ---- the group's per-block outputs (the loop ends with a full wait)
-  const int ng = j1 - j0;
+  // ---- the range's per-block outputs (the loop ends with a full wait)
   if (PASS2) {
     __syncthreads();
     if (tid < ng) {
       const float* q = s_sq[tid];
-      M[(size_t)bh * nb + j0 + tid] = q[0] < 0.f ? 0.f : sqrtf(q[0] + q[1] + q[2] + q[3]);
+      M[(size_t)bh * nb + block_at(tid)] = q[0] < 0.f ? 0.f : sqrtf(q[0] + q[1] + q[2] + q[3]);
     }
   } else {
     const size_t nbp = (size_t)(nb + BLK - 1) / BLK * BLK;
 #pragma unroll
-    for (int g = 0; g < kStatsGroup; ++g) {
-      const int jj = j0 + g - (kStatsGroup - ng);          // block of window entry g
-      if (g < kStatsGroup - ng || hh != 0) continue;
+    for (int g = 0; g < PM; ++g) {
+      const int jj = j0 + g - (PM - ng);                   // block of window entry g
+      if (g < PM - ng || hh != 0) continue;
 #pragma unroll
       for (int a = 0; a < TM; ++a) {
         if (kout) {
@@ -280,10 +310,7 @@ __global__ __launch_bounds__(256, (PASS2 && STORE) ? 2 : (BLK == 64 ? 3 : 2)) vo
         }
       }
     }
-  }
-
-  if (!PASS2) {
-    float* P = partial + ((size_t)bh * ngrp + grp) * D * D;
+    float* P = partial + (size_t)blockIdx.x * D * D;
 #pragma unroll
     for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -294,8 +321,10 @@ __global__ __launch_bounds__(256, (PASS2 && STORE) ? 2 : (BLK == 64 ? 3 : 2)) vo
   }
 }
 
-// Hbar[bh] = (1 / n) sum_g parts[bh][g] (n = the non-empty blocks: all nb
-// without lengths), summed in fp64 in group order (fixed, reproducible).  One
+// Hbar[bh] = (1 / n) sum of head bh's R partial sums (slots bh*R .. bh*R +
+// R - 1: the ranges of the bf16 statistics kernel, or the fp32 path's one
+// matrix per block with R = nb), n = the non-empty blocks (all nb without
+// lengths), summed in fp64 in slot order (fixed, reproducible).  One
 // workgroup per 32x32 tile of one head; each thread sums 4 adjacent entries of
 // a tile row with 16-byte loads.  The tile is then staged in LDS so that the
 // other layouts are written with whole rows too: Hbar in the fragment order of
@@ -364,11 +393,12 @@ __global__ __launch_bounds__(256) void hbar_reduce_kernel(const float* __restric
     }
   }
   if (pk_cen && nbp > nb) {
-    const int per = (nbp - nb) * D;
-    const int npad = (int)(gridDim.x / (TT * TT)) * per;
-    for (int u = blockIdx.x * 256 + t; u < npad; u += gridDim.x * 256) {
-      const int b2 = u / per, rr = u - b2 * per;
-      const size_t o = ((size_t)b2 * nbp + nb) * D + rr;
+    // sizes in 64 bits: b*h*(nbp - nb)*d can pass 2^31 for large head counts
+    const size_t pad = (size_t)(nbp - nb) * D;
+    const size_t npad = (size_t)(gridDim.x / (TT * TT)) * pad;
+    for (size_t u = (size_t)blockIdx.x * 256 + t; u < npad; u += (size_t)gridDim.x * 256) {
+      const size_t b2 = u / pad, rr = u - b2 * pad;
+      const size_t o = (b2 * nbp + nb) * D + rr;
       pk_cen[o] = (bf16)0.f;
       pk_vsum[o] = (bf16)0.f;
     }
@@ -616,31 +646,31 @@ hipError_t launch_spectral(const float* H, const float* hbar, int bh, int nb, fl
 
 template <int D, int BLK>
 hipError_t stats_bf16_t(const StatsArgs& a) {
-  const int ngrp = (a.nb + kStatsGroup - 1) / kStatsGroup;
+  const int R = stats_ranges<D, BLK>(a.bh, a.nb);
+  const int grid = a.bh * R;
   const int nbp = (a.nb + BLK - 1) / BLK * BLK;
   float* parts = static_cast<float*>(a.ws);
   bf16* pk = static_cast<bf16*>(a.packed);
   bf16* pk_cen = pk;
   bf16* pk_vsum = pk ? pk + (size_t)a.bh * nbp * D : nullptr;
   bf16* pk_hbart = pk ? pk + (size_t)2 * a.bh * nbp * D : nullptr;
-  const int grid = a.bh * ngrp;
-  float* frag = parts + (size_t)a.bh * ngrp * D * D;     // Hbar in pass 2's fragment order
+  float* frag = parts + (size_t)grid * D * D;             // Hbar in pass 2's fragment order
   hipLaunchKernelGGL((stats_bf16_kernel<D, BLK, false, false>), dim3(grid), dim3(256), 0, a.stream,
-                     (const bf16*)a.K, (const bf16*)a.V, a.nb, a.centroid, a.vsum, parts,
+                     (const bf16*)a.K, (const bf16*)a.V, a.nb, R, a.centroid, a.vsum, parts,
                      (const float*)nullptr, (float*)nullptr, (float*)nullptr, pk_cen, pk_vsum,
                      (bf16*)nullptr, a.lens, a.heads);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(hbar_reduce_kernel<D>, dim3(a.bh * (D / 32) * (D / 32)), dim3(256), 0, a.stream,
-                     (const float*)parts, ngrp, a.nb, a.hbar, pk_hbart, pk_cen, pk_vsum, nbp,
+                     (const float*)parts, R, a.nb, a.hbar, pk_hbart, pk_cen, pk_vsum, nbp,
                      a.lens, a.heads, BLK, frag);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   auto pass2 = (a.H || a.ht) ? stats_bf16_kernel<D, BLK, true, true> : stats_bf16_kernel<D, BLK, true, false>;
   hipLaunchKernelGGL(pass2, dim3(grid), dim3(256), 0, a.stream,
-                     (const bf16*)a.K, (const bf16*)a.V, a.nb, (float*)nullptr, (float*)nullptr,
-                     (float*)nullptr, (const float*)frag, a.M, a.H, (bf16*)nullptr,
-                     (bf16*)nullptr, static_cast<bf16*>(a.ht), a.lens, a.heads);
+                     (const bf16*)a.K, (const bf16*)a.V, a.nb, R, (float*)nullptr, (float*)nullptr,
+                     (float*)nullptr, (const float*)frag, a.M, a.H, (bf16*)nullptr, (bf16*)nullptr,
+                     static_cast<bf16*>(a.ht), a.lens, a.heads);
   err = hipGetLastError();
   if (err != hipSuccess || !a.spectral) return err;
   return launch_spectral<D>(a.H, a.hbar, a.bh, a.nb, a.M, a);
@@ -668,10 +698,16 @@ hipError_t stats_f32_t(const StatsArgs& a) {
 
 }  // namespace
 
-size_t stats_workspace_bf16(int bh, int nb, int D) {
-  // per-group partial sums of H_j, then Hbar in pass 2's fragment order
-  const size_t ngrp = (size_t)(nb + kStatsGroup - 1) / kStatsGroup;
-  return (size_t)bh * (ngrp + 1) * D * D * sizeof(float);
+size_t stats_workspace_bf16(int bh, int nb, int D, int BLK) {
+  // one partial sum of H_j per range (b*h*R), then Hbar per head in pass 2's
+  // fragment order
+  int R = 0;
+  if (D == 128 && BLK == 64) R = stats_ranges<128, 64>(bh, nb);
+  else if (D == 128 && BLK == 128) R = stats_ranges<128, 128>(bh, nb);
+  else if (D == 64 && BLK == 64) R = stats_ranges<64, 64>(bh, nb);
+  else if (D == 64 && BLK == 128) R = stats_ranges<64, 128>(bh, nb);
+  else return 0;
+  return (size_t)bh * (R + 1) * D * D * sizeof(float);
 }
 
 size_t stats_packed_bytes(int bh, int nb, int D, int BLK) {

@@ -53,7 +53,8 @@ def test_probe_library_exports_its_declared_symbol():
         assert hasattr(probe, name), name
     # invalid arguments are rejected on the host (hipErrorInvalidValue = 1), nothing launched
     out = ctypes.c_double(0.0)
-    assert probe.pisa_probe_chunk_rate(2, 0, 10, 1, ctypes.byref(out)) == 1
+    assert probe.pisa_probe_chunk_rate(3, 0, 10, 1, ctypes.byref(out)) == 1
+    assert probe.pisa_probe_chunk_rate(-1, 0, 10, 1, ctypes.byref(out)) == 1
     assert probe.pisa_probe_chunk_rate(0, 0, 0, 1, ctypes.byref(out)) == 1
     assert probe.pisa_probe_chunk_rate(0, 0, 10, 1, None) == 1
     assert probe.pisa_probe_read_rate(1 << 20, 1, ctypes.byref(out)) == 1      # below 32 MiB
@@ -101,7 +102,8 @@ def test_precompute_arguments(lib):
     s = shape()
     assert pre(lib, s, out=stats(full=False)) == 1                 # missing centroid
     need = lib.pisa_workspace_size(ctypes.byref(s))
-    assert need == 2 * (16 // 8 + 1) * 128 * 128 * 4              # fp32 d x d: a partial per 8 blocks, Hbar
+    # fp32 d x d per head: one partial per workgroup range (16 blocks in ranges of 4), then Hbar
+    assert need == 2 * (16 // 4 + 1) * 128 * 128 * 4
     assert pre(lib, s, ws=None) == 1
     assert pre(lib, s, wsb=need - 1) == 5
     assert b"needs" in lib.pisa_last_error()

@@ -14,13 +14,15 @@ def test_probe_rates_are_below_the_published_peak():
     torch.cuda.set_device(0)
     probe = _lib.load_probe()
     rates = {}
-    for mix, zeros in ((0, 0), (1, 0), (1, 1)):
+    for mix, zeros in ((0, 0), (1, 0), (1, 1), (2, 0), (2, 1)):
         r = ctypes.c_double(0.0)
         assert probe.pisa_probe_chunk_rate(mix, zeros, 200, 2, ctypes.byref(r)) == 0
         assert math.isfinite(r.value) and 0.0 < r.value < 2500.0 * 1.05, (mix, zeros, r.value)
         rates[(mix, zeros)] = r.value
     # the softmax work can only slow the same MFMAs down (small launches are noisy)
     assert rates[(1, 0)] < 1.1 * rates[(0, 0)]
+    # feeding the MFMAs from LDS can only slow the register-only stream down
+    assert rates[(0, 0)] < 1.1 * rates[(2, 0)]
 
 
 def test_read_probe_is_below_the_published_hbm_peak():
