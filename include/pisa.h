@@ -26,8 +26,11 @@
  * - Supported: head_dim in {64, 128}; block in {64, 128}; nb <= 2048;
  *   batch*heads*nb < 2^31.
  * - Every pointer argument except `stream` is a DEVICE pointer owned by the
- *   caller; the library never allocates, frees or retains device memory and
- *   keeps no global mutable state.  `stream` is a hipStream_t (NULL = the
+ *   caller; the library never allocates or frees device memory.  Its only
+ *   device memory of its own is the static workspace array of
+ *   pisa_precompute_noalloc (one per GPU, from module load until the process
+ *   ends), and its only global state the per-device addresses of that array.
+ *   `stream` is a hipStream_t (NULL = the
  *   legacy default stream).  Calls are asynchronous on that stream: results are
  *   valid once the stream reaches them.
  * - Every call validates its arguments on the host first and returns an error
@@ -138,9 +141,10 @@ const char* pisa_last_error(void);
 
 /* Bytes of device workspace pisa_precompute needs for this shape (0 if the
  * shape is invalid).  The workspace holds deterministic partial sums of H_j:
- * for bf16 inputs one d x d fp32 sum per group of eight blocks plus a copy of
- * Hbar per head in the MFMA fragment order, for fp32 inputs one d x d fp32
- * matrix per block. */
+ * for bf16 inputs one d x d fp32 sum per workgroup range of 4 to 24
+ * consecutive blocks of one head (about one round of workgroups on MI355X)
+ * plus a copy of Hbar per head in the MFMA fragment order, for fp32 inputs
+ * one d x d fp32 matrix per block. */
 size_t pisa_workspace_size(const pisa_shape* shape);
 
 /* Bytes of the optional bf16 statistics pack (pisa_stats.packed) for this
@@ -168,6 +172,29 @@ size_t pisa_packed_size(const pisa_shape* shape);
 pisa_status pisa_precompute(const pisa_shape* shape, const void* K, const void* V,
                             const pisa_stats* out, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * pisa_precompute_noalloc -- pisa_precompute for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels and results (bit for bit), with the
+ * workspace taken from a static device array of the library instead of a
+ * caller buffer.  The call itself allocates nothing.
+ *
+ *   K, V, out  as for pisa_precompute (the caller still owns the inputs and
+ *              every output buffer)
+ *
+ * The static array holds PISA_NOALLOC_SCRATCH_BYTES bytes; each GPU the
+ * library runs on holds its own copy until the process ends.  Shapes whose
+ * pisa_workspace_size() exceeds it return PISA_ERR_WORKSPACE before anything
+ * is launched (use pisa_precompute then).  Run with the device of `stream`
+ * current.  Every call on one GPU uses that GPU's array, so calls that overlap
+ * on one GPU (different streams, or several host threads) race; calls on one
+ * stream are ordered and safe.  Nothing in the array needs clearing between
+ * calls: each call overwrites the part it reads.
+ */
+#define PISA_NOALLOC_SCRATCH_BYTES (64u << 20)
+pisa_status pisa_precompute_noalloc(const pisa_shape* shape, const void* K, const void* V,
+                                    const pisa_stats* out, void* stream);
 
 /*
  * pisa_route -- covariance-aware top-k routing (PISA summary, section 2,

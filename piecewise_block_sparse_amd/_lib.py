@@ -25,7 +25,8 @@ NORM_SPECTRAL = 1
 
 # every symbol the header declares
 EXPORTS = ("pisa_version", "pisa_status_string", "pisa_last_error", "pisa_workspace_size",
-           "pisa_packed_size", "pisa_precompute", "pisa_route", "pisa_attention", "pisa_route_attention")
+           "pisa_packed_size", "pisa_precompute", "pisa_precompute_noalloc", "pisa_route",
+           "pisa_attention", "pisa_route_attention")
 # ... and every symbol include/pisa_probe.h declares (libpisa_probe.so)
 PROBE_EXPORTS = ("pisa_probe_chunk_rate", "pisa_probe_read_rate")
 
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_packed_size.argtypes = [sp]
     lib.pisa_precompute.restype = i32
     lib.pisa_precompute.argtypes = [sp, vp, vp, stp, vp, sz, vp]
+    lib.pisa_precompute_noalloc.restype = i32
+    lib.pisa_precompute_noalloc.argtypes = [sp, vp, vp, stp, vp]
     lib.pisa_route.restype = i32
     lib.pisa_route.argtypes = [sp, vp, vp, vp, i32, ctypes.c_double, ctypes.c_double, vp, vp]
     lib.pisa_attention.restype = i32

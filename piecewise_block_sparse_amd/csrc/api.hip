@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "launch.hpp"
 #include "pisa.h"
@@ -48,6 +49,37 @@ pisa_status check_shape(const pisa_shape* s, int* bh, int* nb) {
     return fail(PISA_ERR_SHAPE, "batch * heads * blocks must stay below 2^31");
   *bh = (int)b;
   *nb = (int)n;
+  return PISA_OK;
+}
+
+// Workspace of pisa_precompute_noalloc: a static device array, one copy per
+// GPU, held until the process ends.  Host code never uses its name as an
+// address: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, called once per device with that device current.
+constexpr size_t kScratchBytes = PISA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];                 // device address of `scratch` per device
+
+// The current device's copy of `scratch` (looked up on the first call there).
+pisa_status scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "pisa_precompute_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PISA_ERR_HIP, "pisa_precompute_noalloc: device %d above the %d the library tracks", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (g != hipSuccess) return hip_status(g, "pisa_precompute_noalloc: hipGetSymbolAddress");
+    if (!p) return fail(PISA_ERR_HIP, "pisa_precompute_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
   return PISA_OK;
 }
 
@@ -114,6 +146,25 @@ pisa_status pisa_precompute(const pisa_shape* shape, const void* K, const void* 
                     spectral ? 1 : 0, bh, nb, shape->head_dim, shape->block, shape->seq_lens,
                     shape->heads, (hipStream_t)stream};
   return hip_status(bf ? pisa::launch_stats_bf16(a) : pisa::launch_stats_f32(a), "pisa_precompute");
+}
+
+pisa_status pisa_precompute_noalloc(const pisa_shape* shape, const void* K, const void* V,
+                                    const pisa_stats* out, void* stream) {
+  g_err[0] = 0;
+  int bh = 0, nb = 0;
+  pisa_status st = check_shape(shape, &bh, &nb);
+  if (st != PISA_OK) return st;
+  if (!K || !V || !out) return fail(PISA_ERR_NULL, "K, V and out are required");
+  const size_t need = pisa_workspace_size(shape);
+  if (need > kScratchBytes)
+    return fail(PISA_ERR_WORKSPACE,
+                "this shape needs %zu bytes of workspace, above the %zu bytes of "
+                "pisa_precompute_noalloc's static scratch: use pisa_precompute with a workspace",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != PISA_OK) return st;
+  return pisa_precompute(shape, K, V, out, ws, kScratchBytes, stream);
 }
 
 pisa_status pisa_route(const pisa_shape* shape, const void* Q, const float* centroid,

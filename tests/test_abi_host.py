@@ -195,3 +195,17 @@ def test_route_attention_arguments(lib):
     assert ra(lib, shape(L=64 * 1856)) == 2
     assert b"pisa_route, then pisa_attention" in lib.pisa_last_error()
     assert ra(lib, shape(L=64 * 896, d=64)) == 2                    # d = 64: nb <= 832
+
+
+def test_noalloc_precompute_refuses_shapes_above_its_scratch(lib):
+    # validation on the host: nothing is launched and no HIP call is made
+    fake = 1 << 40                                                   # never dereferenced
+    big = _lib.PisaShape(1, 24, 32768, 128, 64, _lib.DTYPE_BF16, None)
+    need = lib.pisa_workspace_size(ctypes.byref(big))
+    assert need > 64 << 20
+    st = _lib.PisaStats(fake, fake, None, fake, fake, None, None, 0)
+    assert lib.pisa_precompute_noalloc(ctypes.byref(big), fake, fake, ctypes.byref(st), None) == 5
+    assert b"pisa_precompute with a workspace" in lib.pisa_last_error()
+    assert lib.pisa_precompute_noalloc(ctypes.byref(big), None, fake, ctypes.byref(st), None) == 1
+    bad = _lib.PisaShape(1, 2, 1000, 128, 64, _lib.DTYPE_BF16, None)
+    assert lib.pisa_precompute_noalloc(ctypes.byref(bad), fake, fake, ctypes.byref(st), None) == 2
