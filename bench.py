@@ -17,15 +17,17 @@ after a 512 MB scratch write (caches flushed); `density_sweep` re-routes the sam
 inputs at top-k 128 / 64 / 32 / 16 of 256 blocks and times both modes; `orders`
 times the zeroth-order and the per-block first-order treatments of the
 unselected blocks on the same inputs; `route_attention_fused` times the
-single-launch routing-and-attention call against the two calls it replaces
-(also on the short image-DiT workload, under `secondary`);
+single-launch routing-and-attention call against the two calls it replaces;
+`secondary` holds the other workloads: the small video one (whole steps), the
+short image one (whole steps, dense comparator) and the multimodal one with its
+fixed text/image block mask (PISA and keep-or-drop, dense comparator);
 `roofline.attainable` is the MFMA rate
 the chip sustains for the exact phase's per-chunk instruction mix on random
 operands, and its streaming HBM read rate (libpisa_probe), beside the published
 peaks; `cpu_baseline` is the
 fp64 oracle on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4|3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4|3] [--mode approx|drop]
                     [--no-cpu-baseline] [--no-dense] [--no-sweep] [--no-orders]
                     [--no-cold] [--no-probe] [--copy-calibration]
 """
@@ -60,6 +62,20 @@ def flops(w, k):
     return {"exact": exact, "approx": approx, "attention": exact + approx, "stats": stats,
             "route": route, "step": exact + approx + stats + route,
             "attention_zeroth": exact + zeroth, "attention_first": exact + zeroth + first_blocks}
+
+
+def flops_counts(w, counts):
+    """Algorithmic FLOPs of the attention call for exact-block counts per query
+    block (`counts`: [b, h, nb] valid idx entries), e.g. a fixed block mask."""
+    import numpy as np
+    L, d, B, nb = w.seq_len, w.head_dim, w.block, w.nb
+    c = np.asarray(counts, dtype=np.int64)
+    exact = int(c.sum()) * 4 * B * B * d
+    approx = int(((nb - c) * B * 4 * d).sum()) + c.size * B * 2 * d * d
+    zeroth = int(((nb - c) * B * 4 * d).sum())
+    stats = 2 * w.batch * w.heads * nb * 2 * B * d * d
+    return {"exact": exact, "approx": approx, "attention": exact + approx, "stats": stats,
+            "step": exact + approx + stats, "attention_zeroth": exact + zeroth}
 
 
 def bytes_moved(w):
@@ -203,40 +219,58 @@ def time_route_attention(pisa, torch, Qd, Kd, Vd, st, w, reps):
     return a.elapsed_time(b) / reps
 
 
-def short_sequence(pisa, torch, reps):
-    """The image-DiT workload (24 heads x 4096 tokens, 64-token blocks): routing
-    then attention as two calls, and as the single-launch routing call."""
+def fixed_mask(pisa, torch, steps, warmup):
+    """The multimodal workload (24 heads, 512 text + 4096 image tokens, 64-token
+    blocks) with the fixed text/image block mask as idx (-1 padded rows of 8 to
+    72 exact blocks): whole steps (precompute + attention, no routing), the
+    attention call in PISA and keep-or-drop modes, and the dense comparator."""
+    import numpy as np
     from piecewise_block_sparse_amd import workloads as wl
-    w = wl.WORKLOADS[2]
-    log(f"{w.name}: route + attention against the single-launch call")
+    w = wl.WORKLOADS[5]
+    log(f"{w.name}: fixed-mask steps")
     Q, K, V = wl.make_inputs(w)
     Qd, Kd, Vd = (torch.from_numpy(a).to("cuda", torch.bfloat16) for a in (Q, K, V))
-    st = pisa.precompute(Kd, Vd, w.block)
+    del Q, K, V
+    idx_h = wl.idx_fixed_mask(w)
+    counts = (idx_h >= 0).sum(-1)
+    idx = torch.from_numpy(idx_h).to("cuda")
     stream = torch.cuda.current_stream()
+    ws = torch.empty(pisa.workspace_size(Kd, w.block), dtype=torch.uint8, device="cuda")
 
-    def split():
-        idx = pisa.route(Qd, st, w.k, w.lam, w.block)
-        pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode="approx")
+    def step():
+        st = pisa.precompute(Kd, Vd, w.block, workspace=ws)
+        return st, pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode="approx")
 
-    def fused():
-        pisa.route_attention(Qd, Kd, Vd, st, w.k, w.lam, w.block, mode="approx")
-
-    out = {}
-    for name, fn in (("route_plus_attention_ms", split), ("fused_ms", fused),
-                     ("route_plus_attention_ms_again", split), ("fused_ms_again", fused)):
-        for _ in range(3):
-            fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        b.synchronize()
-        out[name] = a.elapsed_time(b) / reps
-    return {"route_attention_fused": {
-        "ms": min(out["fused_ms"], out["fused_ms_again"]),
-        "route_plus_attention_ms": min(out["route_plus_attention_ms"],
-                                       out["route_plus_attention_ms_again"])}}
+    for _ in range(warmup):
+        st, _ = step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st, _ = step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    f = flops_counts(w, counts)
+    reps = max(5, steps // 2)
+    t_a = time_attention(pisa, torch, Qd, Kd, Vd, idx, st, w, "approx", reps)
+    t_d = time_attention(pisa, torch, Qd, Kd, Vd, idx, st, w, "drop", reps)
+    nb = w.nb
+    dense_idx = torch.arange(nb, dtype=torch.int32, device="cuda").expand(w.batch, w.heads, nb, nb).contiguous()
+    t_dense = time_attention(pisa, torch, Qd, Kd, Vd, dense_idx, st, w, "drop", 3)
+    fd = flops(w, nb)["exact"]
+    res = {"wall_ms_per_step": wall, "step_tflops": f["step"] / wall / 1e9,
+           "exact_blocks_per_row": {"min": int(counts.min()), "max": int(counts.max()),
+                                    "mean": float(counts.mean())},
+           "density": float(counts.sum()) / counts.size / nb,
+           "attention_ms": {"approx": t_a, "drop": t_d},
+           "tflops": {"attention": f["attention"] / t_a / 1e9, "exact_phase": f["exact"] / t_d / 1e9},
+           "roofline_frac": {"attention": f["attention"] / t_a / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+                             "exact_phase": f["exact"] / t_d / 1e9 / MFMA_BF16_PEAK_TFLOPS},
+           "dense": {"ms": t_dense, "tflops": fd / t_dense / 1e9,
+                     "speedup_of_pisa_attention": t_dense / t_a},
+           "gflop": {n: v / 1e9 for n, v in f.items()}}
+    del Qd, Kd, Vd, st, idx, dense_idx, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def time_sdpa(torch, Qd, Kd, Vd, dense_flops, t_pisa):
@@ -260,33 +294,56 @@ def time_sdpa(torch, Qd, Kd, Vd, dense_flops, t_pisa):
     return {"ms": ms, "tflops": dense_flops / ms / 1e9, "speedup_of_pisa_attention": ms / t_pisa}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, budget_s=20.0):
-    """The fp64 oracle on whole heads of the same workload, until ~budget_s."""
+    """The fp64 oracle (as it stands) on whole heads of the same workload, until
+    ~budget_s of oracle time, each of its three calls timed on its own."""
     import numpy as np
     import oracle
     from piecewise_block_sparse_amd import workloads as wl
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        cores = len(os.sched_getaffinity(0))
-    done, spent, fl = 0, 0.0, 0.0
+        blas = None
+    done, fl = 0, 0.0
+    calls = {"precompute": 0.0, "route": 0.0, "attention": 0.0}
     per_head = flops(wl.WORKLOADS[w.wid], w.k)
     for h in range(w.heads):
         Q, K, V = wl.make_inputs(w, heads=[h])
         t0 = time.perf_counter()
         st = oracle.precompute(K, V, w.block)
+        t1 = time.perf_counter()
         idx = oracle.route(Q, st["centroid"], st["M"], w.k, w.lam, w.block, w.scale)
+        t2 = time.perf_counter()
         oracle.attention(Q, K, V, idx, st["centroid"], st["vsum"], st["Hbar"], oracle.MODE_APPROX,
                          w.scale, w.block)
-        spent += time.perf_counter() - t0
+        t3 = time.perf_counter()
+        calls["precompute"] += t1 - t0
+        calls["route"] += t2 - t1
+        calls["attention"] += t3 - t2
         done += 1
         fl += per_head["step"] / w.heads
-        if spent >= budget_s:
+        if sum(calls.values()) >= budget_s:
             break
+    spent = sum(calls.values())
     return {"value": fl / spent / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} of {w.heads} heads, full precompute+route+attention each, "
-                      f"{spent:.1f} s of fp64 numpy",
+            "sample": f"{done} of {w.heads} heads of {w.name}, full precompute+route+attention "
+                      f"each, {spent:.1f} s of fp64 numpy",
+            "cpu_model": cpu_model(), "cores_available": cores, "blas_threads": blas,
+            "seconds_per_call": {n: v / done for n, v in calls.items()},
+            "seconds_per_call_unit": "s per head",
             "seconds_per_step_extrapolated": spent * w.heads / done}
 
 
@@ -326,6 +383,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=4, choices=[3, 4])
+    ap.add_argument("--mode", choices=["approx", "drop"], default="approx",
+                    help="attention mode of the timed step (drop: the exact phase alone, for counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense comparators (all blocks exact; torch SDPA)")
@@ -371,7 +430,8 @@ def main():
         Qd, Kd, Vd = (torch.from_numpy(a).to("cuda", torch.bfloat16) for a in (Q, K, V))
         del Q, K, V
         log(f"{w.name}: timing {steps} steps")
-        wall_ms, ph, (st, idx, _) = timed_phases(pisa, torch, Qd, Kd, Vd, w, w.k, steps, warmup)
+        wall_ms, ph, (st, idx, _) = timed_phases(pisa, torch, Qd, Kd, Vd, w, w.k, steps, warmup,
+                                                 mode=args.mode)
         f, by = flops(w, w.k), bytes_moved(w)
         step_pct = ph.pop("step_event_ms")
         res = {"wall_ms_per_step": wall_ms / steps, "phases_ms": ph, "step_event_ms": step_pct}
@@ -380,13 +440,16 @@ def main():
             res["cold_step_ms"] = cold_steps(pisa, torch, Qd, Kd, Vd, w)
         res["tflops"] = {
             "step": f["step"] / (wall_ms / steps) / 1e9,
-            "attention": f["attention"] / ph["attention"] / 1e9,
+            # keep-or-drop steps (--mode drop) run the exact phase alone
+            "attention": f["exact" if args.mode == "drop" else "attention"] / ph["attention"] / 1e9,
         }
+        res["roofline_frac"] = {"attention": res["tflops"]["attention"] / MFMA_BF16_PEAK_TFLOPS}
         if split:
             t_drop = time_attention(pisa, torch, Qd, Kd, Vd, idx, st, w, "drop", max(5, steps // 2))
             res["exact_phase_ms"] = t_drop
             res["approx_phase_ms"] = ph["attention"] - t_drop
             res["tflops"]["exact_phase"] = f["exact"] / t_drop / 1e9
+            res["roofline_frac"]["exact_phase"] = res["tflops"]["exact_phase"] / MFMA_BF16_PEAK_TFLOPS
             t_fused = time_route_attention(pisa, torch, Qd, Kd, Vd, st, w, max(5, steps // 2))
             res["route_attention_fused"] = {
                 "ms": t_fused, "route_plus_attention_ms": ph["route"] + ph["attention"],
@@ -456,7 +519,7 @@ def main():
     f = flops(w, w.k)
     ms = main_res["wall_ms_per_step"]
     t_attn = main_res["phases_ms"]["attention"]
-    achieved = f["attention"] / t_attn / 1e9
+    achieved = f["exact" if args.mode == "drop" else "attention"] / t_attn / 1e9
     traffic = profiled_traffic(w.name)
     bh = w.batch * w.heads
     min_bytes = 4 * bh * w.seq_len * w.head_dim * 2          # Q, K, V read once, O written once
@@ -475,7 +538,7 @@ def main():
         "data": "synthetic (seeded; smooth latent-grid field + N(0,1) noise)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
                    "head_dim": w.head_dim, "block": w.block, "k": w.k,
-                   "density": w.k / w.nb, "lambda": w.lam, "mode": "approx"},
+                   "density": w.k / w.nb, "lambda": w.lam, "mode": args.mode},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": traffic["total"] if traffic else None,
@@ -500,8 +563,12 @@ def main():
         other = 3 if args.workload == 4 else 4
         _, res2 = run(other, args.steps, max(3, args.warmup), False, cold=not args.no_cold)
         line["secondary"] = {wl.WORKLOADS[other].name: res2}
-        if not args.no_exact_split:
-            line["secondary"][wl.WORKLOADS[2].name] = short_sequence(pisa, torch, max(5, args.steps // 2))
+        # the short image workload (4K tokens): whole steps, the single-launch
+        # routing call against route + attention, and the dense comparator
+        _, res3 = run(2, args.steps, max(3, args.warmup), not args.no_dense, split=not args.no_exact_split,
+                      cold=False)
+        line["secondary"][wl.WORKLOADS[2].name] = res3
+        line["secondary"][wl.WORKLOADS[5].name] = fixed_mask(pisa, torch, args.steps, max(3, args.warmup))
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         line["cpu_baseline"] = cpu_baseline(w)

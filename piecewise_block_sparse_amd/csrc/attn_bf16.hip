@@ -341,21 +341,32 @@ __device__ __forceinline__ void first_order_part(RowState<C::D>& st, const bf16x
   for (int mt = 0; mt < C::MT; ++mt) st.acc[mt] += (mt / MTP == part ? f : 0.f) * hq[mt % MTP];
 }
 
+// The lane's query fragments times f, rounded to bf16: the B operands of the
+// global first-order term, so that term accumulates straight into the output
+// tiles (no temporary tile).
+template <class C>
+__device__ __forceinline__ void scale_frags(bf16x8 (&qf)[C::KS], float f) {
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)((float)qf[ks][e] * f);
+}
+
 // Global first-order term, part PART: the stage holds RP rows (value dims
-// PART * RP ..) of Hbar^T in the K-chunk layout; acc[d] += f * (q Hbar)[d] for
-// those dims, q Hbar as MFMAs (A = Hbar^T rows from LDS, B = query fragments).
+// PART * RP ..) of Hbar^T in the K-chunk layout; acc[d] += (q Hbar)[d] f for
+// those dims as MFMAs into the output tiles (A = Hbar^T rows from LDS, B = the
+// query fragments already scaled by f).
 template <class C, int PART>
-__device__ __forceinline__ void hbar_part(RowState<C::D>& st, const bf16x8 (&qf)[C::KS],
-                                          const char* stage, const Offsets<C>& off, float f) {
+__device__ __forceinline__ void hbar_part(RowState<C::D>& st, const bf16x8 (&fq)[C::KS],
+                                          const char* stage, const Offsets<C>& off) {
   constexpr int MTP = C::RP / 32;                     // 32-row tiles per part
 #pragma unroll
   for (int mtl = 0; mtl < MTP; ++mtl) {
     if constexpr (PART * MTP + MTP <= C::MT) {
-      f32x16 hq = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
-        hq = mfma32(as_bf16x8(ld16(stage + mtl * 32 * C::RB + off.koff[ks])), qf[ks], hq);
-      st.acc[PART * MTP + mtl] += f * hq;
+        st.acc[PART * MTP + mtl] = mfma32(as_bf16x8(ld16(stage + mtl * 32 * C::RB + off.koff[ks])), fq[ks],
+                                          st.acc[PART * MTP + mtl]);
     }
   }
 }
@@ -447,7 +458,10 @@ __device__ __forceinline__ void load_q_frags(bf16x8 (&qf)[C::KS], const bf16* Q,
 // FR: the workgroup routes its own query blocks (pooled query, fp64 scores
 // against every centroid, top-k) instead of reading idx; the selection is the
 // route kernel's, bit for bit.
-template <class C, bool VL, bool FO, bool FR = false>
+// NP: the approximate modes without the bf16 statistics pack: stages 2 and 3
+// convert the fp32 statistics while staging them (an instantiation of its own,
+// so that the other instantiations carry none of its registers).
+template <class C, bool VL, bool FO, bool FR = false, bool NP = false>
 __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, int kmax, int approx,
                                                              int order, float scale, int nb,
                                                              const int32_t* lens, int heads,
@@ -482,7 +496,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   const int nbp = (nb + BLK - 1) / BLK * BLK;
   const bf16* Kh = p.K + (size_t)bh * L * D;
   const bf16* Vh = p.V + (size_t)bh * L * D;
-  const bool packed = approx && p.pk_cen != nullptr;
+  const bool packed = approx && !NP;
+  static_assert(!(NP && FO), "the per-block first order streams the pack");
   // valid tokens: blocks j < nne are non-empty; query block i holds ni queries
   const int Lv = VL ? valid_len(lens, bh, heads, (int)L) : (int)L;
   const int nne = VL ? (Lv + BLK - 1) / BLK : nb;
@@ -826,8 +841,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   if (approx && order == kOrderMixed) {
     // ---- stage 3: global first-order correction, acc += scale * (q Hbar) * sum alpha
     // (sum alpha is complete once stage 2 is done; m does not move from here on)
-    const float atot = row_sum(st.a);
-    const float f = scale * atot;
+    // the query fragments are not read again: scale them by f in place
+    scale_frags<C>(qf, scale * row_sum(st.a));
     if (packed) {
       // the Hbar^T parts (HP <= 2), streamed through the ring behind the
       // centroid chunks; each part owns compile-time accumulator tiles
@@ -835,7 +850,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
         wait_vm0();
         __syncthreads();
         if (t + 1 < ntot) issue(t + 1);
-        if (alive) hbar_part<C, 0>(st, qf, lds + (t & 1) * C::STB, off, f);
+        if (alive) hbar_part<C, 0>(st, qf, lds + (t & 1) * C::STB, off);
         ++t;
       }
       if constexpr (C::HP > 1) {
@@ -843,7 +858,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
           wait_vm0();
           __syncthreads();
           if (t + 1 < ntot) issue(t + 1);
-          if (alive) hbar_part<C, 1>(st, qf, lds + (t & 1) * C::STB, off, f);
+          if (alive) hbar_part<C, 1>(st, qf, lds + (t & 1) * C::STB, off);
           ++t;
         }
       }
@@ -853,11 +868,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       __syncthreads();
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt) {
-        f32x16 hq = f32x16{};
         const char* base = (mt < C::MT / 2) ? lds + 32 * mt * C::RB : lds + C::STB + 32 * (mt - C::MT / 2) * C::RB;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) hq = mfma32(as_bf16x8(ld16(base + off.koff[ks])), qf[ks], hq);
-        st.acc[mt] += f * hq;
+        for (int ks = 0; ks < C::KS; ++ks) st.acc[mt] = mfma32(as_bf16x8(ld16(base + off.koff[ks])), qf[ks], st.acc[mt]);
       }
     }
   }
@@ -903,27 +916,33 @@ hipError_t launch_t(const AttnArgs& a) {
   const RouteIn ri{a.route_k, a.route_scale, a.route_lam};
   const bool fo = a.approx && a.order == kOrderFirst;
   const bool fr = a.route_k > 0;
+  const bool np = a.approx && pk == nullptr;           // approximate modes without the pack
+  const bool vl = a.lens != nullptr;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax, a.approx, a.order,
+                       a.scale, a.nb, a.lens, a.heads, ri);
+    return hipGetLastError();
+  };
   if (fr) {
     if constexpr (FR_) {
       if (fo || !fused_route_fits<C>(a.nb)) return hipErrorInvalidValue;
-      auto kern = a.lens ? attn_bf16_kernel<C, true, false, true> : attn_bf16_kernel<C, false, false, true>;
-      hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax, a.approx, a.order,
-                         a.scale, a.nb, a.lens, a.heads, ri);
+      if (np) return vl ? go(attn_bf16_kernel<C, true, false, true, true>) : go(attn_bf16_kernel<C, false, false, true, true>);
+      return vl ? go(attn_bf16_kernel<C, true, false, true>) : go(attn_bf16_kernel<C, false, false, true>);
     } else {
       return hipErrorInvalidValue;
     }
   } else if constexpr (C::QB == 1) {
-    auto kern = a.lens ? (fo ? attn_bf16_kernel<C, true, true> : attn_bf16_kernel<C, true, false>)
-                       : (fo ? attn_bf16_kernel<C, false, true> : attn_bf16_kernel<C, false, false>);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax, a.approx, a.order,
-                       a.scale, a.nb, a.lens, a.heads, ri);
+    if (fo) {
+      if (np) return hipErrorInvalidValue;      // the per-block first order needs the pack
+      return vl ? go(attn_bf16_kernel<C, true, true>) : go(attn_bf16_kernel<C, false, true>);
+    }
+    if (np) return vl ? go(attn_bf16_kernel<C, true, false, false, true>) : go(attn_bf16_kernel<C, false, false, false, true>);
+    return vl ? go(attn_bf16_kernel<C, true, false>) : go(attn_bf16_kernel<C, false, false>);
   } else {
     if (fo) return hipErrorInvalidValue;        // the launcher sends this order to QB = 1
-    auto kern = a.lens ? attn_bf16_kernel<C, true, false> : attn_bf16_kernel<C, false, false>;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax, a.approx, a.order,
-                       a.scale, a.nb, a.lens, a.heads, ri);
+    if (np) return vl ? go(attn_bf16_kernel<C, true, false, false, true>) : go(attn_bf16_kernel<C, false, false, false, true>);
+    return vl ? go(attn_bf16_kernel<C, true, false>) : go(attn_bf16_kernel<C, false, false>);
   }
-  return hipGetLastError();
 }
 
 }  // namespace
