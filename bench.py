@@ -253,6 +253,27 @@ def fixed_mask(pisa, torch, steps, warmup):
     reps = max(5, steps // 2)
     t_a = time_attention(pisa, torch, Qd, Kd, Vd, idx, st, w, "approx", reps)
     t_d = time_attention(pisa, torch, Qd, Kd, Vd, idx, st, w, "drop", reps)
+    # the text rows' items (72 exact blocks) against the image rows' (about
+    # 16): split items, the extra parts dispatched first (pisa_attention_split)
+    split = {}
+    for cap in (36, 24, 18, 12):
+        wsz = pisa.attention_split_workspace_size(Qd, w.block, idx.shape[-1], cap)
+        wsp = torch.empty(wsz, dtype=torch.uint8, device="cuda")
+        row = {}
+        for mode in ("approx", "drop"):
+            for _ in range(2):
+                pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode=mode, split_blocks=cap, workspace=wsp)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode=mode, split_blocks=cap, workspace=wsp)
+            b.record(stream)
+            b.synchronize()
+            row[mode + "_ms"] = a.elapsed_time(b) / reps
+        row["workspace_mb"] = wsz / 1e6
+        split[str(cap)] = row
+        del wsp
+    best = min(split, key=lambda c: split[c]["approx_ms"])
     nb = w.nb
     dense_idx = torch.arange(nb, dtype=torch.int32, device="cuda").expand(w.batch, w.heads, nb, nb).contiguous()
     t_dense = time_attention(pisa, torch, Qd, Kd, Vd, dense_idx, st, w, "drop", 3)
@@ -265,6 +286,11 @@ def fixed_mask(pisa, torch, steps, warmup):
            "tflops": {"attention": f["attention"] / t_a / 1e9, "exact_phase": f["exact"] / t_d / 1e9},
            "roofline_frac": {"attention": f["attention"] / t_a / 1e9 / MFMA_BF16_PEAK_TFLOPS,
                              "exact_phase": f["exact"] / t_d / 1e9 / MFMA_BF16_PEAK_TFLOPS},
+           "split_items": {"by_max_blocks": split, "best_max_blocks": int(best),
+                           "approx_ms": split[best]["approx_ms"], "drop_ms": split[best]["drop_ms"],
+                           "tflops_attention": f["attention"] / split[best]["approx_ms"] / 1e9,
+                           "tflops_exact_phase": f["exact"] / split[best]["drop_ms"] / 1e9,
+                           "speedup_vs_one_workgroup_per_item": t_a / split[best]["approx_ms"]},
            "dense": {"ms": t_dense, "tflops": fd / t_dense / 1e9,
                      "speedup_of_pisa_attention": t_dense / t_a},
            "gflop": {n: v / 1e9 for n, v in f.items()}}

@@ -48,7 +48,8 @@
 extern "C" {
 #endif
 
-#define PISA_VERSION 101 /* major * 100 + minor; 1.01 adds pisa_route_attention */
+#define PISA_VERSION 102 /* major * 100 + minor; 1.01 adds pisa_route_attention, 1.02
+                            pisa_precompute_noalloc and pisa_attention_split */
 
 typedef enum {
   PISA_OK = 0,
@@ -249,6 +250,44 @@ pisa_status pisa_attention(const pisa_shape* shape, const void* Q, const void* K
                            const void* V, const int32_t* idx, int32_t kmax,
                            const pisa_stats* stats, int32_t mode, float scale, void* O,
                            void* stream);
+
+/*
+ * pisa_attention_split -- pisa_attention with long exact lists split over
+ * several workgroups (bf16).  A fixed block mask can give some query blocks
+ * far more exact blocks than others (the block-sparse notes' multimodal mask,
+ * section 4.2: text rows attend to every block, image rows to a window); one
+ * workgroup per query block would then wait on its heaviest rows.  Here a
+ * work item (the query block, or the pair of neighbouring query blocks, that
+ * one workgroup of pisa_attention takes) whose exact list holds more than
+ * max_blocks blocks runs as up to min(32, ceil(min(nb, 2*kmax) / max_blocks))
+ * parts on separate workgroups, each over a contiguous share of the exact
+ * blocks (the
+ * first part also takes the zeroth-order sweep and the correction); the parts
+ * leave unnormalised softmax states (acc, running max, denominator) in the
+ * workspace and a second kernel merges them:
+ *     o = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,   M = max_p m_p.
+ * The extra parts of all items are dispatched before the first parts, so the
+ * heavy items' parts start first and apart from each other.  The result is
+ * pisa_attention's up to the order of floating-point sums (items that run as
+ * one part give it bit for bit).
+ *
+ *   Q, K, V, idx, kmax, stats, scale, O   as for pisa_attention (bf16 only)
+ *   mode        PISA_MODE_APPROX, PISA_MODE_DROP or PISA_MODE_ZEROTH
+ *   max_blocks  >= 1: most exact blocks of one part
+ *   workspace   device scratch of at least
+ *               pisa_attention_split_workspace_size(shape, kmax, max_blocks)
+ *               bytes, caller-owned; contents on entry are ignored
+ *
+ * Errors as pisa_attention, and PISA_ERR_DTYPE for fp32 inputs, PISA_ERR_ARG
+ * for PISA_MODE_FIRST or max_blocks < 1, PISA_ERR_WORKSPACE for a workspace
+ * that is too small.
+ */
+size_t pisa_attention_split_workspace_size(const pisa_shape* shape, int32_t kmax, int32_t max_blocks);
+pisa_status pisa_attention_split(const pisa_shape* shape, const void* Q, const void* K,
+                                 const void* V, const int32_t* idx, int32_t kmax,
+                                 const pisa_stats* stats, int32_t mode, float scale,
+                                 int32_t max_blocks, void* O, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /*
  * pisa_route_attention -- routing and attention in one kernel (PISA summary,

@@ -25,7 +25,8 @@ import math
 
 from . import _lib
 
-__all__ = ["precompute", "route", "attention", "route_attention", "workspace_size", "version", "MODE_APPROX",
+__all__ = ["precompute", "route", "attention", "route_attention", "workspace_size",
+           "attention_split_workspace_size", "version", "MODE_APPROX",
            "MODE_DROP", "MODE_ZEROTH", "MODE_FIRST"]
 
 MODE_APPROX = _lib.MODE_APPROX
@@ -157,8 +158,13 @@ def route(Q, stats: dict, k: int, lam: float, block: int, scale: float | None = 
 
 
 def attention(Q, K, V, idx, stats: dict | None, block: int, mode: int | str = "approx",
-              scale: float | None = None, out=None, seq_lens=None):
-    """PISA block-sparse attention; mode "approx", "zeroth", "first" or "drop"."""
+              scale: float | None = None, out=None, seq_lens=None, split_blocks: int | None = None,
+              workspace=None):
+    """PISA block-sparse attention; mode "approx", "zeroth", "first" or "drop".
+
+    split_blocks (bf16; not mode "first"): run work items whose exact lists
+    hold more than this many blocks as several workgroups and merge them
+    (pisa_attention_split), with `workspace` (allocated when None)."""
     torch = _torch()
     lib = _lib.load()
     _same(Q, K, V)
@@ -192,10 +198,26 @@ def attention(Q, K, V, idx, stats: dict | None, block: int, mode: int | str = "a
             raise ValueError("stats['packed'] does not match this shape")
         st = _lib.PisaStats(_ptr(stats["centroid"]), _ptr(stats["vsum"]), _ptr(stats.get("H")),
                             _ptr(stats["Hbar"]), None, _ptr(pk), _ptr(stats.get("Ht")))
+    if split_blocks is not None:
+        kmax = int(idx.shape[-1])
+        need = lib.pisa_attention_split_workspace_size(ctypes.byref(shp), kmax, int(split_blocks))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+        _lib.check("pisa_attention_split", lib.pisa_attention_split(
+            ctypes.byref(shp), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), kmax,
+            ctypes.byref(st) if st is not None else None, int(mode), scale, int(split_blocks),
+            _ptr(O), _ptr(workspace), workspace.numel(), _stream(Q)))
+        return O
     _lib.check("pisa_attention", lib.pisa_attention(
         ctypes.byref(shp), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), int(idx.shape[-1]),
         ctypes.byref(st) if st is not None else None, int(mode), scale, _ptr(O), _stream(Q)))
     return O
+
+
+def attention_split_workspace_size(X, block: int, kmax: int, split_blocks: int) -> int:
+    """Bytes of workspace attention(..., split_blocks=...) needs for idx rows of kmax entries."""
+    return _lib.load().pisa_attention_split_workspace_size(ctypes.byref(_shape(X, block)), int(kmax),
+                                                           int(split_blocks))
 
 
 def route_attention(Q, K, V, stats: dict, k: int, lam: float, block: int,

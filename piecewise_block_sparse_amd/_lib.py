@@ -26,7 +26,8 @@ NORM_SPECTRAL = 1
 # every symbol the header declares
 EXPORTS = ("pisa_version", "pisa_status_string", "pisa_last_error", "pisa_workspace_size",
            "pisa_packed_size", "pisa_precompute", "pisa_precompute_noalloc", "pisa_route",
-           "pisa_attention", "pisa_route_attention")
+           "pisa_attention", "pisa_attention_split_workspace_size", "pisa_attention_split",
+           "pisa_route_attention")
 # ... and every symbol include/pisa_probe.h declares (libpisa_probe.so)
 PROBE_EXPORTS = ("pisa_probe_chunk_rate", "pisa_probe_read_rate")
 
@@ -80,6 +81,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pisa_route.argtypes = [sp, vp, vp, vp, i32, ctypes.c_double, ctypes.c_double, vp, vp]
     lib.pisa_attention.restype = i32
     lib.pisa_attention.argtypes = [sp, vp, vp, vp, vp, i32, stp, i32, ctypes.c_float, vp, vp]
+    lib.pisa_attention_split_workspace_size.restype = sz
+    lib.pisa_attention_split_workspace_size.argtypes = [sp, i32, i32]
+    lib.pisa_attention_split.restype = i32
+    lib.pisa_attention_split.argtypes = [sp, vp, vp, vp, vp, i32, stp, i32, ctypes.c_float, i32, vp,
+                                         vp, sz, vp]
     lib.pisa_route_attention.restype = i32
     lib.pisa_route_attention.argtypes = [sp, vp, vp, vp, stp, i32, ctypes.c_double, i32,
                                          ctypes.c_double, vp, vp, vp]

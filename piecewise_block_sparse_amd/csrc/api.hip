@@ -223,6 +223,51 @@ pisa_status pisa_attention(const pisa_shape* shape, const void* Q, const void* K
   return hip_status(bf ? pisa::launch_attn_bf16(a) : pisa::launch_attn_f32(a), "pisa_attention");
 }
 
+size_t pisa_attention_split_workspace_size(const pisa_shape* shape, int32_t kmax, int32_t max_blocks) {
+  int bh = 0, nb = 0;
+  if (check_shape(shape, &bh, &nb) != PISA_OK || shape->dtype != PISA_DTYPE_BF16) return 0;
+  if (kmax < 1 || kmax > nb || max_blocks < 1) return 0;
+  return pisa::attn_split_workspace(shape->head_dim, shape->block, bh, nb, kmax, max_blocks);
+}
+
+pisa_status pisa_attention_split(const pisa_shape* shape, const void* Q, const void* K,
+                                 const void* V, const int32_t* idx, int32_t kmax,
+                                 const pisa_stats* stats, int32_t mode, float scale,
+                                 int32_t max_blocks, void* O, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  int bh = 0, nb = 0;
+  pisa_status st = check_shape(shape, &bh, &nb);
+  if (st != PISA_OK) return st;
+  if (shape->dtype != PISA_DTYPE_BF16)
+    return fail(PISA_ERR_DTYPE, "split work items are built for bf16 inputs");
+  if (!Q || !K || !V || !idx || !O) return fail(PISA_ERR_NULL, "Q, K, V, idx and O are required");
+  if (mode != PISA_MODE_APPROX && mode != PISA_MODE_DROP && mode != PISA_MODE_ZEROTH)
+    return fail(PISA_ERR_ARG, "mode %d: split work items run APPROX, DROP or ZEROTH", mode);
+  if (kmax < 1 || kmax > nb) return fail(PISA_ERR_ARG, "kmax=%d outside [1, %d]", kmax, nb);
+  if (max_blocks < 1) return fail(PISA_ERR_ARG, "max_blocks=%d must be at least 1", max_blocks);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(PISA_ERR_ARG, "scale must be finite and positive");
+  const bool approx = mode != PISA_MODE_DROP;
+  if (approx && (!stats || !stats->centroid || !stats->vsum))
+    return fail(PISA_ERR_NULL, "modes other than DROP need stats centroid and vsum");
+  if (mode == PISA_MODE_APPROX && !stats->Hbar)
+    return fail(PISA_ERR_NULL, "APPROX mode needs stats Hbar");
+  const size_t need = pisa_attention_split_workspace_size(shape, kmax, max_blocks);
+  if (!workspace) return fail(PISA_ERR_NULL, "workspace of %zu bytes is required", need);
+  if (workspace_bytes < need)
+    return fail(PISA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  const int order = mode == PISA_MODE_ZEROTH ? pisa::kOrderZeroth : pisa::kOrderMixed;
+  pisa::AttnArgs a{Q, K, V, idx, kmax,
+                   approx ? stats->centroid : nullptr, approx ? stats->vsum : nullptr,
+                   mode == PISA_MODE_APPROX ? stats->Hbar : nullptr,
+                   approx ? stats->packed : nullptr, nullptr, nullptr,
+                   approx ? 1 : 0, order, scale, O, bh, nb, shape->head_dim, shape->block,
+                   shape->seq_lens, shape->heads, (hipStream_t)stream,
+                   nullptr, 0, 0.0, 0.0, nullptr, max_blocks, workspace};
+  return hip_status(pisa::launch_attn_bf16(a), "pisa_attention_split");
+}
+
 pisa_status pisa_route_attention(const pisa_shape* shape, const void* Q, const void* K,
                                  const void* V, const pisa_stats* stats, int32_t k, double lambda,
                                  int32_t mode, double scale, int32_t* idx, void* O, void* stream) {

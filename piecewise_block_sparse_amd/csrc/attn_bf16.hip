@@ -425,7 +425,27 @@ struct AttnPtrs {
   bf16* O;
   const float* M;        // in-kernel routing: M_j [bh][nb]
   int32_t* idx_out;      // in-kernel routing: the selection written out (nullable)
+  float* part;           // split work items: partial states, one slot per (item, part)
+  int* nparts;           // split work items: parts of each item (written by part 0)
 };
+
+// Split work items: an item (the query block(s) of one workgroup) whose exact
+// list holds more than `cap` blocks runs as up to `pmax` parts on separate
+// workgroups, each over a contiguous share of the exact chunks (part 0 also
+// runs stages 2 and 3).  A part leaves its unnormalised state in a slot:
+// acc [QB*BLK][D] | m [QB*BLK] (log2 units) | l [QB*BLK], all fp32.
+struct SplitIn {
+  int cap;
+  int pmax;
+  int items;
+};
+
+constexpr int kSplitMaxParts = 32;                     // parts per split item, at most
+
+template <class C>
+__host__ __device__ constexpr size_t split_slot_floats() {
+  return ((size_t)C::QB * C::BLK * (C::D + 2) + 63) / 64 * 64;
+}
 
 // In-kernel routing (workgroup-local copy of the route kernel's selection):
 // rk blocks per query block, score = rscale * qbar . kbar_j + rlam * M_j in fp64.
@@ -461,11 +481,16 @@ __device__ __forceinline__ void load_q_frags(bf16x8 (&qf)[C::KS], const bf16* Q,
 // NP: the approximate modes without the bf16 statistics pack: stages 2 and 3
 // convert the fp32 statistics while staging them (an instantiation of its own,
 // so that the other instantiations carry none of its registers).
-template <class C, bool VL, bool FO, bool FR = false, bool NP = false>
+// SP: split work items (see SplitIn).  XCD x (workgroups w with w % 8 == x)
+// owns items x*c .. x*c + c - 1 (c = ceil(items / 8)) and runs, in dispatch
+// order, parts 1 .. pmax - 1 of all of them, then their parts 0: the parts of
+// one item are c workgroups apart (different CUs), the parts that an item does
+// not need exit at once, and the extra parts of heavy items start first.
+template <class C, bool VL, bool FO, bool FR = false, bool NP = false, bool SP = false>
 __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, int kmax, int approx,
                                                              int order, float scale, int nb,
                                                              const int32_t* lens, int heads,
-                                                             RouteIn ri) {
+                                                             RouteIn ri, SplitIn si) {
   constexpr int D = C::D, BLK = C::BLK, CK = C::CK;
   __shared__ __attribute__((aligned(1024))) char lds[C::LDSB];
   constexpr int QB = C::QB;
@@ -484,9 +509,20 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q32 = lane & 31, hh = lane >> 5;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int ngrp = (nb + QB - 1) / QB;                 // workgroups per (batch, head)
-  const int bh = logical / ngrp, i0 = (logical - bh * ngrp) * QB;
+  static_assert(!SP || (!FO && !FR), "split work items run the idx-driven orders other than the per-block first order");
+  const int ngrp = (nb + QB - 1) / QB;                 // items per (batch, head)
+  int item, part = 0;
+  if constexpr (SP) {
+    const int nitems = si.items, c = (nitems + 7) / 8;
+    const int xcd = blockIdx.x & 7, sl = blockIdx.x >> 3;
+    const int grp = sl / c;
+    item = xcd * c + (sl - grp * c);
+    part = (grp + 1) % si.pmax;
+    if (item >= nitems) return;                         // (grid padding)
+  } else {
+    item = xcd_remap(blockIdx.x, gridDim.x);
+  }
+  const int bh = item / ngrp, i0 = (item - bh * ngrp) * QB;
   // this wave: query block i0 + qb, rows 32 wq .. (qb as a scalar, so that
   // branches on the wave's query block are uniform)
   const int qb = __builtin_amdgcn_readfirstlane(w / C::WPQ), wq = w - qb * C::WPQ;
@@ -509,6 +545,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
     nlive += (i0 + q < nb) && (!VL || block_count(Lv, i0 + q, BLK) > 0);
   if (nlive == 0) {
     // query blocks past the sequence: their rows are 0
+    if (SP && part > 0) return;
+    if (SP && tid == 0) p.nparts[item] = 1;
     for (int q = 0; q < QB; ++q) {
       if (i0 + q >= nb) break;
       bf16* ob = p.O + ((size_t)bh * L + (size_t)(i0 + q) * BLK) * D;
@@ -736,9 +774,20 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   }
   __syncthreads();
   const int ncnt = s_cnt[0];
+  // split items: this part's share [ex0, ex0 + nex) of the exact chunks; parts
+  // past the item's count have nothing to do; only part 0 runs stages 2 and 3
+  int nparts = 1, ex0 = 0, nexp = ncnt * SPB;
+  if constexpr (SP) {
+    nparts = min(si.pmax, max(1, (ncnt + si.cap - 1) / si.cap));
+    if (part >= nparts) return;
+    if (part == 0 && tid == 0) p.nparts[item] = nparts;
+    ex0 = (int)((long long)ncnt * SPB * part / nparts);
+    nexp = (int)((long long)ncnt * SPB * (part + 1) / nparts) - ex0;
+  }
+  const bool tail = !SP || part == 0;                  // this workgroup runs stages 2 and 3
   // mixed order with the bf16 pack: Hbar^T streams as HP ring chunks after stage 2
-  const int nhb = (packed && order == kOrderMixed) ? C::HP : 0;
-  const int nex = ncnt * SPB, ncen = nex + s_cnt[1], nhbe = ncen + nhb, ntot = nhbe + s_cnt[2] * C::HP;
+  const int nhb = (tail && packed && order == kOrderMixed) ? C::HP : 0;
+  const int nex = nexp, ncen = nex + (tail ? s_cnt[1] : 0), nhbe = ncen + nhb, ntot = nhbe + s_cnt[2] * C::HP;
   const int ws = __builtin_amdgcn_readfirstlane(w);
   const unsigned lds_m0 = (unsigned)(uintptr_t)(lvoid*)lds;
   const char* Kb = reinterpret_cast<const char*>(Kh);
@@ -751,8 +800,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   auto issue = [&](int t) {
     const unsigned m0 = lds_m0 + (unsigned)((t & 1) * C::STB);
     if (t < nex) {
-      const int j = __builtin_amdgcn_readfirstlane((int)s_list[t / SPB] & kIdMask);
-      const size_t off = ((size_t)j * BLK + (size_t)(t % SPB) * CK) * C::RB;
+      const int u = t + ex0;                              // exact chunk u of the item
+      const int j = __builtin_amdgcn_readfirstlane((int)s_list[u / SPB] & kIdMask);
+      const size_t off = ((size_t)j * BLK + (size_t)(u % SPB) * CK) * C::RB;
       dma_stage<C>(Kb + off, Vb + off, m0, ws, loff);
     } else if (t < ncen) {
       const int tcv = __builtin_amdgcn_readfirstlane((int)s_clist[t - nex]);
@@ -776,11 +826,13 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
     return VL ? min(max(block_count(Lv, (int)s_list[u / SPB] & kIdMask, BLK) - (u % SPB) * CK, 0), CK) : CK;
   };
   int t = 0;
-  // chunk u sits in stage u & 1, passed as `stage`
-  auto exact_step = [&](int u, char* stage) {
+  // stream chunk t sits in stage t & 1, passed as `stage`; it is exact chunk
+  // u = t + ex0 of the item
+  auto exact_step = [&](int t, char* stage) {
     wait_vm0();
     __syncthreads();
-    if (u + 1 < ntot) issue(u + 1);
+    if (t + 1 < ntot) issue(t + 1);
+    const int u = t + ex0;
     const int kv = keys_of(u);
     if (VL && kv < CK) {
       // padding values must not reach the MFMA (0 * NaN): zero those V rows
@@ -824,7 +876,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
     }
   }
 
-  if (approx) {
+  if (approx && tail) {
     if (!packed) {
       // ---- stage 2 from the fp32 statistics (converted while staging)
       const float* cen = p.centroid + (size_t)bh * nb * D;
@@ -838,7 +890,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       }
     }
   }
-  if (approx && order == kOrderMixed) {
+  if (approx && tail && order == kOrderMixed) {
     // ---- stage 3: global first-order correction, acc += scale * (q Hbar) * sum alpha
     // (sum alpha is complete once stage 2 is done; m does not move from here on)
     // the query fragments are not read again: scale them by f in place
@@ -877,6 +929,27 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
 
   // ---- epilogue: o = N / D (0 when nothing was attended in keep-or-drop)
   const float ltot = row_sum(st.l);
+  if constexpr (SP) {
+    if (nparts > 1) {
+      // an unnormalised partial state; the merge kernel forms o
+      if (!qvalid) return;
+      const int row = qb * BLK + 32 * wq + q32;
+      float* slot = p.part + ((size_t)item * si.pmax + part) * split_slot_floats<C>();
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x16& a = st.acc[mt];
+          *reinterpret_cast<f32x4*>(slot + (size_t)row * D + 32 * mt + 8 * g4 + 4 * hh) =
+              f32x4{a[4 * g4], a[4 * g4 + 1], a[4 * g4 + 2], a[4 * g4 + 3]};
+        }
+      if (hh == 0) {
+        slot[(size_t)QB * BLK * D + row] = st.m;
+        slot[(size_t)QB * BLK * D + QB * BLK + row] = ltot;
+      }
+      return;
+    }
+  }
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   if (!qvalid) return;                                  // (odd nb: no second query block)
   const bool live = 32 * wq + q32 < ni;                 // padding query rows are written 0
@@ -892,6 +965,63 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
     }
 }
 
+// Split items: o = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p over the
+// item's parts (M = max_p m_p; the states of different parts are relative to
+// their own running maxima), 0 where the weights sum to 0 (keep-or-drop with
+// nothing attended) and for padding queries.  One workgroup per item; items
+// that ran as one part were written by the attention kernel.
+template <class C, bool VL>
+__global__ __launch_bounds__(256) void split_merge_kernel(const float* __restrict__ part,
+                                                          const int* __restrict__ nparts, int pmax,
+                                                          bf16* __restrict__ O, int nb,
+                                                          const int32_t* __restrict__ lens, int heads) {
+  constexpr int D = C::D, BLK = C::BLK, QB = C::QB, R = QB * BLK;
+  constexpr size_t SF = split_slot_floats<C>();
+  __shared__ float s_w[kSplitMaxParts][R];             // per part and row: 2^(m_p - M) / den
+  const int item = blockIdx.x;
+  const int np = nparts[item];
+  if (np <= 1) return;
+  const int ngrp = (nb + QB - 1) / QB;
+  const int bh = item / ngrp, i0 = (item - bh * ngrp) * QB;
+  const size_t L = (size_t)nb * BLK;
+  const int Lv = VL ? valid_len(lens, bh, heads, (int)L) : (int)L;
+  const float* base = part + (size_t)item * pmax * SF;
+  // the rows' weights, once
+  for (int row = threadIdx.x; row < R; row += 256) {
+    const int q = row / BLK, tok = (i0 + q) * BLK + (row - q * BLK);
+    float mx = -INFINITY;
+    for (int pp = 0; pp < np; ++pp) mx = fmaxf(mx, base[pp * SF + (size_t)R * D + row]);
+    float den = 0.f;
+    for (int pp = 0; pp < np; ++pp) {
+      const float wgt = fast_exp2(base[pp * SF + (size_t)R * D + row] - mx);
+      s_w[pp][row] = wgt;
+      den += wgt * base[pp * SF + (size_t)R * D + R + row];
+    }
+    const float inv = (i0 + q < nb && tok < Lv && den > 0.f) ? 1.f / den : 0.f;
+    for (int pp = 0; pp < np; ++pp) s_w[pp][row] *= inv;
+  }
+  __syncthreads();
+  // o = sum_p w_p acc_p, 16 bytes per thread and step, parts four loads at a time
+  for (int e = threadIdx.x; e < R * D / 4; e += 256) {
+    const int row = e / (D / 4), c = 4 * (e - row * (D / 4));
+    const int q = row / BLK;
+    if (i0 + q >= nb) continue;                         // (odd nb: no second query block)
+    const float* a0 = base + (size_t)row * D + c;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    int pp = 0;
+    for (; pp + 4 <= np; pp += 4) {
+      f32x4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const f32x4*>(a0 + (pp + u) * SF);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) num += s_w[pp + u][row] * x[u];
+    }
+    for (; pp < np; ++pp) num += s_w[pp][row] * *reinterpret_cast<const f32x4*>(a0 + pp * SF);
+    const u32x2 pk = {pack2(num[0], num[1]), pack2(num[2], num[3])};
+    st8(O + ((size_t)bh * L + (size_t)(i0 + q) * BLK + (row - q * BLK)) * D + c, pk);
+  }
+}
+
 // In-kernel routing keeps the pooled queries, the score rows and the select
 // histograms in the ring's LDS.
 template <class C>
@@ -904,25 +1034,59 @@ constexpr bool fused_route_fits(int nb) {
 
 // FR_: this configuration also serves in-kernel routing (the ones the
 // per-block first order alone uses do not)
+// parts per split item and workspace bytes (nparts array, then the slots)
+template <class C>
+int split_pmax(int nb, int kmax, int cap) {
+  const int most = min(nb, C::QB * kmax);               // exact blocks an item can hold
+  return cap > 0 ? min(kSplitMaxParts, max(1, (most + cap - 1) / cap)) : 1;
+}
+template <class C>
+size_t split_ws_bytes(int bh, int nb, int kmax, int cap) {
+  const size_t items = (size_t)bh * ((nb + C::QB - 1) / C::QB);
+  return (items * sizeof(int) + 255) / 256 * 256 +
+         items * split_pmax<C>(nb, kmax, cap) * split_slot_floats<C>() * sizeof(float);
+}
+
 template <class C, bool FR_ = true>
 hipError_t launch_t(const AttnArgs& a) {
-  const int grid = a.bh * ((a.nb + C::QB - 1) / C::QB);
+  const int items = a.bh * ((a.nb + C::QB - 1) / C::QB);
   const int nbp = (a.nb + C::BLK - 1) / C::BLK * C::BLK;
   const bf16* pk = static_cast<const bf16*>(a.packed);
   AttnPtrs p{(const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.idx, a.centroid, a.vsum,
              a.hbar, pk, pk ? pk + (size_t)a.bh * nbp * C::D : nullptr,
              pk ? pk + (size_t)2 * a.bh * nbp * C::D : nullptr, (const bf16*)a.ht, (bf16*)a.O,
-             a.M, a.idx_out};
+             a.M, a.idx_out, nullptr, nullptr};
   const RouteIn ri{a.route_k, a.route_scale, a.route_lam};
   const bool fo = a.approx && a.order == kOrderFirst;
   const bool fr = a.route_k > 0;
   const bool np = a.approx && pk == nullptr;           // approximate modes without the pack
   const bool vl = a.lens != nullptr;
+  SplitIn si{0, 1, items};
+  int grid = items;
+  if (a.split_cap > 0) {
+    if (fo || fr) return hipErrorInvalidValue;
+    si = SplitIn{a.split_cap, split_pmax<C>(a.nb, a.kmax, a.split_cap), items};
+    grid = (items + 7) / 8 * 8 * si.pmax;
+    p.nparts = static_cast<int*>(a.split_ws);
+    p.part = reinterpret_cast<float*>(static_cast<char*>(a.split_ws) +
+                                      ((size_t)items * sizeof(int) + 255) / 256 * 256);
+  }
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), 0, a.stream, p, a.kmax, a.approx, a.order,
-                       a.scale, a.nb, a.lens, a.heads, ri);
+                       a.scale, a.nb, a.lens, a.heads, ri, si);
     return hipGetLastError();
   };
+  if (a.split_cap > 0) {
+    if constexpr (!FR_) return hipErrorInvalidValue;   // (configurations of the per-block first order)
+    hipError_t e;
+    if (np) e = vl ? go(attn_bf16_kernel<C, true, false, false, true, true>) : go(attn_bf16_kernel<C, false, false, false, true, true>);
+    else e = vl ? go(attn_bf16_kernel<C, true, false, false, false, true>) : go(attn_bf16_kernel<C, false, false, false, false, true>);
+    if (e != hipSuccess || si.pmax == 1) return e;
+    auto merge = vl ? split_merge_kernel<C, true> : split_merge_kernel<C, false>;
+    hipLaunchKernelGGL(merge, dim3(items), dim3(256), 0, a.stream, (const float*)p.part,
+                       (const int*)p.nparts, si.pmax, (bf16*)a.O, a.nb, a.lens, a.heads);
+    return hipGetLastError();
+  }
   if (fr) {
     if constexpr (FR_) {
       if (fo || !fused_route_fits<C>(a.nb)) return hipErrorInvalidValue;
@@ -958,6 +1122,15 @@ int fused_route_max_blocks(int D, int BLK) {
     if (ok) best = nb;
   }
   return best;
+}
+
+size_t attn_split_workspace(int D, int BLK, int bh, int nb, int kmax, int cap) {
+  // the configurations launch_attn_bf16 picks for the orders other than the per-block first
+  if (D == 128 && BLK == 64) return split_ws_bytes<Cfg<128, 64, 32, 2>>(bh, nb, kmax, cap);
+  if (D == 128 && BLK == 128) return split_ws_bytes<Cfg<128, 128, 32>>(bh, nb, kmax, cap);
+  if (D == 64 && BLK == 64) return split_ws_bytes<Cfg<64, 64, 32, 2>>(bh, nb, kmax, cap);
+  if (D == 64 && BLK == 128) return split_ws_bytes<Cfg<64, 128, 64>>(bh, nb, kmax, cap);
+  return 0;
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a) {

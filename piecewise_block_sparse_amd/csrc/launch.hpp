@@ -37,6 +37,10 @@ struct AttnArgs {
   double route_scale;
   double route_lam;
   int32_t* idx_out;     // nullable
+  // split work items (bf16): cap > 0 runs an item whose exact list holds more
+  // than cap blocks as several parts and merges them (split_ws: workspace)
+  int split_cap;
+  void* split_ws;
 };
 
 struct StatsArgs {
@@ -90,6 +94,8 @@ size_t stats_workspace_f32(int bh, int nb, int D);
 size_t stats_packed_bytes(int bh, int nb, int D, int BLK);
 
 hipError_t launch_attn_bf16(const AttnArgs& a);
+// workspace bytes of a split attention launch (bf16)
+size_t attn_split_workspace(int D, int BLK, int bh, int nb, int kmax, int cap);
 // largest nb whose in-kernel routing fits the attention kernel's LDS (bf16)
 int fused_route_max_blocks(int D, int BLK);
 hipError_t launch_attn_f32(const AttnArgs& a);

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.pisa_version() == 101
+    assert lib.pisa_version() == 102
 
 
 def test_probe_library_exports_its_declared_symbol():
@@ -209,3 +209,25 @@ def test_noalloc_precompute_refuses_shapes_above_its_scratch(lib):
     assert lib.pisa_precompute_noalloc(ctypes.byref(big), None, fake, ctypes.byref(st), None) == 1
     bad = _lib.PisaShape(1, 2, 1000, 128, 64, _lib.DTYPE_BF16, None)
     assert lib.pisa_precompute_noalloc(ctypes.byref(bad), fake, fake, ctypes.byref(st), None) == 2
+
+
+def test_split_attention_arguments(lib):
+    s = shape()                                                     # nb = 16, 64-token blocks
+    fake = 1 << 40                                                  # never dereferenced
+    need = lib.pisa_attention_split_workspace_size(ctypes.byref(s), 8, 3)
+    # pairs of query blocks: 8 items per head, 2 heads; an item holds up to
+    # min(nb, 2 kmax) = 16 blocks, so up to 6 parts of 3; a part's slot is
+    # 128 rows x (128 + 2) fp32; the parts-per-item array takes 256 bytes
+    assert need == 256 + 2 * 8 * 6 * 128 * 130 * 4
+    assert lib.pisa_attention_split_workspace_size(ctypes.byref(s), 8, 0) == 0
+    assert lib.pisa_attention_split_workspace_size(ctypes.byref(s), 17, 3) == 0
+    f = shape(dtype=_lib.DTYPE_FP32)
+    assert lib.pisa_attention_split_workspace_size(ctypes.byref(f), 8, 3) == 0
+    call = lambda shp=s, mode=1, maxb=3, ws=fake, wsb=need: lib.pisa_attention_split(
+        ctypes.byref(shp), fake, fake, fake, fake, 8, None, mode, 0.125, maxb, fake, ws, wsb, None)
+    assert call(wsb=need - 1) == 5
+    assert call(ws=None) == 1
+    assert call(maxb=0) == 3
+    assert call(mode=3) == 3                                        # the per-block first order
+    assert call(mode=0) == 1                                        # APPROX needs the statistics
+    assert call(shp=f) == 4
