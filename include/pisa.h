@@ -226,9 +226,10 @@ pisa_status pisa_route(const pisa_shape* shape, const void* Q, const float* cent
  *
  *   Q, K, V   [b,h,L,d] of shape->dtype (device)
  *   idx       int32 [b,h,nb,kmax]: block ids of S_i; entries < 0 are padding
- *             and are skipped wherever they appear.  Ids must be distinct and
- *             < nb (ids >= nb are skipped, duplicates are counted twice; no
- *             fault either way).  Rows may be fully padded (S_i empty).
+ *             and are skipped wherever they appear, ids >= nb are skipped, and
+ *             an id repeated in a row counts once (S_i is a set).  The exact
+ *             blocks are attended in ascending block order, whatever the order
+ *             of the row.  Rows may be fully padded (S_i empty).
  *   kmax      row length of idx, 1 <= kmax <= nb
  *   stats     centroid, vsum, Hbar (and packed, when non-NULL) read in APPROX;
  *             centroid, vsum (and packed) in ZEROTH; centroid, vsum, packed and Ht

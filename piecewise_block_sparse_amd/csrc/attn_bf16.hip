@@ -498,7 +498,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   __shared__ unsigned bits[QB][kBitWords];
   static_assert(!(FR && FO), "in-kernel routing runs with the other orders");
   static_assert(!FR || QB * BLK * C::RB <= C::LDSB, "in-kernel routing stages the query rows in the ring");
-  __shared__ unsigned exb[QB == 2 ? 2 : 1][(QB == 2 || FR) ? kBitWords : 1];   // exact blocks
+  __shared__ unsigned exb[QB][kBitWords];               // exact blocks (a set: duplicates count once)
   __shared__ short s_list[kMaxBlocks];                 // exact block ids of S_i, in order;
                                                        // then (per-block first order) U_i.
                                                        // Pairs: the union, ascending, with
@@ -663,9 +663,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       for (int q = 0; q < QB; ++q) bits[q][e] |= exb[q][e];
     __syncthreads();
   }
-  if (!FR && (approx || QB == 2)) {
+  if (!FR) {
     // bits[q]: bit j set when block j is exact for query block i0 + q (in its
-    // S_i) or padding (j >= nne); exb[q] (pairs): the exact blocks alone
+    // S_i) or padding (j >= nne); exb[q]: the exact blocks alone
     for (int e = tid; e < nbp / 32; e += C::NT) {
       const int lo = 32 * e;
       unsigned pad = 0u;                                 // padding and empty blocks: j >= nne
@@ -673,7 +673,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
 #pragma unroll
       for (int q = 0; q < QB; ++q) {
         bits[q][e] = pad;
-        if constexpr (QB == 2) exb[q][e] = 0u;
+        exb[q][e] = 0u;
       }
     }
     __syncthreads();
@@ -685,7 +685,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
         const int j = rq[e];
         if (j >= 0 && j < nne) {
           atomicOr(&bits[q][j >> 5], 1u << (j & 31));
-          if constexpr (QB == 2) atomicOr(&exb[q][j >> 5], 1u << (j & 31));
+          atomicOr(&exb[q][j >> 5], 1u << (j & 31));
         }
       }
     }
@@ -712,18 +712,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   const int nctile = packed ? nbp / CK : 0;
   if (w == 0) {
     int cnt = 0;
-    if constexpr (QB == 1 && !FR) {
-      const int32_t* row = p.idx + ((size_t)bh * nb + i) * kmax;
-      for (int e0 = 0; e0 < kmax; e0 += 64) {
-        const int e = e0 + lane;
-        const int j = (e < kmax) ? row[e] : -1;
-        const bool ok = j >= 0 && j < nne;
-        const unsigned long long m = __ballot(ok);
-        if (ok) s_list[cnt + __popcll(m & ((1ull << lane) - 1))] = (short)j;
-        cnt += __popcll(m);
-      }
-    } else {
-      // the union of the two rows, ascending (lane = bitmap word: nbp <= 2048)
+    {
+      // the exact blocks (pairs: the union of the two rows), ascending, from
+      // the bitmaps (lane = bitmap word: nbp <= 2048)
       const unsigned a = (lane < nbp / 32) ? exb[0][lane] : 0u;
       const unsigned b = (QB == 2 && lane < nbp / 32) ? exb[QB - 1][lane] : 0u;
       const unsigned u = a | b;

@@ -42,6 +42,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
     const int j = row[e];
     if (j >= 0 && j < nne) atomicOr(&bits[j >> 5], 1u << (j & 31));
   }
+  __syncthreads();
 
   float q[D], acc[D];
   const float* qrow = Q + ((size_t)bh * L + (size_t)i * BLK + tid) * D;
@@ -100,10 +101,10 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
     }
   };
 
-  // stage 1: exact keys of the selected blocks
-  for (int e = 0; e < kmax; ++e) {
-    const int j = row[e];
-    if (j < 0 || j >= nne) continue;
+  // stage 1: exact keys of the selected blocks, ascending, each once (S_i is
+  // a set: an id repeated in the idx row counts once)
+  for (int j = 0; j < nne; ++j) {
+    if (!((bits[j >> 5] >> (j & 31)) & 1u)) continue;
     const int nj = block_count(Lv, j, BLK);
     for (int n0 = 0; n0 < BLK; n0 += CH) {
       const int nv = min(max(nj - n0, 0), CH);       // keys of this chunk inside the sequence

@@ -629,3 +629,37 @@ def test_route_exact_ties_go_to_lower_ids(torch, nb, k):
     idx = pisa.route(to_dev(Q, "bf16"), st, k, 1.0, B)
     ref = oracle.route(Q, cen, M, k, 1.0, B, 1 / math.sqrt(d))
     assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("dtype,d,B", [("bf16", 128, 64), ("bf16", 128, 128), ("bf16", 64, 128),
+                                       ("fp32", 128, 64)])
+def test_duplicate_ids_count_once(torch, dtype, d, B):
+    """S_i is a set: an id repeated in an idx row (in any order) gives the
+    result of the row without the repeat, bit for bit, on every path (64-token
+    pairs, 128-token blocks, fp32), and matches the oracle on the clean rows."""
+    pisa = pisa_mod()
+    nb = 10
+    L = nb * B
+    Q, K, V = (_rand(torch, (1, 2, L, d), dtype, s) for s in (61, 62, 63))
+    Qd, Kd, Vd = (to_dev(x, dtype) for x in (Q, K, V))
+    g = np.random.default_rng(64)
+    clean = np.full((1, 2, nb, 6), -1, dtype=np.int32)
+    dup = np.full((1, 2, nb, 6), -1, dtype=np.int32)
+    for hi in range(2):
+        for i in range(nb):
+            n = int(g.integers(1, 5))
+            ids = np.sort(g.choice(nb, n, replace=False))
+            clean[0, hi, i, :n] = ids
+            row = np.concatenate([ids, ids[:1], ids[-1:]])[::-1]       # repeats, descending
+            dup[0, hi, i, :len(row)] = row
+    st = pisa.precompute(Kd, Vd, B, store_H=True)
+    ref_st = oracle.precompute(K, V, B)
+    scale = 1 / math.sqrt(d)
+    for m, code in (("approx", oracle.MODE_APPROX), ("drop", oracle.MODE_DROP)):
+        a = pisa.attention(Qd, Kd, Vd, torch.from_numpy(dup).cuda(), st, B, mode=m)
+        b = pisa.attention(Qd, Kd, Vd, torch.from_numpy(clean).cuda(), st, B, mode=m)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), (dtype, d, B, m)
+        ref = oracle.attention(Q, K, V, clean, ref_st["centroid"], ref_st["vsum"], ref_st["Hbar"],
+                               code, scale, B)
+        check_attention(to_np(a), ref, dtype, name=f"duplicates/{dtype}/{B}/{m}")
