@@ -558,6 +558,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   }
   const bool alive = ni > 0;                           // wave-uniform
   const bool first = FO && approx && order == kOrderFirst && packed && p.ht != nullptr;
+  // this lane's query row as 16-byte B-operand fragments (d = 16 ks + 8 hh + 0..7);
+  // with in-kernel routing they are loaded first, as the pooling reads them too
+  bf16x8 qf[C::KS];
+  if constexpr (FR) load_q_frags<C, VL>(qf, p.Q, bh, L, qvalid ? i : i0, wq, q32, hh, ni);
 
   if constexpr (FR) {
     // ---- in-kernel routing.  LDS (the ring, idle until the chunk stream
@@ -584,14 +588,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
     // query rows, already in registers as MFMA fragments (padding queries are
     // zero rows), are staged row-major in the ring; the waves of each query
     // block then sum its columns with 16-byte LDS reads and times 1 / ni below.
-    {
-      bf16x8 qt[C::KS];                                  // (loaded again from L2 below)
-      load_q_frags<C, VL>(qt, p.Q, bh, L, qvalid ? i : i0, wq, q32, hh, ni);
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        st16(lds + (size_t)(qb * BLK + 32 * wq + q32) * C::RB + 32 * ks + 16 * hh,
-             __builtin_bit_cast(u32x4, qt[ks]));
-    }
+    for (int ks = 0; ks < C::KS; ++ks)
+      st16(lds + (size_t)(qb * BLK + 32 * wq + q32) * C::RB + 32 * ks + 16 * hh,
+           __builtin_bit_cast(u32x4, qf[ks]));
     __syncthreads();
     {
       constexpr int CPR = D / 8, TPQ = 64 * C::WPQ, RPI = TPQ / CPR, NR = BLK / RPI;
@@ -633,16 +633,37 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
         double acc[QB];
 #pragma unroll
         for (int q = 0; q < QB; ++q) acc[q] = 0.0;
-#pragma unroll 4
-        for (int a = 0; a < D; a += 4) {
-          const f32x4 kv = *reinterpret_cast<const f32x4*>(cj + a);
+        if constexpr (QB == 2) {
+          // the centroid row in batches of eight 16-byte loads in flight (with
+          // one query block per workgroup the same batches make the compiler
+          // spill the main loop, so that case reads four at a time)
+          for (int a0 = 0; a0 < D; a0 += 32) {
+            f32x4 kv[8];
 #pragma unroll
-          for (int q = 0; q < QB; ++q) {
-            const double* qq = s_qbar + q * D + a;
-            acc[q] = fma(qq[0], (double)kv[0], acc[q]);
-            acc[q] = fma(qq[1], (double)kv[1], acc[q]);
-            acc[q] = fma(qq[2], (double)kv[2], acc[q]);
-            acc[q] = fma(qq[3], (double)kv[3], acc[q]);
+            for (int u = 0; u < 8; ++u) kv[u] = *reinterpret_cast<const f32x4*>(cj + a0 + 4 * u);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+              for (int q = 0; q < QB; ++q) {
+                const double* qq = s_qbar + q * D + a0 + 4 * u;
+                acc[q] = fma(qq[0], (double)kv[u][0], acc[q]);
+                acc[q] = fma(qq[1], (double)kv[u][1], acc[q]);
+                acc[q] = fma(qq[2], (double)kv[u][2], acc[q]);
+                acc[q] = fma(qq[3], (double)kv[u][3], acc[q]);
+              }
+          }
+        } else {
+#pragma unroll 4
+          for (int a = 0; a < D; a += 4) {
+            const f32x4 kv = *reinterpret_cast<const f32x4*>(cj + a);
+#pragma unroll
+            for (int q = 0; q < QB; ++q) {
+              const double* qq = s_qbar + q * D + a;
+              acc[q] = fma(qq[0], (double)kv[0], acc[q]);
+              acc[q] = fma(qq[1], (double)kv[1], acc[q]);
+              acc[q] = fma(qq[2], (double)kv[2], acc[q]);
+              acc[q] = fma(qq[3], (double)kv[3], acc[q]);
+            }
           }
         }
         const double mj = ri.rlam * (double)Mh[j];
@@ -693,8 +714,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   }
 
   // this lane's query row as 16-byte B-operand fragments (d = 16 ks + 8 hh + 0..7)
-  bf16x8 qf[C::KS];
-  load_q_frags<C, VL>(qf, p.Q, bh, L, qvalid ? i : i0, wq, q32, hh, ni);
+  if constexpr (!FR) load_q_frags<C, VL>(qf, p.Q, bh, L, qvalid ? i : i0, wq, q32, hh, ni);
   const Offsets<C> off = make_offsets<C>(lane);
   const DmaOff<C> loff = dma_lane_offsets<C>(w, lane);
   RowState<D> st;
