@@ -33,17 +33,18 @@ struct SCfg {
   static constexpr int NSL = CK / 16;                 // 16-token MFMA k-steps per chunk
   static constexpr int RB = 2 * D, CPR = D / 8, SUBB = CK * RB, STB = 2 * SUBB;
   static constexpr int NDMA = STB / 1024, DPW = NDMA / NW, RPD = 1024 / RB;
-  // ring stages: 64-token blocks end every two chunks, and run best at three
-  // workgroups per CU (three 16 KB stages each at d = 128); 128-token blocks
-  // at two workgroups per CU with four stages
-  static constexpr int NS = (BLK == 64) ? 3 : 4;
+  // ring stages: four 16 KB stages (d = 128) at two workgroups per CU, for
+  // both block sizes (64-token blocks measured 15% faster this way than at
+  // three workgroups per CU with three stages and 8-block ranges: the longer
+  // ranges halve the pass-1 partial sums written and re-read)
+  static constexpr int NS = 4;
   static constexpr int TM = (D == 128) ? 2 : 1;       // 32x32 output tiles per wave, per dim
   // blocks per workgroup range: at most PMAX (the pass-1 register window of
   // per-block outputs), at least PMIN, else enough for one round of GT
-  // workgroups (two or three per CU on 256 CUs)
-  static constexpr int PMAX = (BLK == 128) ? 24 : 8;
+  // workgroups (two per CU on 256 CUs)
+  static constexpr int PMAX = 24;
   static constexpr int PMIN = 4;
-  static constexpr int GT = (BLK == 64) ? 768 : 512;
+  static constexpr int GT = 512;
   static_assert(BLK % CK == 0 && NDMA % NW == 0 && DPW % 2 == 0, "chunking");
 };
 
@@ -90,7 +91,7 @@ __device__ __forceinline__ float frag_sum(const u32x4& f, float acc) {
 // sums give kbar_j and sigma_j, and H_j = K_j^T V_j - kbar_j^T sigma_j.
 // STORE: pass 2 also writes the optional H_j (fp32) and H_j^T (bf16) outputs.
 template <int D, int BLK, bool PASS2, bool STORE>
-__global__ __launch_bounds__(256, (PASS2 && STORE) ? 2 : (BLK == 64 ? 3 : 2)) void stats_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void stats_bf16_kernel(
     const bf16* __restrict__ K, const bf16* __restrict__ V, int nb, int R,
     float* __restrict__ centroid, float* __restrict__ vsum, float* __restrict__ partial,
     const float* __restrict__ hbar_frag, float* __restrict__ M, float* __restrict__ Hout,

@@ -200,7 +200,7 @@ def test_route_attention_arguments(lib):
 def test_noalloc_precompute_refuses_shapes_above_its_scratch(lib):
     # validation on the host: nothing is launched and no HIP call is made
     fake = 1 << 40                                                   # never dereferenced
-    big = _lib.PisaShape(1, 24, 32768, 128, 64, _lib.DTYPE_BF16, None)
+    big = _lib.PisaShape(1, 48, 32768, 128, 64, _lib.DTYPE_BF16, None)
     need = lib.pisa_workspace_size(ctypes.byref(big))
     assert need > 64 << 20
     st = _lib.PisaStats(fake, fake, None, fake, fake, None, None, 0)
