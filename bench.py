@@ -87,25 +87,78 @@ def bytes_moved(w):
     return {"stats": 2 * kv + stats_out, "route": bh * L * d * e + bh * nb * (d + 1) * 4}
 
 
-def profiled_traffic(workload_name):
-    """HBM bytes per launch of the attention kernel from the committed rocprofv3
-    summary (FETCH_SIZE and WRITE_SIZE passes, copy-calibrated), or None when the
-    kernel source changed after the counters were taken."""
+def _source_stamp(files):
     import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        path = os.path.join(ROOT, "piecewise_block_sparse_amd", "csrc", f)
+        if not os.path.exists(path):
+            return None                   # matches no stamp
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
+
+
+# the sources each stamped counter line of a profile covers
+_ATTN_SOURCES = ("attn_bf16.hip", "lds_stream.hpp", "common.hpp", "topk.hpp")
+_STATS_SOURCES = ("stats.hip", "lds_stream.hpp", "common.hpp")
+
+
+def profiled_counters(workload_name):
+    """Counter figures from the committed rocprofv3 summary of a workload:
+    `traffic` (HBM bytes per attention launch, FETCH_SIZE and WRITE_SIZE passes,
+    copy-calibrated), `exact_phase` (the keep-or-drop call: MFMA GFLOP, busy
+    fraction, co-execution, clock), `approx_phase` (APPROX call minus DROP call)
+    and `statistics` (the three precompute kernels).  A line whose kernel source
+    changed after the counters were taken is left out (its `source` stamp no
+    longer matches), so stale counters are never reported."""
     import re
     path = os.path.join(ROOT, "profiles", f"kernels_{workload_name}.md")
     if not os.path.exists(path):
+        return {}
+    text = open(path).read()
+    stamps = {"attn": _source_stamp(_ATTN_SOURCES), "stats": _source_stamp(_STATS_SOURCES)}
+    out = {}
+    for key, tag, which in (("traffic", "attn_bf16_kernel", "attn"), ("exact_phase", "exact_phase", "attn"),
+                            ("approx_phase", "approx_phase", "attn"), ("statistics", "statistics", "stats")):
+        m = re.search(rf"^{tag} ((?:\w+=[0-9.e+-]+ )+)source=([0-9a-f]+)$", text, re.M)
+        if not m or m.group(2) != stamps[which]:
+            continue
+        vals = {}
+        for kv in m.group(1).split():
+            k, v = kv.split("=")
+            vals[k] = float(v) if any(c in v for c in ".e") else int(v)
+        out[key] = vals
+    return out
+
+
+def profiled_traffic(workload_name):
+    """HBM bytes per launch of the attention kernel from the committed rocprofv3
+    summary, or None when the kernel source changed after the counters were
+    taken."""
+    t = profiled_counters(workload_name).get("traffic")
+    if t is None:
         return None
-    # the stamp covers every source the attention kernel is compiled from
-    stamp = hashlib.sha256()
-    for f in ("attn_bf16.hip", "lds_stream.hpp", "common.hpp", "topk.hpp"):
-        stamp.update(open(os.path.join(ROOT, "piecewise_block_sparse_amd", "csrc", f), "rb").read())
-    m = re.search(r"attn_bf16_kernel traffic_bytes_per_launch=(\d+) read=(\d+) write=(\d+) "
-                  r"avg_ns=(\d+) source=([0-9a-f]+)", open(path).read())
-    if not m or stamp.hexdigest()[:16] != m.group(5):
-        return None
-    return {"total": int(m.group(1)), "read": int(m.group(2)), "write": int(m.group(3)),
-            "profiled_avg_ms": int(m.group(4)) / 1e6}
+    return {"total": t["traffic_bytes_per_launch"], "read": t["read"], "write": t["write"],
+            "profiled_avg_ms": t["avg_ns"] / 1e6}
+
+
+def phase_counters(workload_name):
+    """The profile's per-phase counter figures, with the rates they imply."""
+    c = profiled_counters(workload_name)
+    out = {}
+    if "exact_phase" in c:
+        e = c["exact_phase"]
+        rate = e["mfma_gflop"] / (e["avg_ns"] * 1e-9) / 1e3          # TFLOP/s
+        out["exact_phase"] = dict(e, profiled_tflops=rate, frac=rate / MFMA_BF16_PEAK_TFLOPS)
+    if "approx_phase" in c:
+        a = c["approx_phase"]
+        t = a["avg_ns"] * 1e-9
+        out["approx_phase"] = dict(a, operand_stream_gbs=a["operand_stream_bytes"] / t / 1e9 if t > 0 else None)
+    if "statistics" in c:
+        st = c["statistics"]
+        gbs = st["algorithmic_bytes"] / (st["avg_ns"] * 1e-9) / 1e9
+        out["statistics"] = dict(st, algorithmic_gbs=gbs, frac=gbs / HBM_PEAK_GBS)
+    return out or None
 
 
 def timed_phases(pisa, torch, Qd, Kd, Vd, w, k, steps, warmup, mode="approx"):
@@ -583,6 +636,8 @@ def main():
                      "traffic": traffic["total"] if traffic else None,
                      "traffic_detail": dict(traffic, algorithmic_min=min_bytes) if traffic else None,
                      "kernel": f"attn_bf16_kernel (d={w.head_dim}, block={w.block})",
+                     # rocprofv3 counters of the same kernels (committed profile, source-stamped)
+                     "phase_counters": phase_counters(w.name),
                      "avg_launch_ms": t_attn,
                      # the metric's MFMA utilisation: algorithmic bf16 rate over the peak
                      "mfma_util": {

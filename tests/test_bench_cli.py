@@ -38,6 +38,39 @@ def test_profiled_traffic_is_read_only_for_the_profiled_kernel_source(tmp_path, 
     assert bench.profiled_traffic("missing") is None
 
 
+def test_phase_counters_follow_each_lines_own_source_stamp(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    csrc = tmp_path / "piecewise_block_sparse_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for f in ("attn_bf16.hip", "lds_stream.hpp", "common.hpp", "topk.hpp", "stats.hip"):
+        (csrc / f).write_text(f)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    attn = bench._source_stamp(bench._ATTN_SOURCES)
+    stats = bench._source_stamp(bench._STATS_SOURCES)
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "kernels_x.md").write_text(
+        "text before\n"
+        f"exact_phase mfma_gflop=2500.0 mfma_busy=0.5 coexec=0.25 clock_ghz=2.0 avg_ns=2000000 source={attn}\n"
+        f"approx_phase mfma_gflop=10.0 read_bytes=5 write_bytes=0 avg_ns=0 operand_stream_bytes=7 source={attn}\n"
+        f"statistics avg_ns=1000 algorithmic_bytes=4000000 read_bytes=1 write_bytes=2 pass1_write_bytes=2 "
+        f"source={stats}\n")
+    c = bench.phase_counters("x")
+    assert c["exact_phase"]["profiled_tflops"] == 2500.0 / 2e-3 / 1e3           # 1250 TFLOP/s
+    assert abs(c["exact_phase"]["frac"] - 0.5) < 1e-12
+    assert c["approx_phase"]["operand_stream_gbs"] is None                     # no time, no rate
+    assert abs(c["statistics"]["algorithmic_gbs"] - 4000.0) < 1e-9
+    assert abs(c["statistics"]["frac"] - 0.5) < 1e-12
+    # a change to stats.hip drops the statistics line only
+    (csrc / "stats.hip").write_text("changed")
+    c = bench.phase_counters("x")
+    assert "statistics" not in c and "exact_phase" in c
+    # a change to the attention kernel drops its lines
+    (csrc / "attn_bf16.hip").write_text("changed")
+    assert bench.phase_counters("x") is None
+
+
 def test_flops_model_matches_the_stated_algorithmic_work():
     sys.path.insert(0, ROOT)
     import bench
