@@ -622,9 +622,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       s_qbar[e] = sum * ((nq == BLK) ? 1.0 / BLK : 1.0 / (double)(nq > 0 ? nq : 1));
     }
     __syncthreads();
-    // scores of the candidates j < nne against the QB pooled queries: fp64
-    // FMAs over d in order, then scale * dot + lambda * M_j as one FMA (the
-    // route kernel's arithmetic)
+    // scores of the candidates j < nne against the QB pooled queries: one
+    // fp64 FMA chain over d in the route kernel's order (within each 16-wide
+    // chunk of the head dimension: d = 16 t + 4 g + s for s, then g), then
+    // scale * dot + lambda * M_j as one FMA: the route kernel's arithmetic, so
+    // both select the same blocks
     {
       const float* cen = p.centroid + (size_t)bh * nb * D;
       const float* Mh = p.M + (size_t)bh * nb;
@@ -633,38 +635,23 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
         double acc[QB];
 #pragma unroll
         for (int q = 0; q < QB; ++q) acc[q] = 0.0;
-        if constexpr (QB == 2) {
-          // the centroid row in batches of eight 16-byte loads in flight (with
-          // one query block per workgroup the same batches make the compiler
-          // spill the main loop, so that case reads four at a time)
-          for (int a0 = 0; a0 < D; a0 += 32) {
-            f32x4 kv[8];
+        // the centroid row in 16-byte loads, eight in flight for query-block
+        // pairs (with one query block per workgroup eight make the compiler
+        // spill the main loop, so that case reads four at a time)
+        constexpr int CH = (QB == 2) ? 2 : 1;            // 16-wide chunks per batch
+        for (int a0 = 0; a0 < D; a0 += 16 * CH) {
+          f32x4 kv[4 * CH];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) kv[u] = *reinterpret_cast<const f32x4*>(cj + a0 + 4 * u);
+          for (int u = 0; u < 4 * CH; ++u) kv[u] = *reinterpret_cast<const f32x4*>(cj + a0 + 4 * u);
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+          for (int h = 0; h < CH; ++h)
 #pragma unroll
-              for (int q = 0; q < QB; ++q) {
-                const double* qq = s_qbar + q * D + a0 + 4 * u;
-                acc[q] = fma(qq[0], (double)kv[u][0], acc[q]);
-                acc[q] = fma(qq[1], (double)kv[u][1], acc[q]);
-                acc[q] = fma(qq[2], (double)kv[u][2], acc[q]);
-                acc[q] = fma(qq[3], (double)kv[u][3], acc[q]);
-              }
-          }
-        } else {
-#pragma unroll 4
-          for (int a = 0; a < D; a += 4) {
-            const f32x4 kv = *reinterpret_cast<const f32x4*>(cj + a);
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int q = 0; q < QB; ++q) {
-              const double* qq = s_qbar + q * D + a;
-              acc[q] = fma(qq[0], (double)kv[0], acc[q]);
-              acc[q] = fma(qq[1], (double)kv[1], acc[q]);
-              acc[q] = fma(qq[2], (double)kv[2], acc[q]);
-              acc[q] = fma(qq[3], (double)kv[3], acc[q]);
-            }
-          }
+              for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int q = 0; q < QB; ++q)
+                  acc[q] = fma(s_qbar[q * D + a0 + 16 * h + 4 * g + s], (double)kv[4 * h + g][s], acc[q]);
         }
         const double mj = ri.rlam * (double)Mh[j];
 #pragma unroll

@@ -5,20 +5,31 @@
 //     score_ij = scale * qbar_i . kbar_j + lambda * M_j     (float64)
 //
 // qbar_i is the mean query of block i.  The sum of bf16 (or fp32) values in
-// float64 is exact for these block sizes, so qbar_i carries no rounding; the
-// dot products are float64 FMAs.  S_i = the k highest scores, ties to the lower
-// j, written in ascending order.
+// float64 is exact for these block sizes, so qbar_i carries no rounding.  The
+// dot product is a chain of fp64 FMAs over the head dimension in the order
+// d = 16 t + 4 g + s for t, then s, then g (t < D / 16, s, g < 4), then
+// scale * dot + lambda * M_j as one more FMA; the in-kernel routing of the
+// attention kernel uses the same chain, so both select the same blocks.
+// S_i = the k highest scores, ties to the lower j, written in ascending order.
 //
-// One workgroup = R waves = R query blocks of one head (R = 8 when there are at
-// least 256 blocks to score, else 4; each centroid is read from L2 once per
-// workgroup, so more rows per workgroup means fewer re-reads of it).  Each wave pools its
-// block's queries with fully unrolled 16-byte loads (the HBM-bound part); for
-// the scores each thread owns one centroid and forms its dot products with all
-// R pooled queries (broadcast LDS reads); each wave then selects its row's
-// top k with a radix select over order-preserving 64-bit keys (ties at the
-// threshold resolved to the lower block ids), stopping as soon as the keys
-// still in play are exactly the ones it has left to take.  LDS is sized to the padded
-// block count, so small nb keeps many workgroups resident.
+// One workgroup = R waves = R query blocks of one head (R = 8 when there are
+// at least 256 blocks to score, else 4).  Workgroups are placed so that each
+// XCD takes a contiguous range of them: the query blocks of one head then share
+// that XCD's L2 copy of the head's centroids.  Three phases:
+//   pool   each wave sums its block's queries with fully unrolled 16-byte
+//          loads (the HBM-bound part) into a qbar row in LDS;
+//   score  the R x nb scores on fp64 MFMA 16x16x4 (A = the qbar rows, the
+//          rows past R zero; B = 16 centroids per tile, read with 16-byte
+//          loads).  One such MFMA is the chain of four FMAs over its k index
+//          in order, so the tiles reproduce the FMA chain above exactly; each
+//          wave runs two tiles side by side, sharing every A fragment read.
+//          (The fp64 FMAs of a thread-per-centroid loop would read every qbar
+//          value from LDS once per FMA as a broadcast, which made the LDS port
+//          the bound of this phase.)
+//   select each wave takes its row's top k with a radix select over
+//          order-preserving 64-bit keys (ties at the threshold resolved to the
+//          lower block ids), stopping as soon as the keys still in play are
+//          exactly the ones it has left to take.
 //
 // With valid lengths, block i pools its n_i valid queries, only the non-empty
 // blocks (a prefix: j < ceil(len / BLK)) are candidates, a row with fewer than
@@ -58,39 +69,69 @@ struct Chunk8<float> {
   }
 };
 
-// dynamic LDS layout (bytes): q[R][D] f64 | sc[R][nbp] f64 |
-// hist[R][256] u32 | sel[R][nbp/32] u32
-template <int D, int R>
-__host__ __device__ constexpr size_t route_lds_bytes(int nbp) {
-  return (size_t)R * D * 8 + (size_t)R * nbp * 8 + (size_t)R * 256 * 4 +
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// D[16x16] += A[16x4] B[4x16] in fp64, as four FMAs per element in k order.
+// Lane l holds A[l % 16][l / 16] and B[l / 16][l % 16]; register r of the
+// result holds D[l / 16 + 4 r][l % 16].
+__device__ __forceinline__ f64x4 mfma_f64(double a, double b, const f64x4& c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// qbar rows are padded by two doubles (16 bytes) so that the rows a fragment
+// read touches start in different banks
+template <int D>
+__host__ __device__ constexpr int qbar_stride() { return D + 2; }
+
+// dynamic LDS layout (bytes): qbar [R][D + 2] f64 | scores [R][nbp] f64 |
+// hist [R][256] u32 | sel [R][nbp / 32] u32
+template <int D>
+__host__ __device__ constexpr size_t route_lds_bytes(int R, int nbp) {
+  return (size_t)R * qbar_stride<D>() * 8 + (size_t)R * nbp * 8 + (size_t)R * 256 * 4 +
          (size_t)R * (nbp / 32) * 4;
 }
 
-template <int D, int BLK, typename T, int kRows>
-__global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__ Q,
-                                                            const float* __restrict__ centroid,
-                                                            const float* __restrict__ M, int nb,
-                                                            int nbp, int k, double scale,
-                                                            double lam, int32_t* __restrict__ idx,
-                                                            const int32_t* __restrict__ lens,
-                                                            int heads) {
+// A fragments of 16-wide chunk t: lane (col, g) holds qbar[col][16 t + 4 g + s]
+// for s = 0..3 (rows col >= R are zero)
+template <int D, int R>
+__device__ __forceinline__ void qbar_frag(const double* s_q, int col, int g, int t, double (&a)[4]) {
+  if (col < R) {
+    const double* p = s_q + col * qbar_stride<D>() + 16 * t + 4 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = p[s];
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = 0.0;
+  }
+}
+
+template <int D, int BLK, typename T, int R>
+__global__ __launch_bounds__(64 * R) void route_kernel(const T* __restrict__ Q,
+                                                        const float* __restrict__ centroid,
+                                                        const float* __restrict__ M, int nb, int nbp,
+                                                        int k, double scale, double lam,
+                                                        int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ lens, int heads) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int QS = qbar_stride<D>();
+  constexpr int NT = D / 16;                             // 16-wide chunks of the head dimension
   double* s_q = reinterpret_cast<double*>(smem);
-  double* s_sc = s_q + kRows * D;
-  unsigned* s_hist = reinterpret_cast<unsigned*>(s_sc + kRows * nbp);
-  unsigned* s_sel = s_hist + kRows * 256;
+  double* s_sc = s_q + R * QS;
+  unsigned* s_hist = reinterpret_cast<unsigned*>(s_sc + R * nbp);
+  unsigned* s_sel = s_hist + R * 256;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int nrb = (nb + kRows - 1) / kRows;
-  const int bh = blockIdx.x / nrb;
-  const int i = (blockIdx.x - bh * nrb) * kRows + w;   // this wave's query block
+  const int ngr = (nb + R - 1) / R;                      // row groups per (batch, head)
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = item / ngr, i0 = (item - bh * ngr) * R;
+  const int i = i0 + w;                                  // this wave's query block
   const bool active = i < nb;
   const size_t L = (size_t)nb * BLK;
   const int Lv = valid_len(lens, bh, heads, (int)L);
-  const int nne = (Lv + BLK - 1) / BLK;                // non-empty blocks: j < nne
-  const int ni = block_count(Lv, i, BLK);              // valid queries of block i
+  const int nne = (Lv + BLK - 1) / BLK;                  // non-empty blocks: j < nne
+  const int ni = active ? block_count(Lv, i, BLK) : 0;   // valid queries of block i
 
-  // ---- pool: qbar_i = (1/BLK) sum of the block's queries, exact in fp64
+  // ---- pool: qbar_i = (1 / n_i) sum of the block's valid queries, exact in fp64
   {
     constexpr int CPR = D / 8;               // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;            // rows per wave instruction
@@ -118,47 +159,51 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
     const double inv = (ni == BLK) ? 1.0 / BLK : 1.0 / (double)(ni > 0 ? ni : 1);
     if (rs == 0)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_q[w * D + 8 * c + e] = x[e] * inv;
+      for (int e = 0; e < 8; ++e) s_q[w * QS + 8 * c + e] = x[e] * inv;
   }
-
-  // ---- scores against every block centroid: thread t owns centroid j0 + t
-  // and all kRows pooled queries (read as LDS broadcasts), fp64 FMAs
+  for (int t = tid; t < R * (nbp / 32); t += 64 * R) s_sel[t] = 0u;
   __syncthreads();
+
+  // ---- score, on fp64 MFMA: tile n = rows 0..15 (those past R are zero) x
+  // centroids 16 n .. 16 n + 15.  MFMA (t, s) contracts its k = g (the lane's
+  // quarter) with d = 16 t + 4 k + s, so every output gets the FMA chain in
+  // the order stated at the top.  Each wave runs two tiles side by side (two
+  // independent accumulator chains share each A fragment read).
+  const int g = lane >> 4, col = lane & 15;
   const float* cen = centroid + (size_t)bh * nb * D;
   const float* Mh = M + (size_t)bh * nb;
-  for (int j0 = 0; j0 < nb; j0 += 64 * kRows) {
-    const int j = j0 + tid;
-    if (j < nb) {
-      const float* cj = cen + (size_t)j * D;
-      double acc[kRows];
+  const int ntile = nbp / 16;
+#pragma unroll 1
+  for (int n0 = 2 * w; n0 < ntile; n0 += 2 * R) {
+    const int ja = 16 * n0 + col, jb = ja + 16;          // (ntile is even: nbp >= 64)
+    const bool va = ja < nb, vb = jb < nb;
+    const float* ca = cen + (size_t)(va ? ja : 0) * D + 4 * g;
+    const float* cb = cen + (size_t)(vb ? jb : 0) * D + 4 * g;
+    f64x4 acc_a = {0.0, 0.0, 0.0, 0.0}, acc_b = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) acc[r] = 0.0;
-      // the centroid row in batches of eight 16-byte loads in flight (the
-      // scoring waits on L2 latency, not on the FMAs)
-      for (int a0 = 0; a0 < D; a0 += 32) {
-        f32x4 kv[8];
+    for (int t = 0; t < NT; ++t) {
+      const f32x4 xa = va ? *reinterpret_cast<const f32x4*>(ca + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 xb = vb ? *reinterpret_cast<const f32x4*>(cb + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
+      double a[4];
+      qbar_frag<D, R>(s_q, col, g, t, a);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) kv[u] = *reinterpret_cast<const f32x4*>(cj + a0 + 4 * u);
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-          for (int r = 0; r < kRows; ++r) {
-            const double* q = s_q + r * D + a0 + 4 * u;
-            acc[r] = fma(q[0], (double)kv[u][0], acc[r]);
-            acc[r] = fma(q[1], (double)kv[u][1], acc[r]);
-            acc[r] = fma(q[2], (double)kv[u][2], acc[r]);
-            acc[r] = fma(q[3], (double)kv[u][3], acc[r]);
-          }
+      for (int s = 0; s < 4; ++s) {
+        acc_a = mfma_f64(a[s], (double)xa[s], acc_a);
+        acc_b = mfma_f64(a[s], (double)xb[s], acc_b);
       }
-      const double mj = lam * (double)Mh[j];
+    }
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) s_sc[r * nbp + j] = fma(scale, acc[r], mj);
+    for (int r = 0; r < 4; ++r) {
+      const int row = g + 4 * r;
+      if (row < R) {
+        if (va) s_sc[row * nbp + ja] = fma(scale, acc_a[r], lam * (double)Mh[ja]);
+        if (vb) s_sc[row * nbp + jb] = fma(scale, acc_b[r], lam * (double)Mh[jb]);
+      }
     }
   }
   double* sc = s_sc + w * nbp;
   unsigned* hist = s_hist + w * 256;
   unsigned* sel = s_sel + w * (nbp / 32);
-  for (int t = lane; t < nbp / 32; t += 64) sel[t] = 0u;
   __syncthreads();
 
   // ---- top-k of this wave's row (ties to the lower block ids)
@@ -172,15 +217,15 @@ __global__ __launch_bounds__(64 * kRows) void route_kernel(const T* __restrict__
 
 template <int D, int BLK, typename T, int R>
 hipError_t route_launch(const RouteArgs& a, int nbp) {
-  const size_t lds = route_lds_bytes<D, R>(nbp);
+  const size_t lds = route_lds_bytes<D>(R, nbp);
   auto kern = route_kernel<D, BLK, T, R>;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const int nrb = (a.nb + R - 1) / R;
-  hipLaunchKernelGGL(kern, dim3(a.bh * nrb), dim3(64 * R), lds, a.stream, (const T*)a.Q,
+  const int ngr = (a.nb + R - 1) / R;
+  hipLaunchKernelGGL(kern, dim3(a.bh * ngr), dim3(64 * R), lds, a.stream, (const T*)a.Q,
                      a.centroid, a.M, a.nb, nbp, a.k, a.scale, a.lam, a.idx, a.lens, a.heads);
   return hipGetLastError();
 }
