@@ -639,7 +639,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
         // pairs (with one query block per workgroup eight make the compiler
         // spill the main loop, so that case reads four at a time)
         constexpr int CH = (QB == 2) ? 2 : 1;            // 16-wide chunks per batch
-        for (int a0 = 0; a0 < D; a0 += 16 * CH) {
+        auto batch = [&](int a0) {
           f32x4 kv[4 * CH];
 #pragma unroll
           for (int u = 0; u < 4 * CH; ++u) kv[u] = *reinterpret_cast<const f32x4*>(cj + a0 + 4 * u);
@@ -652,6 +652,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
 #pragma unroll
                 for (int q = 0; q < QB; ++q)
                   acc[q] = fma(s_qbar[q * D + a0 + 16 * h + 4 * g + s], (double)kv[4 * h + g][s], acc[q]);
+        };
+        if constexpr (QB == 2) {
+          for (int a0 = 0; a0 < D; a0 += 16 * CH) batch(a0);
+        } else {
+#pragma unroll 1
+          for (int a0 = 0; a0 < D; a0 += 16 * CH) batch(a0);   // one batch at a time: no spills
         }
         const double mj = ri.rlam * (double)Mh[j];
 #pragma unroll
