@@ -574,6 +574,31 @@ def test_route_max_blocks(torch):
     check_route(idx.cpu().numpy(), scores, k, name="nb2048")
 
 
+@pytest.mark.parametrize("dtype,d,nb", [("bf16", 128, 255), ("bf16", 128, 256), ("bf16", 64, 257),
+                                        ("bf16", 128, 300), ("fp32", 128, 300), ("fp32", 64, 255)])
+def test_route_block_counts_around_the_row_split(torch, dtype, d, nb):
+    """Block counts on both sides of the route kernel's switch from four to
+    eight query blocks per workgroup (256), counts that are not a multiple of
+    the 16-block score tiles, both input types and head dims, batch 2 with
+    one shorter sequence: routing against the oracle's scores."""
+    pisa = pisa_mod()
+    B, k = 64, 23
+    L = nb * B
+    lens = [L, L - 5 * B - 17]
+    Q, K, V = (_rand(torch, (2, 2, L, d), dtype, s) for s in (71, 72, 73))
+    K = K + np.repeat(_rand(torch, (2, 2, nb, d), "fp32", 74) * 0.5, B, axis=2)
+    if dtype == "bf16":
+        K = wl.round_bf16(K)
+    Qd, Kd, Vd = (to_dev(x, dtype) for x in (Q, K, V))
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    st = pisa.precompute(Kd, Vd, B, seq_lens=sl)
+    idx = pisa.route(Qd, st, k, 0.05, B, seq_lens=sl)
+    torch.cuda.synchronize()
+    scores = oracle.route_scores(Q, to_np(st["centroid"]), to_np(st["M"]), 0.05, B, 1 / math.sqrt(d),
+                                 seq_lens=lens)
+    check_route(idx.cpu().numpy(), scores, k, name=f"route/{dtype}/d{d}/nb{nb}")
+
+
 @pytest.mark.parametrize("B", [64, 128])
 def test_attention_max_blocks_all_modes(torch, B):
     """nb = 2048 (the largest supported block count) with a large k: the
