@@ -24,7 +24,7 @@
  *   4.1); the library rejects ragged blocks rather than bias centroids with pad
  *   tokens.  nb = L / block.
  * - Supported: head_dim in {64, 128}; block in {64, 128}; nb <= 2048;
- *   batch*heads*nb < 2^31.
+ *   batch*heads*nb < 2^31; batch*heads < 2^27 (PISA_ERR_SHAPE otherwise).
  * - Every pointer argument except `stream` is a DEVICE pointer owned by the
  *   caller; the library never allocates or frees device memory.  Its only
  *   device memory of its own is the static workspace array of

@@ -1,5 +1,6 @@
 // C ABI of libpisa: argument validation on the host, then kernel launches on
 // the caller's stream.  Declared in include/pisa.h.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -47,6 +48,8 @@ pisa_status check_shape(const pisa_shape* s, int* bh, int* nb) {
   const long long b = (long long)s->batch * s->heads;
   if (b * n >= (1LL << 31))
     return fail(PISA_ERR_SHAPE, "batch * heads * blocks must stay below 2^31");
+  // the Hbar reduction launches (d / 32)^2 <= 16 workgroups per head
+  if (b >= (1LL << 27)) return fail(PISA_ERR_SHAPE, "batch * heads must stay below 2^27");
   *bh = (int)b;
   *nb = (int)n;
   return PISA_OK;
@@ -255,6 +258,17 @@ pisa_status pisa_attention_split(const pisa_shape* shape, const void* Q, const v
     return fail(PISA_ERR_NULL, "APPROX mode needs stats Hbar");
   const size_t need = pisa_attention_split_workspace_size(shape, kmax, max_blocks);
   if (!workspace) return fail(PISA_ERR_NULL, "workspace of %zu bytes is required", need);
+  {
+    // the grid holds every part of every work item (a work item is a pair of
+    // query blocks for 64-token blocks; items rounded up to a multiple of the
+    // 8 XCDs)
+    const long long qb = shape->block == 64 ? 2 : 1;
+    const long long items = (long long)bh * ((nb + qb - 1) / qb);
+    const long long most = std::min<long long>(nb, qb * kmax);
+    const long long parts = std::min<long long>(32, std::max<long long>(1, (most + max_blocks - 1) / max_blocks));
+    if ((items + 7) / 8 * 8 * parts >= (1LL << 31))
+      return fail(PISA_ERR_SHAPE, "split attention: %lld work items x %lld parts exceed one grid", items, parts);
+  }
   if (workspace_bytes < need)
     return fail(PISA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   const int order = mode == PISA_MODE_ZEROTH ? pisa::kOrderZeroth : pisa::kOrderMixed;

@@ -211,6 +211,27 @@ def test_noalloc_precompute_refuses_shapes_above_its_scratch(lib):
     assert lib.pisa_precompute_noalloc(ctypes.byref(bad), fake, fake, ctypes.byref(st), None) == 2
 
 
+def test_sizes_of_very_large_shapes_do_not_wrap(lib):
+    # 2^26 - 1 heads of two 64-token blocks: every size is far above 2^32 bytes
+    # and must come out exact (host arithmetic in 64 bits)
+    h = (1 << 26) - 1
+    s = shape(h=h, L=128)
+    assert lib.pisa_packed_size(ctypes.byref(s)) == h * (2 * 64 * 128 + 128 * 128) * 2     # nbp = 64
+    assert lib.pisa_workspace_size(ctypes.byref(s)) == h * (1 + 1) * 128 * 128 * 4      # one range per head
+    # 2^27 heads: the Hbar reduction's grid (16 workgroups per head) would not fit an int
+    big = shape(h=1 << 27, L=64)
+    assert lib.pisa_workspace_size(ctypes.byref(big)) == 0
+    assert pre(lib, big) == 2
+    assert b"2^27" in lib.pisa_last_error()
+    # split attention whose parts would overflow one grid: refused on the host
+    fake = 1 << 40                                                  # never dereferenced
+    s = shape(h=h, L=32 * 64)                                       # nb = 32: 16 pairs per head
+    rc = lib.pisa_attention_split(ctypes.byref(s), fake, fake, fake, fake, 16, None, 1, 0.125, 1, fake,
+                                  fake, 1 << 62, None)
+    assert rc == 2
+    assert b"exceed one grid" in lib.pisa_last_error()
+
+
 def test_split_attention_arguments(lib):
     s = shape()                                                     # nb = 16, 64-token blocks
     fake = 1 << 40                                                  # never dereferenced
