@@ -18,11 +18,13 @@
 // that XCD's L2 copy of the head's centroids.  Three phases:
 //   pool   each wave sums its block's queries with fully unrolled 16-byte
 //          loads (the HBM-bound part) into a qbar row in LDS;
-//   score  the R x nb scores on fp64 MFMA 16x16x4 (A = the qbar rows, the
-//          rows past R zero; B = 16 centroids per tile, read with 16-byte
-//          loads).  One such MFMA is the chain of four FMAs over its k index
-//          in order, so the tiles reproduce the FMA chain above exactly; each
-//          wave runs two tiles side by side, sharing every A fragment read.
+//   score  the R x nb scores on fp64 MFMA (A = the qbar rows, B = 16
+//          centroids per tile, read with 16-byte loads): 16x16x4 for eight
+//          rows (A rows 8..15 zero), four 4x4x4 blocks per instruction for
+//          four rows (no padding).  Both compute each output as the chain of
+//          four FMAs over k in order, so the tiles reproduce the FMA chain
+//          above exactly; each wave runs two tiles side by side, sharing every
+//          A fragment read.
 //          (The fp64 FMAs of a thread-per-centroid loop would read every qbar
 //          value from LDS once per FMA as a broadcast, which made the LDS port
 //          the bound of this phase.)
@@ -71,11 +73,19 @@ struct Chunk8<float> {
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-// D[16x16] += A[16x4] B[4x16] in fp64, as four FMAs per element in k order.
-// Lane l holds A[l % 16][l / 16] and B[l / 16][l % 16]; register r of the
-// result holds D[l / 16 + 4 r][l % 16].
-__device__ __forceinline__ f64x4 mfma_f64(double a, double b, const f64x4& c) {
+// D[16x16] += A[16x4] B[4x16] in fp64, each output the chain of four FMAs over
+// k in order.  Lane l holds A[l % 16][l / 16] and B[l / 16][l % 16]; register
+// r of the result holds D[l / 16 + 4 r][l % 16].
+__device__ __forceinline__ f64x4 mfma_f64_16x16(double a, double b, const f64x4& c) {
   return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// Four independent 4x4x4 fp64 products per instruction (blocks b = 0..3),
+// each output the chain of four FMAs over k in order: lane 16 k + 4 b + i
+// holds A_b[i][k], lane 16 k + 4 b + j holds B_b[k][j], and the result lane
+// 16 i + 4 b + j holds D_b[i][j].
+__device__ __forceinline__ double mfma_f64_4x4(double a, double b, double c) {
+  return __builtin_amdgcn_mfma_f64_4x4x4f64(a, b, c, 0, 0, 0);
 }
 
 // qbar rows are padded by two doubles (16 bytes) so that the rows a fragment
@@ -91,18 +101,13 @@ __host__ __device__ constexpr size_t route_lds_bytes(int R, int nbp) {
          (size_t)R * (nbp / 32) * 4;
 }
 
-// A fragments of 16-wide chunk t: lane (col, g) holds qbar[col][16 t + 4 g + s]
-// for s = 0..3 (rows col >= R are zero)
-template <int D, int R>
-__device__ __forceinline__ void qbar_frag(const double* s_q, int col, int g, int t, double (&a)[4]) {
-  if (col < R) {
-    const double* p = s_q + col * qbar_stride<D>() + 16 * t + 4 * g;
+// A operand of 16-wide chunk t for a lane whose k index is kq: qbar[row][16 t
+// + 4 kq + s] for s = 0..3 (two 16-byte LDS reads)
+template <int D>
+__device__ __forceinline__ void qbar_frag(const double* s_q, int row, int kq, int t, double (&a)[4]) {
+  const double* p = s_q + row * qbar_stride<D>() + 16 * t + 4 * kq;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) a[s] = p[s];
-  } else {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) a[s] = 0.0;
-  }
+  for (int s = 0; s < 4; ++s) a[s] = p[s];
 }
 
 template <int D, int BLK, typename T, int R>
@@ -164,41 +169,74 @@ __global__ __launch_bounds__(64 * R) void route_kernel(const T* __restrict__ Q,
   for (int t = tid; t < R * (nbp / 32); t += 64 * R) s_sel[t] = 0u;
   __syncthreads();
 
-  // ---- score, on fp64 MFMA: tile n = rows 0..15 (those past R are zero) x
-  // centroids 16 n .. 16 n + 15.  MFMA (t, s) contracts its k = g (the lane's
-  // quarter) with d = 16 t + 4 k + s, so every output gets the FMA chain in
-  // the order stated at the top.  Each wave runs two tiles side by side (two
-  // independent accumulator chains share each A fragment read).
-  const int g = lane >> 4, col = lane & 15;
+  // ---- score, on fp64 MFMA.  Every MFMA (t, s) contracts k (the lane's
+  // quarter, lane / 16) with d = 16 t + 4 k + s, so every score gets the FMA
+  // chain in the order stated at the top.  Each wave runs two tiles side by
+  // side, sharing each A fragment read.
+  const int kq = lane >> 4;
   const float* cen = centroid + (size_t)bh * nb * D;
   const float* Mh = M + (size_t)bh * nb;
-  const int ntile = nbp / 16;
+  if constexpr (R == 8) {
+    // 16x16x4 tiles of 16 centroids; A rows 8..15 are zero (measured faster
+    // for eight rows than 4x4x4 blocks without padding)
+    const int col = lane & 15;
+    const int ntile = nbp / 16;                           // even: nbp >= 64
 #pragma unroll 1
-  for (int n0 = 2 * w; n0 < ntile; n0 += 2 * R) {
-    const int ja = 16 * n0 + col, jb = ja + 16;          // (ntile is even: nbp >= 64)
-    const bool va = ja < nb, vb = jb < nb;
-    const float* ca = cen + (size_t)(va ? ja : 0) * D + 4 * g;
-    const float* cb = cen + (size_t)(vb ? jb : 0) * D + 4 * g;
-    f64x4 acc_a = {0.0, 0.0, 0.0, 0.0}, acc_b = {0.0, 0.0, 0.0, 0.0};
+    for (int n0 = 2 * w; n0 < ntile; n0 += 2 * R) {
+      const int ja = 16 * n0 + col, jb = ja + 16;
+      const bool va = ja < nb, vb = jb < nb;
+      const float* ca = cen + (size_t)(va ? ja : 0) * D + 4 * kq;
+      const float* cb = cen + (size_t)(vb ? jb : 0) * D + 4 * kq;
+      f64x4 acc_a = {0.0, 0.0, 0.0, 0.0}, acc_b = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const f32x4 xa = va ? *reinterpret_cast<const f32x4*>(ca + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
-      const f32x4 xb = vb ? *reinterpret_cast<const f32x4*>(cb + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
-      double a[4];
-      qbar_frag<D, R>(s_q, col, g, t, a);
+      for (int t = 0; t < NT; ++t) {
+        const f32x4 xa = va ? *reinterpret_cast<const f32x4*>(ca + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 xb = vb ? *reinterpret_cast<const f32x4*>(cb + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
+        double a[4] = {0.0, 0.0, 0.0, 0.0};
+        if (col < R) qbar_frag<D>(s_q, col, kq, t, a);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        acc_a = mfma_f64(a[s], (double)xa[s], acc_a);
-        acc_b = mfma_f64(a[s], (double)xb[s], acc_b);
+        for (int s = 0; s < 4; ++s) {
+          acc_a = mfma_f64_16x16(a[s], (double)xa[s], acc_a);
+          acc_b = mfma_f64_16x16(a[s], (double)xb[s], acc_b);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = kq + 4 * r;
+        if (row < R) {
+          if (va) s_sc[row * nbp + ja] = fma(scale, acc_a[r], lam * (double)Mh[ja]);
+          if (vb) s_sc[row * nbp + jb] = fma(scale, acc_b[r], lam * (double)Mh[jb]);
+        }
       }
     }
+  } else {
+    // four rows: 4x4x4 blocks, block b taking centroids 4 b .. 4 b + 3 of a
+    // 16-centroid tile (no padding)
+    static_assert(R == 4, "route rows per workgroup: 4 or 8");
+    const int blk = (lane & 15) >> 2, i4 = lane & 3;
+    const int ntile = nbp / 16;
+#pragma unroll 1
+    for (int n0 = 2 * w; n0 < ntile; n0 += 2 * R) {
+      const int ja = 16 * n0 + 4 * blk + i4, jb = ja + 16;   // B and result centroids of the lane
+      const bool va = ja < nb, vb = jb < nb;
+      const float* ca = cen + (size_t)(va ? ja : 0) * D + 4 * kq;
+      const float* cb = cen + (size_t)(vb ? jb : 0) * D + 4 * kq;
+      double acc_a = 0.0, acc_b = 0.0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = g + 4 * r;
-      if (row < R) {
-        if (va) s_sc[row * nbp + ja] = fma(scale, acc_a[r], lam * (double)Mh[ja]);
-        if (vb) s_sc[row * nbp + jb] = fma(scale, acc_b[r], lam * (double)Mh[jb]);
+      for (int t = 0; t < NT; ++t) {
+        const f32x4 xa = va ? *reinterpret_cast<const f32x4*>(ca + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 xb = vb ? *reinterpret_cast<const f32x4*>(cb + 16 * t) : f32x4{0.f, 0.f, 0.f, 0.f};
+        double a[4];
+        qbar_frag<D>(s_q, i4, kq, t, a);                     // A row of the lane: i4
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          acc_a = mfma_f64_4x4(a[s], (double)xa[s], acc_a);
+          acc_b = mfma_f64_4x4(a[s], (double)xb[s], acc_b);
+        }
       }
+      // result lane 16 i + 4 b + j: row i = kq, centroid 4 b + j of the tile
+      if (va) s_sc[kq * nbp + ja] = fma(scale, acc_a, lam * (double)Mh[ja]);
+      if (vb) s_sc[kq * nbp + jb] = fma(scale, acc_b, lam * (double)Mh[jb]);
     }
   }
   double* sc = s_sc + w * nbp;
