@@ -205,7 +205,11 @@ pisa_status pisa_precompute_noalloc(const pisa_shape* shape, const void* K, cons
  *     score_ij = scale * qbar_i . kbar_j + lambda * M_j,
  *     qbar_i   = mean of the `block` queries of block i.
  *
- * S_i = the k highest scores; ties go to the lower j.
+ * qbar_i is exact (an fp64 sum of the bf16 or fp32 queries); the dot product
+ * is one chain of fp64 FMAs over d in a fixed order, and scale * dot +
+ * lambda * M_j one more FMA.  pisa_route_attention computes the same chain,
+ * so both select the same blocks.  S_i = the k highest scores; ties go to the
+ * lower j.
  *
  *   Q         [b,h,L,d] of shape->dtype (device)
  *   centroid  [b,h,nb,d] float32, M [b,h,nb] float32 (from pisa_precompute)
