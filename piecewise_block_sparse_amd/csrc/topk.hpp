@@ -14,6 +14,47 @@
 
 namespace pisa {
 
+// Wave-wide scans and reductions on DPP row shifts (within rows of 16 lanes)
+// plus three or four readlanes across the rows, instead of LDS permutes: each
+// step costs a few cycles rather than an LDS round trip.  The whole wave must
+// be active.
+template <int N>
+__device__ __forceinline__ unsigned dpp_row_shr(unsigned x, unsigned fill) {
+  // row_shr:N; a lane with no source lane in its row gets `fill`
+  return (unsigned)__builtin_amdgcn_update_dpp((int)fill, (int)x, 0x110 + N, 0xF, 0xF, false);
+}
+
+// inclusive prefix sum over lanes 0 .. lane
+__device__ __forceinline__ unsigned wave_prefix_sum(unsigned x, int lane) {
+  x += dpp_row_shr<1>(x, 0u);
+  x += dpp_row_shr<2>(x, 0u);
+  x += dpp_row_shr<4>(x, 0u);
+  x += dpp_row_shr<8>(x, 0u);
+  const unsigned r0 = (unsigned)__builtin_amdgcn_readlane((int)x, 15);
+  const unsigned r1 = (unsigned)__builtin_amdgcn_readlane((int)x, 31);
+  const unsigned r2 = (unsigned)__builtin_amdgcn_readlane((int)x, 47);
+  const int row = lane >> 4;
+  return x + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
+}
+
+// AND and OR of x over the wave (uniform results)
+__device__ __forceinline__ unsigned wave_and(unsigned x) {
+  x &= dpp_row_shr<1>(x, ~0u);
+  x &= dpp_row_shr<2>(x, ~0u);
+  x &= dpp_row_shr<4>(x, ~0u);
+  x &= dpp_row_shr<8>(x, ~0u);
+  return (unsigned)__builtin_amdgcn_readlane((int)x, 15) & (unsigned)__builtin_amdgcn_readlane((int)x, 31) &
+         (unsigned)__builtin_amdgcn_readlane((int)x, 47) & (unsigned)__builtin_amdgcn_readlane((int)x, 63);
+}
+__device__ __forceinline__ unsigned wave_or(unsigned x) {
+  x |= dpp_row_shr<1>(x, 0u);
+  x |= dpp_row_shr<2>(x, 0u);
+  x |= dpp_row_shr<4>(x, 0u);
+  x |= dpp_row_shr<8>(x, 0u);
+  return (unsigned)__builtin_amdgcn_readlane((int)x, 15) | (unsigned)__builtin_amdgcn_readlane((int)x, 31) |
+         (unsigned)__builtin_amdgcn_readlane((int)x, 47) | (unsigned)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 // fp64 score -> unsigned key with the same order (larger score, larger key)
 __device__ __forceinline__ unsigned long long order_key(double x) {
   const unsigned long long b = __builtin_bit_cast(unsigned long long, x + 0.0);
@@ -43,21 +84,15 @@ __device__ inline void select_top_k(const double* sc, unsigned* hist, unsigned* 
         kand &= key;
         kor |= key;
       }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const unsigned alo = __shfl_xor((unsigned)kand, off), ahi = __shfl_xor((unsigned)(kand >> 32), off);
-      const unsigned olo = __shfl_xor((unsigned)kor, off), ohi = __shfl_xor((unsigned)(kor >> 32), off);
-      kand &= ((unsigned long long)ahi << 32) | alo;
-      kor |= ((unsigned long long)ohi << 32) | olo;
-    }
+    kand = ((unsigned long long)wave_and((unsigned)(kand >> 32)) << 32) | wave_and((unsigned)kand);
+    kor = ((unsigned long long)wave_or((unsigned)(kor >> 32)) << 32) | wave_or((unsigned)kor);
     const unsigned long long diff = kor & ~kand;          // bits that differ somewhere
     if (diff != 0ull) top_pass = (63 - __clzll((long long)diff)) / 8;
   }
   for (int pass = top_pass; pass >= 0; --pass) {
     // every candidate still in play is needed: take them all and stop early
-    int ip = __popc(inplay);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ip += __shfl_xor(ip, off);
+    int ip = 0;
+    for (int u = 0; u < nu; ++u) ip += __popcll(__ballot((inplay >> u) & 1u));
     if (ip == krem) {
       chosen |= inplay;
       inplay = 0u;
@@ -80,13 +115,8 @@ __device__ inline void select_top_k(const double* sc, unsigned* hist, unsigned* 
     // exclusive suffix sum over lanes: above = sum of `own` over lanes > this lane
     unsigned above;
     {
-      unsigned incl = own;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const unsigned y = __shfl_down(incl, off);
-        if (lane + off < 64) incl += y;
-      }
-      above = incl - own;
+      const unsigned incl = wave_prefix_sum(own, lane);  // over lanes <= this one
+      above = (unsigned)__builtin_amdgcn_readlane((int)incl, 63) - incl;
     }
     int dstar = -1;
     unsigned cnt_above = 0u;
@@ -106,9 +136,9 @@ __device__ inline void select_top_k(const double* sc, unsigned* hist, unsigned* 
       dstar = 256;
       cnt_above = 0u;
     } else {
-      const int src = __ffsll(who) - 1;
-      dstar = __shfl(dstar, src);
-      cnt_above = __shfl(cnt_above, src);
+      const int src = __ffsll(who) - 1;                  // uniform
+      dstar = __builtin_amdgcn_readlane(dstar, src);
+      cnt_above = (unsigned)__builtin_amdgcn_readlane((int)cnt_above, src);
     }
     krem -= (int)cnt_above;
     for (int u = 0; u < nu; ++u)
@@ -142,15 +172,10 @@ __device__ inline void select_top_k(const double* sc, unsigned* hist, unsigned* 
 __device__ inline void write_ids_ascending(const unsigned* sel, int nw, int kk, int k, int32_t* out,
                                            int lane) {
   const unsigned word = (lane < nw) ? sel[lane] : 0u;
-  int cnt = __popc(word), pre = cnt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(pre, off);
-    if (lane >= off) pre += y;
-  }
-  int pos = pre - cnt;
+  const int cnt = __popc(word);
+  int pos = (int)wave_prefix_sum((unsigned)cnt, lane) - cnt;
   unsigned wv = word;
-  while (wv) {
+  while (wv && pos < k) {
     const int b = __ffs(wv) - 1;
     out[pos++] = 32 * lane + b;
     wv &= wv - 1;
