@@ -317,8 +317,8 @@ pisa_status pisa_attention_split(const pisa_shape* shape, const void* Q, const v
  * Errors as pisa_route and pisa_attention, and: PISA_ERR_DTYPE for fp32
  * inputs, PISA_ERR_ARG for PISA_MODE_FIRST, PISA_ERR_SHAPE for nb above what
  * the kernel's LDS holds for the score rows (d = 128: nb <= 2048 with
- * 128-token blocks, nb <= 1792 with 64-token blocks; d = 64: nb <= 2048 and
- * 832); the caller then uses pisa_route and pisa_attention.
+ * 128-token blocks, nb <= 1920 with 64-token blocks; d = 64: nb <= 2048 and
+ * 960); the caller then uses pisa_route and pisa_attention.
  */
 pisa_status pisa_route_attention(const pisa_shape* shape, const void* Q, const void* K,
                                  const void* V, const pisa_stats* stats, int32_t k, double lambda,

@@ -567,12 +567,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
     // ---- in-kernel routing.  LDS (the ring, idle until the chunk stream
     // starts): first the query rows, staged for pooling over the whole ring;
     // then qbar [QB][D] f64 | pooling partials [QB][WPQ][D] f64, then the
-    // scores [QB][ncol] f64 in their place | at the end, the select
-    // histograms [QB][256] u32 (the launcher checks that the scores fit).
+    // scores [QB][ncol] f64 in their place (the launcher checks that the
+    // scores fit).
     double* s_qbar = reinterpret_cast<double*>(lds);
     double* s_part = s_qbar + QB * D;
     double* s_sc = s_qbar + QB * D;
-    unsigned* s_hist = reinterpret_cast<unsigned*>(lds + C::LDSB) - QB * 256;
     const int ncol = (nb + 63) / 64 * 64;
     for (int e = tid; e < kBitWords; e += C::NT) {
       const int lo = 32 * e;
@@ -668,7 +667,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
     // top-k of each query block by its first wave; the ids go out when asked
     if (wq == 0 && qvalid) {
       const int kk = (ni > 0) ? min(ri.rk, nne) : 0;
-      select_top_k(s_sc + qb * ncol, s_hist + qb * 256, exb[qb], ncol / 64, nne, kk, lane);
+      select_top_k(s_sc + qb * ncol, exb[qb], ncol / 64, nne, kk, lane);
       if (p.idx_out) write_ids_ascending(exb[qb], ncol / 32, kk, ri.rk, p.idx_out + ((size_t)bh * nb + i) * ri.rk, lane);
     }
     __syncthreads();
@@ -1026,13 +1025,13 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restric
   }
 }
 
-// In-kernel routing keeps the pooled queries, the score rows and the select
-// histograms in the ring's LDS.
+// In-kernel routing keeps the pooled queries and the score rows in the ring's
+// LDS.
 template <class C>
 constexpr bool fused_route_fits(int nb) {
   const int ncol = (nb + 63) / 64 * 64;
   return nb <= kMaxBlocks &&
-         (size_t)C::QB * (C::D * 8 + ncol * 8 + 1024) <= (size_t)C::LDSB &&
+         (size_t)C::QB * (C::D * 8 + ncol * 8) <= (size_t)C::LDSB &&
          (size_t)C::QB * (C::D * 8 + C::WPQ * C::D * 8) <= (size_t)C::LDSB;
 }
 

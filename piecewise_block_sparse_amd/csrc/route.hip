@@ -28,10 +28,11 @@
 //          (The fp64 FMAs of a thread-per-centroid loop would read every qbar
 //          value from LDS once per FMA as a broadcast, which made the LDS port
 //          the bound of this phase.)
-//   select each wave takes its row's top k with a radix select over
-//          order-preserving 64-bit keys (ties at the threshold resolved to the
-//          lower block ids), stopping as soon as the keys still in play are
-//          exactly the ones it has left to take.
+//   select each wave takes its row's top k over order-preserving 64-bit keys:
+//          the k-th largest key is found bit by bit with ballot counts, from
+//          the highest bit in which the keys differ, stopping as soon as
+//          exactly k keys lie at or above the prefix (ties at the threshold
+//          resolved to the lower block ids).
 //
 // With valid lengths, block i pools its n_i valid queries, only the non-empty
 // blocks (a prefix: j < ceil(len / BLK)) are candidates, a row with fewer than
@@ -94,11 +95,10 @@ template <int D>
 __host__ __device__ constexpr int qbar_stride() { return D + 2; }
 
 // dynamic LDS layout (bytes): qbar [R][D + 2] f64 | scores [R][nbp] f64 |
-// hist [R][256] u32 | sel [R][nbp / 32] u32
+// sel [R][nbp / 32] u32
 template <int D>
 __host__ __device__ constexpr size_t route_lds_bytes(int R, int nbp) {
-  return (size_t)R * qbar_stride<D>() * 8 + (size_t)R * nbp * 8 + (size_t)R * 256 * 4 +
-         (size_t)R * (nbp / 32) * 4;
+  return (size_t)R * qbar_stride<D>() * 8 + (size_t)R * nbp * 8 + (size_t)R * (nbp / 32) * 4;
 }
 
 // A operand of 16-wide chunk t for a lane whose k index is kq: qbar[row][16 t
@@ -122,8 +122,7 @@ __global__ __launch_bounds__(64 * R) void route_kernel(const T* __restrict__ Q,
   constexpr int NT = D / 16;                             // 16-wide chunks of the head dimension
   double* s_q = reinterpret_cast<double*>(smem);
   double* s_sc = s_q + R * QS;
-  unsigned* s_hist = reinterpret_cast<unsigned*>(s_sc + R * nbp);
-  unsigned* s_sel = s_hist + R * 256;
+  unsigned* s_sel = reinterpret_cast<unsigned*>(s_sc + R * nbp);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ngr = (nb + R - 1) / R;                      // row groups per (batch, head)
@@ -240,13 +239,12 @@ __global__ __launch_bounds__(64 * R) void route_kernel(const T* __restrict__ Q,
     }
   }
   double* sc = s_sc + w * nbp;
-  unsigned* hist = s_hist + w * 256;
   unsigned* sel = s_sel + w * (nbp / 32);
   __syncthreads();
 
   // ---- top-k of this wave's row (ties to the lower block ids)
   const int kk = (ni > 0) ? min(k, nne) : 0;            // blocks this row can hold
-  select_top_k(sc, hist, sel, nbp / 64, nne, kk, lane);
+  select_top_k(sc, sel, nbp / 64, nne, kk, lane);
 
   // ---- the selected ids, written in ascending order
   if (!active) return;

@@ -1,13 +1,9 @@
 // Top-k selection of one row of fp64 scores by one wave, shared by the route
 // kernel and the attention kernel's in-kernel routing.
 //
-// Radix select over order-preserving 64-bit keys of the scores.  Lane l owns
-// candidates j = l + 64 u.  Each pass histograms the next 8-bit digit of the
-// candidates still in play, finds the digit value d* holding the k-th largest,
-// selects the candidates above it and keeps those equal to it in play.  After
-// the last pass the ones left tie exactly with the k-th largest score; the
-// lowest block ids among them fill the rest.  -0.0 is folded into +0.0 first so
-// that equal scores give equal keys.
+// Threshold search over order-preserving 64-bit keys of the scores.  Lane l
+// owns candidates j = l + 64 u.  -0.0 is folded into +0.0 first so that equal
+// scores give equal keys.
 #pragma once
 
 #include "common.hpp"
@@ -63,108 +59,101 @@ __device__ __forceinline__ unsigned long long order_key(double x) {
 
 // One wave selects the kk largest of sc[0 .. nne) (LDS, nu = ceil(columns / 64)
 // <= 32 per lane, ties to the lower index) and sets their bits in sel (LDS,
-// zeroed beforehand and ordered before this call).  hist: 256 words of LDS
-// owned by this wave.  kk <= nne.  Ends with the wave's writes to sel visible
-// to the wave.
-__device__ inline void select_top_k(const double* sc, unsigned* hist, unsigned* sel, int nu,
-                                    int nne, int kk, int lane) {
-  unsigned inplay = 0u, chosen = 0u;
+// zeroed beforehand and ordered before this call).  kk <= nne.  Ends with the
+// wave's writes to sel visible to the wave.
+//
+// The threshold T (the kk-th largest key) is found bit by bit from the highest
+// bit in which the keys differ: a bit is kept when at least kk keys are >= the
+// prefix with that bit set.  Counts are ballots of 64-bit compares, so a step
+// costs a few instructions and no LDS traffic.  As soon as exactly kk keys are
+// >= the prefix, those are the answer; otherwise the keys > T are taken and
+// the keys == T fill the rest, lowest ids first.  The first eight keys of each
+// lane stay in registers; beyond that (more than 512 candidates) they are
+// re-read from LDS at each step.
+__device__ inline void select_top_k(const double* sc, unsigned* sel, int nu, int nne, int kk,
+                                    int lane) {
+  constexpr int NRK = 8;                                 // keys held in registers per lane
+  unsigned valid = 0u;
   for (int u = 0; u < nu; ++u)
-    if (lane + 64 * u < nne) inplay |= 1u << u;
-  int krem = kk;
-  // Digits above the highest bit in which the candidates' keys differ are the
-  // same for all of them (on these scores: the sign and most of the exponent),
-  // so those passes would split nothing: start below them.
-  int top_pass = 0;
-  {
+    if (lane + 64 * u < nne) valid |= 1u << u;
+  unsigned long long kr[NRK];
+#pragma unroll
+  for (int u = 0; u < NRK; ++u)
+    kr[u] = (u < nu && ((valid >> u) & 1u)) ? order_key(sc[lane + 64 * u]) : 0ull;
+  auto key = [&](int u) { return order_key(sc[lane + 64 * u]); };   // u >= NRK
+  // number of candidates with key >= t (uniform)
+  auto count_ge = [&](unsigned long long t) {
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < NRK; ++u)
+      if (u < nu) c += __popcll(__ballot(((valid >> u) & 1u) && kr[u] >= t));
+    for (int u = NRK; u < nu; ++u) c += __popcll(__ballot(((valid >> u) & 1u) && key(u) >= t));
+    return c;
+  };
+  unsigned chosen = 0u;
+  if (kk >= nne) {
+    chosen = valid;                                      // every candidate
+  } else if (kk > 0) {
     unsigned long long kand = ~0ull, kor = 0ull;
-    for (int u = 0; u < nu; ++u)
-      if ((inplay >> u) & 1u) {
-        const unsigned long long key = order_key(sc[lane + 64 * u]);
-        kand &= key;
-        kor |= key;
+#pragma unroll
+    for (int u = 0; u < NRK; ++u)
+      if (u < nu && ((valid >> u) & 1u)) {
+        kand &= kr[u];
+        kor |= kr[u];
+      }
+    for (int u = NRK; u < nu; ++u)
+      if ((valid >> u) & 1u) {
+        const unsigned long long x = key(u);
+        kand &= x;
+        kor |= x;
       }
     kand = ((unsigned long long)wave_and((unsigned)(kand >> 32)) << 32) | wave_and((unsigned)kand);
     kor = ((unsigned long long)wave_or((unsigned)(kor >> 32)) << 32) | wave_or((unsigned)kor);
     const unsigned long long diff = kor & ~kand;          // bits that differ somewhere
-    if (diff != 0ull) top_pass = (63 - __clzll((long long)diff)) / 8;
-  }
-  for (int pass = top_pass; pass >= 0; --pass) {
-    // every candidate still in play is needed: take them all and stop early
-    int ip = 0;
-    for (int u = 0; u < nu; ++u) ip += __popcll(__ballot((inplay >> u) & 1u));
-    if (ip == krem) {
-      chosen |= inplay;
-      inplay = 0u;
-      krem = 0;
-      break;
-    }
-    const int shift = 8 * pass;
-    for (int b = lane; b < 256; b += 64) hist[b] = 0u;
-    wave_sync();
-    for (int u = 0; u < nu; ++u)
-      if ((inplay >> u) & 1u) atomicAdd(&hist[(order_key(sc[lane + 64 * u]) >> shift) & 255u], 1u);
-    wave_sync();
-    // this lane holds histogram bins 4l .. 4l + 3
-    unsigned h[4], own = 0u;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      h[e] = hist[4 * lane + e];
-      own += h[e];
-    }
-    // exclusive suffix sum over lanes: above = sum of `own` over lanes > this lane
-    unsigned above;
-    {
-      const unsigned incl = wave_prefix_sum(own, lane);  // over lanes <= this one
-      above = (unsigned)__builtin_amdgcn_readlane((int)incl, 63) - incl;
-    }
-    int dstar = -1;
-    unsigned cnt_above = 0u;
-    {
-      unsigned acc = above;                               // count of bins > 4l + 3
-#pragma unroll
-      for (int e = 3; e >= 0; --e) {
-        if (dstar < 0 && acc < (unsigned)krem && acc + h[e] >= (unsigned)krem) {
-          dstar = 4 * lane + e;
-          cnt_above = acc;
-        }
-        acc += h[e];
-      }
-    }
-    const unsigned long long who = __ballot(dstar >= 0);
-    if (who == 0ull) {                                    // krem == 0: nothing left to pick
-      dstar = 256;
-      cnt_above = 0u;
-    } else {
-      const int src = __ffsll(who) - 1;                  // uniform
-      dstar = __builtin_amdgcn_readlane(dstar, src);
-      cnt_above = (unsigned)__builtin_amdgcn_readlane((int)cnt_above, src);
-    }
-    krem -= (int)cnt_above;
-    for (int u = 0; u < nu; ++u)
-      if ((inplay >> u) & 1u) {
-        const int dg = (int)((order_key(sc[lane + 64 * u]) >> shift) & 255u);
-        if (dg > dstar) {
-          chosen |= 1u << u;
-          inplay &= ~(1u << u);
-        } else if (dg < dstar) {
-          inplay &= ~(1u << u);
+    unsigned long long t = kand;                          // all keys equal: T is that key
+    bool exact = false;
+    if (diff != 0ull) {
+      const int top = 63 - __clzll((long long)diff);
+      t = (top == 63) ? 0ull : (kand & ~((2ull << top) - 1ull));   // the common prefix
+      for (int b = top; b >= 0; --b) {
+        const unsigned long long cand = t | (1ull << b);
+        const int c = count_ge(cand);
+        if (c >= kk) t = cand;
+        if (c == kk) {
+          exact = true;
+          break;
         }
       }
-    wave_sync();
-  }
-  // exact ties with the k-th largest: lowest block ids first
-  for (int u = 0; u < nu && krem > 0; ++u) {
-    const bool tie = (inplay >> u) & 1u;
-    const unsigned long long m = __ballot(tie);
-    const int before_me = __popcll(m & ((1ull << lane) - 1));
-    if (tie && before_me < krem) chosen |= 1u << u;
-    krem -= min(krem, __popcll(m));
+    }
+    // keys above T (with `exact`, keys >= T: exactly kk of them)
+    int taken = 0;
+#pragma unroll
+    for (int u = 0; u < NRK; ++u)
+      if (u < nu && ((valid >> u) & 1u) && (exact ? kr[u] >= t : kr[u] > t)) chosen |= 1u << u;
+    for (int u = NRK; u < nu; ++u)
+      if ((valid >> u) & 1u) {
+        const unsigned long long x = key(u);
+        if (exact ? x >= t : x > t) chosen |= 1u << u;
+      }
+    if (!exact) {
+      for (int u = 0; u < nu; ++u) taken += __popcll(__ballot((chosen >> u) & 1u));
+      // exact ties with the kk-th largest: lowest block ids first
+      int krem = kk - taken;
+      auto take_ties = [&](int u, bool tie) {
+        const unsigned long long m = __ballot(tie);
+        const int before_me = __popcll(m & ((1ull << lane) - 1));
+        if (tie && before_me < krem) chosen |= 1u << u;
+        krem -= min(krem, __popcll(m));
+      };
+#pragma unroll
+      for (int u = 0; u < NRK; ++u)
+        if (u < nu && krem > 0) take_ties(u, ((valid >> u) & 1u) && kr[u] == t);
+      for (int u = NRK; u < nu && krem > 0; ++u) take_ties(u, ((valid >> u) & 1u) && key(u) == t);
+    }
   }
   for (int u = 0; u < nu; ++u)
     if ((chosen >> u) & 1u) atomicOr(&sel[(lane + 64 * u) >> 5], 1u << ((lane + 64 * u) & 31));
   wave_sync();
-
 }
 
 // The ids set in sel (nw <= 64 words), ascending, into out[0 .. kk), then -1

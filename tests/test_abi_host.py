@@ -191,10 +191,10 @@ def test_route_attention_arguments(lib):
     assert ra(lib, s, st=_lib.PisaStats(p, p, None, None, p, None)) == 1    # APPROX reads Hbar
     assert ra(lib, s, mode=_lib.MODE_ZEROTH, st=_lib.PisaStats(p, None, None, None, p, None)) == 1
     assert ra(lib, shape(dtype=_lib.DTYPE_FP32)) == 4
-    # score rows that do not fit the kernel's LDS: 64-token blocks, d = 128, nb = 1856
-    assert ra(lib, shape(L=64 * 1856)) == 2
+    # score rows that do not fit the kernel's LDS: 64-token blocks, d = 128, nb = 1921
+    assert ra(lib, shape(L=64 * 1921)) == 2
     assert b"pisa_route, then pisa_attention" in lib.pisa_last_error()
-    assert ra(lib, shape(L=64 * 896, d=64)) == 2                    # d = 64: nb <= 832
+    assert ra(lib, shape(L=64 * 961, d=64)) == 2                    # d = 64: nb <= 960
 
 
 def test_noalloc_precompute_refuses_shapes_above_its_scratch(lib):

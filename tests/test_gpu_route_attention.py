@@ -117,11 +117,11 @@ def test_random_small_configurations(torch, seed):
         check_attention(to_np(outs[m]), ref, "bf16", name=f"{name}/{m}")
 
 
-@pytest.mark.parametrize("d,B,nb,k", [(128, 64, 1792, 200), (64, 64, 832, 100),
+@pytest.mark.parametrize("d,B,nb,k", [(128, 64, 1920, 200), (64, 64, 960, 100),
                                       (128, 128, 2048, 300), (64, 128, 2048, 64)])
 def test_largest_block_counts(torch, d, B, nb, k):
-    """The largest nb each configuration's LDS holds (score rows of 1792 and
-    832 blocks for query-block pairs, 2048 otherwise): same selection and
+    """The largest nb each configuration's LDS holds (score rows of 1920 and
+    960 blocks for query-block pairs, 2048 otherwise): same selection and
     outputs as the split path; one block more is refused on the host."""
     pisa = pisa_mod()
     L = nb * B
