@@ -485,163 +485,207 @@ __global__ __launch_bounds__(256) void frob_kernel(const float* __restrict__ Hbu
 
 // ---- spectral reading of M_j = ||H_j - Hbar||_2: the largest singular value
 //
-// One workgroup per block.  A = H_j - Hbar is staged in LDS (rows padded to
-// D + 4 floats, so the row reads of A v are conflict-free 16-byte reads and the
-// column reads of A^T u conflict-free 4-byte reads).  kLanczos steps of plain
-// Lanczos on A^T A from a fixed start vector give a tridiagonal T whose largest
+// One workgroup per block, A = H_j - Hbar held in registers: thread (tr, tc)
+// owns the 8 x 8 tile of rows 8 tr .. 8 tr + 7 and columns 8 tc .. 8 tc + 7
+// (D / 8 tiles a side; D = 128: four waves, a tile row per 16 lanes; D = 64:
+// one wave, a tile row per 8 lanes).  kLanczos steps of plain Lanczos on
+// A^T A from a fixed start vector give a tridiagonal T whose largest
 // eigenvalue approximates sigma_max^2 from below; without reorthogonalisation
 // the extreme eigenvalue still converges (lost orthogonality only repeats
-// converged values).  Wave 0 then finds lambda_max(T) by multisection on Sturm
-// counts in fp64 (64 points per round, 6 rounds: 65^6 > 7e10), and
-// M_j = sqrt(lambda_max).
-// Reductions run in a fixed order, so the result is bitwise reproducible.
+// converged values).  Per step, u = A v sums each tile row across its lanes
+// (DPP), w = A^T u sums each tile column across the wave's rows and then
+// across the waves (one LDS exchange, double-buffered: one barrier per step);
+// every thread then holds u for its tile's rows and v, w for its tile's
+// columns, so the dot products need no further exchange.  All threads then
+// find lambda_max(T) by multisection on Sturm counts in fp64 (one point per
+// thread and round: 4 rounds of 256 points, or 6 of 64 for d = 64), and
+// M_j = sqrt(lambda_max).  Every sum runs in a fixed order, so the result is
+// bitwise reproducible.
 constexpr int kLanczos = 24;
 
-template <int NT>
-__device__ __forceinline__ float block_sum(float x, float* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) s += red[i];
-  __syncthreads();
-  return s;
+// x + x of another lane, by DPP within rows of 16 lanes (the permutations are
+// involutions, so both lanes of a pair form the same sum)
+template <int CTRL>
+__device__ __forceinline__ float dpp_pair_sum(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// sum over a tile row: the NL consecutive lanes (NL = 8 or 16) holding it
+template <int NL>
+__device__ __forceinline__ float tile_row_sum(float x) {
+  x = dpp_pair_sum<0xB1>(x);                       // quad_perm [1,0,3,2]: lane ^ 1
+  x = dpp_pair_sum<0x4E>(x);                       // quad_perm [2,3,0,1]: lane ^ 2
+  x = dpp_pair_sum<0x141>(x);                      // row_half_mirror: the other quad of 8
+  if (NL == 16) x = dpp_pair_sum<0x140>(x);        // row_mirror: the other 8 of 16
+  return x;
+}
+
+// sum over the lanes l ^ m for every m the mask covers above NL (the wave's
+// tile rows that share this lane's tile column)
+template <int NL>
+__device__ __forceinline__ float tile_col_sum_wave(float x) {
+  if (NL == 8) x += __shfl_xor(x, 8);
+  x += __shfl_xor(x, 16);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);   // lanes l and l ^ 32: same order
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void spectral_kernel(const float* __restrict__ H,
-                                                       const float* __restrict__ hbar, int nb,
-                                                       float* __restrict__ M, const int32_t* lens,
-                                                       int heads, int BLK) {
-  constexpr int NT = 256, LD = D + 4, NH = NT / D, CW = D / NH;
-  __shared__ __attribute__((aligned(16))) float A[D * LD];
-  __shared__ __attribute__((aligned(16))) float v[D];
-  __shared__ float vp[D], u[D], part[NT], red[NT / 64];
+__global__ __launch_bounds__(D * D / 64, 4) void spectral_kernel(const float* __restrict__ H,
+                                                              const float* __restrict__ hbar, int nb,
+                                                              float* __restrict__ M,
+                                                              const int32_t* lens, int heads,
+                                                              int BLK) {
+  constexpr int T = D / 8, NT = T * T, NWV = NT / 64, NL = (T < 16) ? T : 16;
+  __shared__ float xch[2][NWV][D];                 // per-wave column partials of A^T u
   __shared__ float s_al[kLanczos], s_be[kLanczos];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tr = tid / T, tc = tid % T;
   const int blk = blockIdx.x, bh = blk / nb;
   if (block_count(valid_len(lens, bh, heads, nb * BLK), blk - bh * nb, BLK) == 0) {
     if (tid == 0) M[blk] = 0.f;                   // empty block: never routed
     return;
   }
-  const float* Hj = H + (size_t)blk * D * D;
-  const float* Hb = hbar + (size_t)bh * D * D;
-  for (int e = 4 * tid; e < D * D; e += 4 * NT) {
-    const f32x4 h = *reinterpret_cast<const f32x4*>(Hj + e);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(Hb + e);
-    *reinterpret_cast<f32x4*>(&A[(e / D) * LD + e % D]) = h - b;
+  const float* Hj = H + (size_t)blk * D * D + (size_t)(8 * tr) * D + 8 * tc;
+  const float* Hb = hbar + (size_t)bh * D * D + (size_t)(8 * tr) * D + 8 * tc;
+  float A[8][8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const f32x4 h = *reinterpret_cast<const f32x4*>(Hj + r * D + 4 * hf);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(Hb + r * D + 4 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) A[r][4 * hf + e] = h[e] - b[e];
+    }
+  // start vector on this tile's columns
+  float v[8], vp[8];
+  float n0 = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    v[e] = 1.f + (float)((unsigned)(8 * tc + e) * 2654435761u % 1024u) * (1.f / 1024.f);
+    n0 = fmaf(v[e], v[e], n0);
+    vp[e] = 0.f;
   }
-  const int r = tid % D, h = tid / D;            // row (or column) and which slice of it
-  float x0 = 0.f;
-  if (tid < D) x0 = 1.f + (float)((unsigned)tid * 2654435761u % 1024u) * (1.f / 1024.f);
-  const float n0 = block_sum<NT>(x0 * x0, red);
-  if (tid < D) {
-    v[tid] = x0 / sqrtf(n0);
-    vp[tid] = 0.f;
-  }
-  __syncthreads();
+  n0 = tile_row_sum<NL>(n0);
+  const float inv0 = 1.f / sqrtf(n0);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] *= inv0;
   float beta = 0.f;
   int kk = 0;
   for (int it = 0; it < kLanczos; ++it) {
-    // u = A v: thread (r, h) sums columns h*CW .. h*CW + CW - 1 of row r
-    f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};             // four independent FMA chains
-    {
-      const float* Ar = &A[r * LD + h * CW];
-      const float* vv = &v[h * CW];
+    // u = A v on this tile's rows
+    float u[8];
 #pragma unroll
-      for (int c = 0; c < CW; c += 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(Ar + c);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(vv + c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc4[e] = fmaf(a[e], b[e], acc4[e]);
-      }
-    }
-    part[tid] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
-    __syncthreads();
-    if (tid < D) {
+    for (int r = 0; r < 8; ++r) {
       float t = 0.f;
 #pragma unroll
-      for (int q = 0; q < NH; ++q) t += part[q * D + tid];
-      u[tid] = t;
+      for (int e = 0; e < 8; ++e) t = fmaf(A[r][e], v[e], t);
+      u[r] = tile_row_sum<NL>(t);
     }
-    __syncthreads();
-    // w = A^T u: thread (c = r, h) sums rows h*CW .. h*CW + CW - 1 of column c
-    acc4 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int rr = h * CW; rr < h * CW + CW; rr += 4) {
+    // w = A^T u on this tile's columns: this wave's rows, then all waves
+    float w[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc4[e] = fmaf(A[(rr + e) * LD + r], u[rr + e], acc4[e]);
-    }
-    part[tid] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
-    __syncthreads();
-    float w = 0.f, vc = 0.f;
-    if (tid < D) {
+    for (int e = 0; e < 8; ++e) {
+      float t = 0.f;
 #pragma unroll
-      for (int q = 0; q < NH; ++q) w += part[q * D + tid];
-      vc = v[tid];
+      for (int r = 0; r < 8; ++r) t = fmaf(A[r][e], u[r], t);
+      w[e] = tile_col_sum_wave<NL>(t);
     }
-    const float alpha = block_sum<NT>(vc * w, red);
-    if (tid < D) w = w - alpha * vc - beta * vp[tid];
-    const float bnew = sqrtf(block_sum<NT>(w * w, red));
+    if constexpr (NWV > 1) {
+      float* x = xch[it & 1][wv];
+      if (lane < T)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[8 * tc + e] = w[e];
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float t = xch[it & 1][0][8 * tc + e];
+#pragma unroll
+        for (int q = 1; q < NWV; ++q) t += xch[it & 1][q][8 * tc + e];
+        w[e] = t;
+      }
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot = fmaf(v[e], w[e], dot);
+    const float alpha = tile_row_sum<NL>(dot);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      w[e] = w[e] - alpha * v[e] - beta * vp[e];
+      ss = fmaf(w[e], w[e], ss);
+    }
+    const float bnew = sqrtf(tile_row_sum<NL>(ss));
     if (tid == 0) {
       s_al[it] = alpha;
       s_be[it] = bnew;
     }
     kk = it + 1;
-    if (!(bnew > 1e-6f * fabsf(alpha))) break;      // invariant subspace (or A = 0)
-    if (tid < D) {
-      vp[tid] = vc;
-      v[tid] = w / bnew;
+    if (!(bnew > 1e-6f * fabsf(alpha))) break;      // invariant subspace (or A = 0); uniform
+    const float ib = 1.f / bnew;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      vp[e] = v[e];
+      v[e] = w[e] * ib;
     }
     beta = bnew;
-    __syncthreads();
   }
   __syncthreads();
-  if (tid < 64) {
-    // lambda_max of the kk x kk tridiagonal (diag s_al, off-diag s_be) by
-    // multisection: count(x) = number of eigenvalues below x = number of
-    // negative pivots of T - x I; lanes with count < kk lie below lambda_max.
-    const int lane = tid;
-    double hi = 0.0;
-    for (int i = 0; i < kk; ++i) {
-      double g = fabs((double)s_al[i]);
-      if (i > 0) g += fabs((double)s_be[i - 1]);
-      if (i + 1 < kk) g += fabs((double)s_be[i]);
-      hi = fmax(hi, g);
-    }
-    double lo = 0.0;                               // A^T A is positive semidefinite
-    for (int round = 0; round < 6; ++round) {
-      const double step = (hi - lo) / 65.0;
-      const double x = lo + step * (lane + 1);
-      int cnt = 0;
-      double dd = 1.0;
-      for (int i = 0; i < kk; ++i) {
-        const double b2 = (i > 0) ? (double)s_be[i - 1] * (double)s_be[i - 1] : 0.0;
-        dd = ((double)s_al[i] - x) - (i > 0 ? b2 / dd : 0.0);
-        if (dd == 0.0) dd = -1e-300;
-        cnt += dd < 0.0;
-      }
-      const unsigned long long below = __ballot(cnt < kk);
-      if (below == 0ull) {
-        hi = lo + step;
-      } else {
-        const int l = 63 - __clzll(below);
-        const double nlo = lo + step * (l + 1);
-        hi = (l == 63) ? hi : lo + step * (l + 2);
-        lo = nlo;
-      }
-    }
-    if (lane == 0) M[blk] = (float)sqrt(0.5 * (lo + hi));
+  // lambda_max of the kk x kk tridiagonal (diag s_al, off-diag s_be) by
+  // multisection over all NT threads: count(x) = number of eigenvalues below x
+  // = number of negative pivots of T - x I, nondecreasing in x, so the points
+  // with count < kk (below lambda_max) form a prefix; the interval shrinks to
+  // the gap after its last point.  (NT + 1)^rounds > 4e9 either way.
+  constexpr int ROUNDS = (NT >= 256) ? 4 : 6;
+  __shared__ unsigned long long s_below[2][NWV];
+  double hi = 0.0;
+  for (int i = 0; i < kk; ++i) {
+    double g = fabs((double)s_al[i]);
+    if (i > 0) g += fabs((double)s_be[i - 1]);
+    if (i + 1 < kk) g += fabs((double)s_be[i]);
+    hi = fmax(hi, g);
   }
+  double lo = 0.0;                                 // A^T A is positive semidefinite
+  for (int round = 0; round < ROUNDS; ++round) {
+    const double step = (hi - lo) / (double)(NT + 1);
+    const double x = lo + step * (tid + 1);
+    int cnt = 0;
+    double dd = 1.0;
+    for (int i = 0; i < kk; ++i) {
+      const double b2 = (i > 0) ? (double)s_be[i - 1] * (double)s_be[i - 1] : 0.0;
+      dd = ((double)s_al[i] - x) - (i > 0 ? b2 / dd : 0.0);
+      if (dd == 0.0) dd = -1e-300;
+      cnt += dd < 0.0;
+    }
+    const unsigned long long below = __ballot(cnt < kk);
+    int l = -1;                                    // last point below lambda_max
+    if constexpr (NWV > 1) {
+      if (lane == 0) s_below[round & 1][wv] = below;
+      __syncthreads();
+      for (int q = NWV - 1; q >= 0 && l < 0; --q) {
+        const unsigned long long m = s_below[round & 1][q];
+        if (m != 0ull) l = 64 * q + 63 - __clzll(m);
+      }
+    } else {
+      if (below != 0ull) l = 63 - __clzll(below);
+    }
+    if (l < 0) {
+      hi = lo + step;
+    } else {
+      const double nlo = lo + step * (l + 1);
+      hi = (l == NT - 1) ? hi : lo + step * (l + 2);
+      lo = nlo;
+    }
+  }
+  if (tid == 0) M[blk] = (float)sqrt(0.5 * (lo + hi));
 }
 
 template <int D>
 hipError_t launch_spectral(const float* H, const float* hbar, int bh, int nb, float* M,
                            const StatsArgs& a) {
-  hipLaunchKernelGGL((spectral_kernel<D>), dim3(bh * nb), dim3(256), 0, a.stream, H, hbar, nb, M,
-                     a.lens, a.heads, a.BLK);
+  hipLaunchKernelGGL((spectral_kernel<D>), dim3(bh * nb), dim3(D * D / 64), 0, a.stream, H, hbar, nb,
+                     M, a.lens, a.heads, a.BLK);
   return hipGetLastError();
 }
 
