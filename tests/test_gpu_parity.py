@@ -190,6 +190,38 @@ def test_spectral_M_parity(torch, wid):
     assert np.all(g <= to_np(fro["M"])[:, heads] * (1 + 1e-5))
 
 
+@pytest.mark.parametrize("dtype,d,B,nb", [("bf16", 64, 128, 9), ("bf16", 128, 64, 13),
+                                          ("fp32", 128, 128, 5), ("fp32", 64, 64, 11)])
+def test_spectral_M_small_shapes(torch, dtype, d, B, nb):
+    """Spectral M_j on both head dims and block sizes, batch 2 with a second
+    sequence that ends inside a block and leaves empty blocks (M = 0 there),
+    against the oracle's SVD; one head whose H_j are rank one (within a block
+    every value row is one vector times a power of two, exact in bf16), and one
+    head with V = 0 (every H_j = Hbar = 0, so M = 0 exactly)."""
+    pisa = pisa_mod()
+    L = nb * B
+    lens = [L, L - 3 * B - 5]
+    K = _rand(torch, (2, 3, L, d), dtype, 81)
+    V = _rand(torch, (2, 3, L, d), dtype, 82)
+    c = np.random.default_rng(83).choice([-2.0, -1.0, -0.5, 0.5, 1.0, 2.0], size=(2, L, 1))
+    V[:, 1] = (c * np.repeat(V[:, 1, ::B], B, axis=1)).astype(np.float32)   # rank-one H_j
+    V[:, 2] = 0.0
+    Kd, Vd = (to_dev(x, dtype) for x in (K, V))
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    st = pisa.precompute(Kd, Vd, B, norm="spectral", seq_lens=sl)
+    torch.cuda.synchronize()
+    ref = oracle.precompute(K, V, B, norm="spectral", seq_lens=lens)["M"]
+    g = to_np(st["M"])
+    assert np.all(g[:, 2] == 0.0)
+    nne = (lens[1] + B - 1) // B
+    assert np.all(g[1, :, nne:] == 0.0)
+    live = ref > 1e-6 * ref.max()
+    mrel = float(np.max(np.abs(g - ref)[live] / ref[live]))
+    print(f"spectral {dtype}/d{d}/B{B}: max rel {mrel:.3e}")
+    assert mrel <= SPECTRAL_MAX_REL
+    assert np.all(np.abs(g - ref)[~live] <= 1e-6 * ref.max())
+
+
 @pytest.mark.parametrize("wid", [2, 3])
 def test_route_with_spectral_M(torch, wid):
     """Routing on the spectral M_j: bit-exact with the oracle's top-k of the same
