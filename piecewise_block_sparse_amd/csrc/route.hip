@@ -45,12 +45,17 @@ namespace pisa {
 namespace {
 
 
+// The queries are read once: their loads carry the non-temporal hint, so the
+// Q stream does not push the head's centroids (read by every row group) out of
+// L2 (video-DiT-L: 80-82 us against 86-87 us with plain loads).
 template <typename T>
 struct Chunk8;
 template <>
 struct Chunk8<bf16> {
   typedef u32x4 raw;
-  __device__ static raw load(const bf16* p) { return ld16(p); }
+  __device__ static raw load(const bf16* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
   __device__ static void add(double (&x)[8], const raw& r) {
     const bf16x8 v = as_bf16x8(r);
 #pragma unroll
@@ -61,7 +66,8 @@ template <>
 struct Chunk8<float> {
   struct raw { f32x4 a, b; };
   __device__ static raw load(const float* p) {
-    return raw{*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4)};
+    return raw{__builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p)),
+               __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4))};
   }
   __device__ static void add(double (&x)[8], const raw& r) {
 #pragma unroll
