@@ -17,7 +17,8 @@ after a 512 MB scratch write (caches flushed); `density_sweep` re-routes the sam
 inputs at top-k 128 / 64 / 32 / 16 of 256 blocks and times both modes; `orders`
 times the zeroth-order and the per-block first-order treatments of the
 unselected blocks on the same inputs; `route_attention_fused` times the
-single-launch routing-and-attention call against the two calls it replaces;
+routing-and-attention call (its automatic form, and the in-kernel routing form
+forced) against the two calls it replaces;
 `secondary` holds the other workloads: the small video one (whole steps), the
 short image one (whole steps, dense comparator) and the multimodal one with its
 fixed text/image block mask (PISA and keep-or-drop, dense comparator);
@@ -259,20 +260,26 @@ def time_attention(pisa, torch, Qd, Kd, Vd, idx, st, w, mode, reps):
 
 
 def time_route_attention(pisa, torch, Qd, Kd, Vd, st, w, reps):
-    """The in-kernel routing call (route and attention in one launch) and the
-    two calls it replaces, each timed the same way: back-to-back calls between
-    two HIP events, the two forms alternated twice (best of each kept)."""
+    """The routing-and-attention call in its automatic form (in-kernel routing
+    while the work fits one round of workgroups, else two launches), with the
+    in-kernel form forced, and the two calls it replaces, each timed the same
+    way: back-to-back calls between two HIP events, the forms alternated twice
+    (best of each kept).  Returns the three times in ms."""
     stream = torch.cuda.current_stream()
 
     def fused():
         pisa.route_attention(Qd, Kd, Vd, st, w.k, w.lam, w.block, mode="approx")
+
+    def in_kernel():
+        pisa.route_attention(Qd, Kd, Vd, st, w.k, w.lam, w.block, mode="approx", form="in_kernel")
 
     def split():
         idx = pisa.route(Qd, st, w.k, w.lam, w.block)
         pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode="approx")
 
     best = {}
-    for name, fn in (("fused", fused), ("split", split), ("fused", fused), ("split", split)):
+    for name, fn in (("fused", fused), ("in_kernel", in_kernel), ("split", split),
+                     ("fused", fused), ("in_kernel", in_kernel), ("split", split)):
         for _ in range(2):
             fn()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -282,7 +289,7 @@ def time_route_attention(pisa, torch, Qd, Kd, Vd, st, w, reps):
         b.record(stream)
         b.synchronize()
         best[name] = min(best.get(name, 1e30), a.elapsed_time(b) / reps)
-    return best["fused"], best["split"]
+    return best["fused"], best["in_kernel"], best["split"]
 
 
 def fixed_mask(pisa, torch, steps, warmup):
@@ -544,9 +551,10 @@ def main():
             res["approx_phase_ms"] = ph["attention"] - t_drop
             res["tflops"]["exact_phase"] = f["exact"] / t_drop / 1e9
             res["roofline_frac"]["exact_phase"] = res["tflops"]["exact_phase"] / MFMA_BF16_PEAK_TFLOPS
-            t_fused, t_split = time_route_attention(pisa, torch, Qd, Kd, Vd, st, w, max(5, steps // 2))
+            t_fused, t_ink, t_split = time_route_attention(pisa, torch, Qd, Kd, Vd, st, w,
+                                                           max(5, steps // 2))
             res["route_attention_fused"] = {
-                "ms": t_fused, "route_plus_attention_ms": t_split,
+                "ms": t_fused, "in_kernel_ms": t_ink, "route_plus_attention_ms": t_split,
                 "step_ms_with_fused": ph["precompute"] + t_fused}
         res["gbs"] = {"precompute": by["stats"] / ph["precompute"] / 1e6,
                       "route": by["route"] / ph["route"] / 1e6}

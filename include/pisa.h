@@ -48,8 +48,9 @@
 extern "C" {
 #endif
 
-#define PISA_VERSION 102 /* major * 100 + minor; 1.01 adds pisa_route_attention, 1.02
-                            pisa_precompute_noalloc and pisa_attention_split */
+#define PISA_VERSION 103 /* major * 100 + minor; 1.01 adds pisa_route_attention, 1.02
+                            pisa_precompute_noalloc and pisa_attention_split, 1.03 the
+                            form argument of pisa_route_attention */
 
 typedef enum {
   PISA_OK = 0,
@@ -76,6 +77,16 @@ typedef enum {
                                order avoids these per-block terms because each needs its own
                                d x d matrix) */
 } pisa_mode;
+
+/* How pisa_route_attention runs (the selection and the output are the same
+ * bit for bit in every form). */
+typedef enum {
+  PISA_ROUTE_AUTO = 0,         /* IN_KERNEL when idx is NULL or when the call's work items fit
+                                  one round of resident workgroups; TWO_LAUNCH otherwise     */
+  PISA_ROUTE_IN_KERNEL = 1,    /* each attention workgroup routes its own query block(s)    */
+  PISA_ROUTE_TWO_LAUNCH = 2    /* the route kernel writes idx, then the attention kernel reads
+                                  it (idx required)                                          */
+} pisa_route_form;
 
 typedef enum {
   PISA_NORM_FROBENIUS = 0,  /* M_j = ||H_j - Hbar||_F (entrywise 2-norm)                    */
@@ -295,13 +306,22 @@ pisa_status pisa_attention_split(const pisa_shape* shape, const void* Q, const v
                                  size_t workspace_bytes, void* stream);
 
 /*
- * pisa_route_attention -- routing and attention in one kernel (PISA summary,
+ * pisa_route_attention -- routing and attention in one call (PISA summary,
  * section 2, "Covariance-aware routing" for the selection and "Hardware
- * implementation" for the stages).  Each workgroup routes its own query
- * block(s) exactly as pisa_route does (same fp64 pooled query, scores and
- * top-k, so the selection is identical bit for bit) and then runs the
- * attention of pisa_attention on that selection; no idx round trip through
- * memory and no separate routing launch.
+ * implementation" for the stages).  In the in-kernel form each attention
+ * workgroup routes its own query block(s) exactly as pisa_route does (same
+ * fp64 pooled query, scores and top-k, so the selection is identical bit for
+ * bit) and then runs the attention of pisa_attention on that selection: no
+ * idx round trip through memory and no separate routing launch.  The
+ * two-launch form runs pisa_route into idx, then pisa_attention on it.  Both
+ * give the same selection and the same O bit for bit.  In-kernel routing wins
+ * when the call's work items (one per query block, or per pair of query
+ * blocks with 64-token blocks) fit one round of resident workgroups: the
+ * separate launch and its pass over Q are then a large share of a short call.
+ * Over several rounds every workgroup scoring all nb centroids for one query
+ * block costs more than the route kernel, which scores eight query blocks per
+ * workgroup, so PISA_ROUTE_AUTO switches to two launches there (it needs idx
+ * to hold the selection between them).
  *
  *   Q, K, V   [b,h,L,d] bf16 (device)
  *   stats     centroid and M (routing), plus what pisa_attention reads in `mode`
@@ -311,18 +331,23 @@ pisa_status pisa_attention_split(const pisa_shape* shape, const void* Q, const v
  *   scale     the routing score uses it as given (float64); the attention uses
  *             (float)scale, as pisa_attention with that value
  *   idx       NULLABLE out: int32 [b,h,nb,k], the selection, as pisa_route
- *             writes it (ascending, -1 after fewer than k candidates)
+ *             writes it (ascending, -1 after fewer than k candidates);
+ *             required for PISA_ROUTE_TWO_LAUNCH
  *   O         out: [b,h,L,d] bf16 (device)
+ *   form      pisa_route_form
  *
  * Errors as pisa_route and pisa_attention, and: PISA_ERR_DTYPE for fp32
- * inputs, PISA_ERR_ARG for PISA_MODE_FIRST, PISA_ERR_SHAPE for nb above what
- * the kernel's LDS holds for the score rows (d = 128: nb <= 2048 with
- * 128-token blocks, nb <= 1920 with 64-token blocks; d = 64: nb <= 2048 and
- * 960); the caller then uses pisa_route and pisa_attention.
+ * inputs, PISA_ERR_ARG for PISA_MODE_FIRST or an unknown form, PISA_ERR_NULL
+ * for PISA_ROUTE_TWO_LAUNCH without idx, PISA_ERR_SHAPE when the in-kernel
+ * form would run with nb above what the kernel's LDS holds for the score rows
+ * (d = 128: nb <= 2048 with 128-token blocks, nb <= 1920 with 64-token blocks;
+ * d = 64: nb <= 2048 and 960); PISA_ROUTE_AUTO with idx takes two launches
+ * there instead.
  */
 pisa_status pisa_route_attention(const pisa_shape* shape, const void* Q, const void* K,
                                  const void* V, const pisa_stats* stats, int32_t k, double lambda,
-                                 int32_t mode, double scale, int32_t* idx, void* O, void* stream);
+                                 int32_t mode, double scale, int32_t* idx, void* O, int32_t form,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

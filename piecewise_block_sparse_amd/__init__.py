@@ -220,12 +220,20 @@ def attention_split_workspace_size(X, block: int, kmax: int, split_blocks: int) 
                                                            int(split_blocks))
 
 
+_ROUTE_FORMS = {"auto": _lib.ROUTE_AUTO, "in_kernel": _lib.ROUTE_IN_KERNEL,
+                "two_launch": _lib.ROUTE_TWO_LAUNCH}
+
+
 def route_attention(Q, K, V, stats: dict, k: int, lam: float, block: int,
                     mode: int | str = "approx", scale: float | None = None, out=None,
-                    seq_lens=None, return_idx: bool = False):
-    """Routing and attention in one kernel (bf16): the selection of route()
-    (bit for bit) followed by attention() on it, without the idx round trip.
-    Modes "approx", "zeroth" and "drop".  With return_idx, returns (O, idx)."""
+                    seq_lens=None, return_idx: bool = False, form: str = "auto"):
+    """Routing and attention in one call (bf16): the selection of route()
+    (bit for bit) followed by attention() on it.  form "in_kernel": each
+    attention workgroup routes its own query block(s), no idx round trip;
+    "two_launch": route() then attention(); "auto" (default): in-kernel while
+    the work fits one round of workgroups, else two launches (the same
+    selection and output either way).  Modes "approx", "zeroth" and "drop".
+    With return_idx, returns (O, idx)."""
     torch = _torch()
     lib = _lib.load()
     _same(Q, K, V)
@@ -244,13 +252,16 @@ def route_attention(Q, K, V, stats: dict, k: int, lam: float, block: int,
     pk = stats.get("packed")
     if pk is not None and pk.numel() != lib.pisa_packed_size(ctypes.byref(shp)):
         raise ValueError("stats['packed'] does not match this shape")
+    if form not in _ROUTE_FORMS:
+        raise ValueError(f"unknown form {form!r}")
+    # the automatic form may need idx to hold the selection between two launches
     idx = (torch.empty((b, h, nb, max(k, 0)), dtype=torch.int32, device=Q.device)
-           if return_idx else None)
+           if return_idx or form != "in_kernel" else None)
     O = torch.empty_like(Q) if out is None else out
     _same(Q, O)
     st = _lib.PisaStats(_ptr(stats["centroid"]), _ptr(stats.get("vsum")), None,
                         _ptr(stats.get("Hbar")), _ptr(stats["M"]), _ptr(pk), None)
     _lib.check("pisa_route_attention", lib.pisa_route_attention(
         ctypes.byref(shp), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(st), int(k), float(lam),
-        int(mode), scale, _ptr(idx), _ptr(O), _stream(Q)))
+        int(mode), scale, _ptr(idx), _ptr(O), _ROUTE_FORMS[form], _stream(Q)))
     return (O, idx) if return_idx else O

@@ -20,6 +20,9 @@ MODE_APPROX = 0
 MODE_DROP = 1
 MODE_ZEROTH = 2
 MODE_FIRST = 3
+ROUTE_AUTO = 0
+ROUTE_IN_KERNEL = 1
+ROUTE_TWO_LAUNCH = 2
 NORM_FROBENIUS = 0
 NORM_SPECTRAL = 1
 
@@ -88,7 +91,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                          vp, sz, vp]
     lib.pisa_route_attention.restype = i32
     lib.pisa_route_attention.argtypes = [sp, vp, vp, vp, stp, i32, ctypes.c_double, i32,
-                                         ctypes.c_double, vp, vp, vp]
+                                         ctypes.c_double, vp, vp, i32, vp]
     _lib = lib
     return lib
 

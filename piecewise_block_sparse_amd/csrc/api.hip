@@ -284,13 +284,18 @@ pisa_status pisa_attention_split(const pisa_shape* shape, const void* Q, const v
 
 pisa_status pisa_route_attention(const pisa_shape* shape, const void* Q, const void* K,
                                  const void* V, const pisa_stats* stats, int32_t k, double lambda,
-                                 int32_t mode, double scale, int32_t* idx, void* O, void* stream) {
+                                 int32_t mode, double scale, int32_t* idx, void* O, int32_t form,
+                                 void* stream) {
   g_err[0] = 0;
   int bh = 0, nb = 0;
   pisa_status st = check_shape(shape, &bh, &nb);
   if (st != PISA_OK) return st;
   if (!Q || !K || !V || !O || !stats || !stats->centroid || !stats->M)
     return fail(PISA_ERR_NULL, "Q, K, V, O and stats centroid and M are required");
+  if (form != PISA_ROUTE_AUTO && form != PISA_ROUTE_IN_KERNEL && form != PISA_ROUTE_TWO_LAUNCH)
+    return fail(PISA_ERR_ARG, "unknown form %d", form);
+  if (form == PISA_ROUTE_TWO_LAUNCH && !idx)
+    return fail(PISA_ERR_NULL, "the two-launch form needs idx for the selection");
   if (shape->dtype != PISA_DTYPE_BF16)
     return fail(PISA_ERR_DTYPE, "in-kernel routing is built for bf16 inputs");
   if (mode == PISA_MODE_FIRST)
@@ -301,15 +306,36 @@ pisa_status pisa_route_attention(const pisa_shape* shape, const void* Q, const v
   if (!std::isfinite(scale) || !(scale > 0.0) || !((float)scale > 0.f) || !std::isfinite((float)scale))
     return fail(PISA_ERR_ARG, "scale must be finite and positive");
   if (!std::isfinite(lambda)) return fail(PISA_ERR_ARG, "lambda must be finite");
-  const int maxnb = pisa::fused_route_max_blocks(shape->head_dim, shape->block);
-  if (nb > maxnb)
-    return fail(PISA_ERR_SHAPE, "nb=%d above %d for in-kernel routing at d=%d, block=%d: "
-                "use pisa_route, then pisa_attention", nb, maxnb, shape->head_dim, shape->block);
   const bool approx = mode != PISA_MODE_DROP;
   if (approx && !stats->vsum) return fail(PISA_ERR_NULL, "modes other than DROP need stats vsum");
   if (mode == PISA_MODE_APPROX && !stats->Hbar)
     return fail(PISA_ERR_NULL, "APPROX mode needs stats Hbar");
+  const int maxnb = pisa::fused_route_max_blocks(shape->head_dim, shape->block);
+  bool two = form == PISA_ROUTE_TWO_LAUNCH;
+  if (form == PISA_ROUTE_AUTO && idx) {
+    // in-kernel routing only while the work items fit one round of workgroups
+    const int resident = pisa::fused_route_resident(shape->head_dim, shape->block);
+    two = nb > maxnb ||
+          (resident > 0 && pisa::fused_route_items(shape->head_dim, shape->block, bh, nb) > resident);
+  }
+  if (!two && nb > maxnb)
+    return fail(PISA_ERR_SHAPE, "nb=%d above %d for in-kernel routing at d=%d, block=%d: "
+                "use pisa_route, then pisa_attention", nb, maxnb, shape->head_dim, shape->block);
   const int order = mode == PISA_MODE_ZEROTH ? pisa::kOrderZeroth : pisa::kOrderMixed;
+  if (two) {
+    // pisa_route into idx, then pisa_attention on it (scale as the in-kernel form uses it)
+    pisa::RouteArgs r{Q, stats->centroid, stats->M, k, scale, lambda, idx, bh, nb, shape->head_dim,
+                      shape->block, shape->seq_lens, shape->heads, (hipStream_t)stream};
+    const pisa_status rs = hip_status(pisa::launch_route_bf16(r), "pisa_route_attention (routing)");
+    if (rs != PISA_OK) return rs;
+    pisa::AttnArgs a{Q, K, V, idx, k,
+                     approx ? stats->centroid : nullptr, approx ? stats->vsum : nullptr,
+                     mode == PISA_MODE_APPROX ? stats->Hbar : nullptr,
+                     approx ? stats->packed : nullptr, nullptr, nullptr,
+                     approx ? 1 : 0, order, (float)scale, O, bh, nb, shape->head_dim, shape->block,
+                     shape->seq_lens, shape->heads, (hipStream_t)stream};
+    return hip_status(pisa::launch_attn_bf16(a), "pisa_route_attention (attention)");
+  }
   pisa::AttnArgs a{Q, K, V, nullptr, k,
                    stats->centroid, approx ? stats->vsum : nullptr,
                    mode == PISA_MODE_APPROX ? stats->Hbar : nullptr,

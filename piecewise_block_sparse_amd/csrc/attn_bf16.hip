@@ -31,6 +31,8 @@
 // picks the keys that the lane's P registers hold, so P feeds the MFMA as is.
 // PISA's zeroth-order sweep streams the bf16 centroid / value-sum pack through
 // the same ring (a centroid chunk has the layout of a K / V chunk).
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "lds_stream.hpp"
@@ -1126,6 +1128,58 @@ int fused_route_max_blocks(int D, int BLK) {
   }
   return best;
 }
+
+namespace {
+int fused_route_resident_query(int D, int BLK);
+
+template <class C>
+int resident_of(const void* kern) {
+  int dev = 0, per_cu = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, C::NT, 0) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return per_cu * cus;
+}
+}  // namespace
+
+int fused_route_items(int D, int BLK, int bh, int nb) {
+  const int qb = (BLK == 64) ? 2 : 1;                   // query blocks per workgroup (see launch_attn_bf16)
+  (void)D;
+  return bh * ((nb + qb - 1) / qb);
+}
+
+int fused_route_resident(int D, int BLK) {
+  // answered once per device and configuration (the occupancy of a kernel
+  // on a device does not change)
+  constexpr int kDevs = 64;
+  static std::atomic<int> cache[kDevs][4];
+  const int cfg = (D == 128 ? 0 : 2) + (BLK == 64 ? 0 : 1);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kDevs) {
+    const int c = cache[dev][cfg].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  const int r = fused_route_resident_query(D, BLK);
+  if (r > 0 && dev >= 0 && dev < kDevs) cache[dev][cfg].store(r, std::memory_order_relaxed);
+  return r;
+}
+
+namespace {
+int fused_route_resident_query(int D, int BLK) {
+  // the in-kernel routing instantiations launch_t picks (without valid lengths
+  // and with the bf16 pack; the others hold as many workgroups per CU)
+  if (D == 128 && BLK == 64)
+    return resident_of<Cfg<128, 64, 32, 2>>((const void*)attn_bf16_kernel<Cfg<128, 64, 32, 2>, false, false, true>);
+  if (D == 128 && BLK == 128)
+    return resident_of<Cfg<128, 128, 32>>((const void*)attn_bf16_kernel<Cfg<128, 128, 32>, false, false, true>);
+  if (D == 64 && BLK == 64)
+    return resident_of<Cfg<64, 64, 32, 2>>((const void*)attn_bf16_kernel<Cfg<64, 64, 32, 2>, false, false, true>);
+  if (D == 64 && BLK == 128)
+    return resident_of<Cfg<64, 128, 64>>((const void*)attn_bf16_kernel<Cfg<64, 128, 64>, false, false, true>);
+  return 0;
+}
+}  // namespace
 
 size_t attn_split_workspace(int D, int BLK, int bh, int nb, int kmax, int cap) {
   // the configurations launch_attn_bf16 picks for the orders other than the per-block first

@@ -98,6 +98,11 @@ hipError_t launch_attn_bf16(const AttnArgs& a);
 size_t attn_split_workspace(int D, int BLK, int bh, int nb, int kmax, int cap);
 // largest nb whose in-kernel routing fits the attention kernel's LDS (bf16)
 int fused_route_max_blocks(int D, int BLK);
+// in-kernel routing (bf16): the launch's work items, and how many of its
+// workgroups the current device holds at once over all CUs (<= 0 when the
+// runtime cannot say)
+int fused_route_items(int D, int BLK, int bh, int nb);
+int fused_route_resident(int D, int BLK);
 hipError_t launch_attn_f32(const AttnArgs& a);
 hipError_t launch_stats_bf16(const StatsArgs& a);
 hipError_t launch_stats_f32(const StatsArgs& a);

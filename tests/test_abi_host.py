@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
     assert declared == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.pisa_version() == 102
+    assert lib.pisa_version() == 103
 
 
 def test_probe_library_exports_its_declared_symbol():
@@ -168,10 +168,11 @@ def test_precompute_Ht_is_bf16_only(lib):
     assert b"Ht" in lib.pisa_last_error()
 
 
-def ra(lib, shp, k=4, lam=0.1, mode=0, scale=0.1, st=None, O=FAKE):
+def ra(lib, shp, k=4, lam=0.1, mode=0, scale=0.1, st=None, O=FAKE, idx=None,
+       form=_lib.ROUTE_IN_KERNEL):
     st = stats() if st is None else st
     return lib.pisa_route_attention(ctypes.byref(shp), FAKE, FAKE, FAKE, ctypes.byref(st), k, lam,
-                                    mode, scale, None, O, None)
+                                    mode, scale, idx, O, form, None)
 
 
 def test_route_attention_arguments(lib):
@@ -195,6 +196,13 @@ def test_route_attention_arguments(lib):
     assert ra(lib, shape(L=64 * 1921)) == 2
     assert b"pisa_route, then pisa_attention" in lib.pisa_last_error()
     assert ra(lib, shape(L=64 * 961, d=64)) == 2                    # d = 64: nb <= 960
+    # the form: known values only; two launches need idx for the selection
+    assert ra(lib, s, form=3) == 3
+    assert ra(lib, s, form=-1) == 3
+    assert ra(lib, s, form=_lib.ROUTE_TWO_LAUNCH) == 1
+    assert b"two-launch" in lib.pisa_last_error()
+    # without idx the automatic form routes in-kernel, so the LDS limit holds
+    assert ra(lib, shape(L=64 * 1921), form=_lib.ROUTE_AUTO) == 2
 
 
 def test_noalloc_precompute_refuses_shapes_above_its_scratch(lib):

@@ -41,17 +41,27 @@ def _rand(shape, dtype, seed):
     return wl.round_bf16(x) if dtype == "bf16" else x
 
 
+FORMS = ("in_kernel", "auto", "two_launch")
+
+
 def _fused_vs_split(torch, pisa, Qd, Kd, Vd, st, k, lam, B, sl=None, modes=MODES, name=""):
-    """Fused and split paths on the same tensors: identical idx and outputs."""
+    """Fused and split paths on the same tensors: identical idx and outputs,
+    in every form of the fused call (in-kernel routing forced, the automatic
+    choice, and the two-launch form)."""
     idx = pisa.route(Qd, st, k, lam, B, seq_lens=sl)
     outs = {}
     for m in modes:
         ref = pisa.attention(Qd, Kd, Vd, idx, st, B, mode=m, seq_lens=sl)
-        got, gidx = pisa.route_attention(Qd, Kd, Vd, st, k, lam, B, mode=m, seq_lens=sl,
-                                         return_idx=True)
+        for form in FORMS:
+            got, gidx = pisa.route_attention(Qd, Kd, Vd, st, k, lam, B, mode=m, seq_lens=sl,
+                                             return_idx=True, form=form)
+            torch.cuda.synchronize()
+            assert torch.equal(gidx, idx), f"{name}/{m}/{form}: selection differs from pisa_route"
+            assert torch.equal(got, ref), f"{name}/{m}/{form}: output differs from route + attention"
+        # without idx the in-kernel form writes no selection
+        got = pisa.route_attention(Qd, Kd, Vd, st, k, lam, B, mode=m, seq_lens=sl, form="in_kernel")
         torch.cuda.synchronize()
-        assert torch.equal(gidx, idx), f"{name}/{m}: in-kernel selection differs from pisa_route"
-        assert torch.equal(got, ref), f"{name}/{m}: output differs from route + attention"
+        assert torch.equal(got, ref), f"{name}/{m}: output without idx differs from route + attention"
         outs[m] = got
     return idx, outs
 
@@ -122,7 +132,8 @@ def test_random_small_configurations(torch, seed):
 def test_largest_block_counts(torch, d, B, nb, k):
     """The largest nb each configuration's LDS holds (score rows of 1920 and
     960 blocks for query-block pairs, 2048 otherwise): same selection and
-    outputs as the split path; one block more is refused on the host."""
+    outputs as the split path.  One block more is refused on the host for
+    in-kernel routing, and the automatic form runs it as two launches."""
     pisa = pisa_mod()
     L = nb * B
     Q, K, V = (_rand((1, 1, L, d), "bf16", s) for s in (21, 22, 23))
@@ -134,11 +145,17 @@ def test_largest_block_counts(torch, d, B, nb, k):
         Qx = torch.zeros((1, 1, L + B, d), dtype=torch.bfloat16, device="cuda")
         stx = pisa.precompute(Qx, Qx, B)
         with pytest.raises(pisa._lib.PisaError):
-            pisa.route_attention(Qx, Qx, Qx, stx, k, 0.02, B)
+            pisa.route_attention(Qx, Qx, Qx, stx, k, 0.02, B, form="in_kernel")
+        got, gidx = pisa.route_attention(Qx, Qx, Qx, stx, k, 0.02, B, return_idx=True)
+        idx = pisa.route(Qx, stx, k, 0.02, B)
+        ref = pisa.attention(Qx, Qx, Qx, idx, stx, B)
+        torch.cuda.synchronize()
+        assert torch.equal(gidx, idx) and torch.equal(got, ref)
 
 
+@pytest.mark.parametrize("form", ["in_kernel", "two_launch"])
 @pytest.mark.parametrize("nb,k", [(16, 5), (72, 30), (512, 64)])
-def test_exact_ties_go_to_lower_ids(torch, nb, k):
+def test_exact_ties_go_to_lower_ids(torch, nb, k, form):
     """Zero queries make every score lambda * M_j; repeated M values (and
     +-0) force exact ties at the k-th score: the in-kernel selection breaks
     them towards the lower block id, as the oracle does."""
@@ -151,7 +168,8 @@ def test_exact_ties_go_to_lower_ids(torch, nb, k):
     cen = np.zeros((1, 2, nb, d), dtype=np.float32)
     Qd = to_dev(Q, "bf16")
     st = {"centroid": torch.from_numpy(cen).cuda(), "M": torch.from_numpy(M).cuda()}
-    _, idx = pisa.route_attention(Qd, Qd, Qd, st, k, 1.0, B, mode="drop", return_idx=True)
+    _, idx = pisa.route_attention(Qd, Qd, Qd, st, k, 1.0, B, mode="drop", return_idx=True,
+                                  form=form)
     torch.cuda.synchronize()
     ref = oracle.route(Q, cen, M, k, 1.0, B, 1 / math.sqrt(d))
     assert np.array_equal(idx.cpu().numpy(), ref)
