@@ -263,8 +263,10 @@ def time_route_attention(pisa, torch, Qd, Kd, Vd, st, w, reps):
     """The routing-and-attention call in its automatic form (in-kernel routing
     while the work fits one round of workgroups, else two launches), with the
     in-kernel form forced, and the two calls it replaces, each timed the same
-    way: back-to-back calls between two HIP events, the forms alternated twice
-    (best of each kept).  Returns the three times in ms."""
+    way: back-to-back calls between two HIP events, the forms alternated four
+    times (best of each kept: the automatic form runs the same kernels as one of
+    the other two, so only the noise between passes separates them).  Returns
+    the three times in ms."""
     stream = torch.cuda.current_stream()
 
     def fused():
@@ -278,8 +280,7 @@ def time_route_attention(pisa, torch, Qd, Kd, Vd, st, w, reps):
         pisa.attention(Qd, Kd, Vd, idx, st, w.block, mode="approx")
 
     best = {}
-    for name, fn in (("fused", fused), ("in_kernel", in_kernel), ("split", split),
-                     ("fused", fused), ("in_kernel", in_kernel), ("split", split)):
+    for name, fn in (("fused", fused), ("in_kernel", in_kernel), ("split", split)) * 4:
         for _ in range(2):
             fn()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
