@@ -30,7 +30,9 @@
 // 32 columns) are both free of bank conflicts.  The V read of each 4-key group
 // picks the keys that the lane's P registers hold, so P feeds the MFMA as is.
 // PISA's zeroth-order sweep streams the bf16 centroid / value-sum pack through
-// the same ring (a centroid chunk has the layout of a K / V chunk).
+// the same ring (a centroid chunk has the layout of a K / V chunk), gathering
+// only the rows of blocks that some query row of the workgroup leaves
+// unselected.
 #include <atomic>
 
 #include "common.hpp"
@@ -183,9 +185,10 @@ __device__ __forceinline__ void s_tiles(f32x16 (&s)[C::NKT], const bf16x8 (&qf)[
   }
 }
 
-// Logits of keys that do not take part -> -inf.  STAGE2: centroid entries
-// whose block is in S_i or is padding (bit set in `bits`); stage 1: keys past
-// the sequence's end (key of register r: 32 kt + 8 (r / 4) + 4 hh + r % 4).
+// Logits of keys that do not take part -> -inf.  STAGE2: positions of the
+// stage-2 list that this query block does not take (bit jbase + key set in
+// `bits`: a block of its S_i, or the list's padding); stage 1: keys past the
+// sequence's end (key of register r: 32 kt + 8 (r / 4) + 4 hh + r % 4).
 template <class C, bool STAGE2>
 __device__ __forceinline__ void mask_keys(f32x16 (&s)[C::NKT], int hh, const unsigned* bits,
                                           int jbase, int kvalid) {
@@ -373,18 +376,54 @@ __device__ __forceinline__ void hbar_part(RowState<C::D>& st, const bf16x8 (&fq)
   }
 }
 
-// fp32 statistics -> bf16 chunk of CK centroids / value sums in the stage
-// layout (used when no bf16 pack was supplied); rows past nb are zero.
+// Stage-2 copy of CK gathered rows: row r of the stage's centroid half is row
+// rows[r] of the bf16 centroid pack gC, and the same row of the value-sum
+// pack gS fills the other half.  The pieces and lane slots are those of
+// dma_stage (wave w copies pieces w H .. w H + H - 1 of each half, H = DPW / 2),
+// with the row's global offset taken per lane from its id instead of from its
+// position, and M0 set per piece since the pieces are no longer contiguous in
+// global memory.  The lane's row within its piece and its swizzled slot are
+// read back from its dma_stage offset o.v[u] = row * RB + 16 * slot (RB a power
+// of two above 16 * slot), so no other per-lane value stays live for this.
 template <class C>
-__device__ __forceinline__ void stage_centroids(const float* cen, const float* vs, int j0, int nb,
-                                                char* stage, int tid) {
+__device__ __forceinline__ void dma_rows(const char* gC, const char* gS, const short* rows,
+                                         unsigned stage_m0, int w, const DmaOff<C>& o) {
+  constexpr int H = C::DPW / 2;
+  static_assert((C::RB & (C::RB - 1)) == 0 && C::RPD * C::RB == 1024, "rows are a power of two bytes");
+#pragma unroll
+  for (int u = 0; u < H; ++u) {
+    // an opaque copy: what is derived from it is recomputed at each call
+    // instead of being hoisted out of the chunk loop and held in registers
+    unsigned ov = o.v[u];
+    asm volatile("" : "+v"(ov));
+    const int r = (w * H + u) * C::RPD + (int)(ov / C::RB);   // row of the chunk
+    const unsigned voff = (unsigned)rows[r] * C::RB + (ov & (C::RB - 1));
+    const unsigned m0c = stage_m0 + (unsigned)(w * H + u) * 1024u;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %2, %4"
+        :
+        : "s"(m0c), "s"(m0c + (unsigned)C::SUBB), "v"(voff), "s"(gC), "s"(gS)
+        : "memory", "m0");
+  }
+}
+
+// fp32 statistics -> bf16 chunk of CK centroids / value sums in the stage
+// layout (used when no bf16 pack was supplied): row r of the chunk is block
+// rows[r] (an id at or past nb gives a zero row).
+template <class C>
+__device__ __forceinline__ void stage_centroids(const float* cen, const float* vs, const short* rows,
+                                                int nb, char* stage, int tid) {
   for (int q = tid; q < 2 * C::CK * C::CPR; q += C::NT) {
     const bool isv = q >= C::CK * C::CPR;
     const int qq = isv ? q - C::CK * C::CPR : q;
     const int r = qq / C::CPR, c = qq % C::CPR;
-    const float* src = (isv ? vs : cen) + (size_t)(j0 + r) * C::D + 8 * c;
+    const int j = rows[r];
+    const float* src = (isv ? vs : cen) + (size_t)j * C::D + 8 * c;
     f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
-    if (j0 + r < nb) {
+    if (j < nb) {
       lo = *reinterpret_cast<const f32x4*>(src);
       hi = *reinterpret_cast<const f32x4*>(src + 4);
     }
@@ -506,8 +545,14 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
                                                        // Pairs: the union, ascending, with
                                                        // bit 12 + q set if query block q
                                                        // routes the block
-  __shared__ short s_clist[kBitWords];                 // centroid chunks to sweep
+  // stage 2: the blocks that some live query block of the item leaves
+  // unselected, ascending, then id 0 up to a whole chunk; s_umask[q] bit p set
+  // when position p does not take part for query block q (a block of its S_i,
+  // or past the list's end); s_rag: the position of the ragged last block
+  __shared__ short s_ulist[kMaxBlocks];
+  __shared__ unsigned s_umask[QB][kBitWords];
   __shared__ int s_cnt[3];
+  __shared__ int s_rag;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int q32 = lane & 31, hh = lane >> 5;
@@ -720,10 +765,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   const float c2 = scale * kLog2e;
 
   // ---- the chunk stream: CK-token chunks of the exact blocks of S_i (in idx
-  // order), then (PISA mode with a pack) the chunks of CK centroids that hold
-  // any unselected block.  Both lists are compacted into LDS once, in order.
+  // order), then (approximate modes with a pack) the compacted stage-2 list,
+  // CK gathered centroid / value-sum rows per chunk.  Both lists are built in
+  // LDS once, in ascending block order.
   constexpr int SPB = BLK / CK;                          // chunks per KV block
-  const int nctile = packed ? nbp / CK : 0;
   if (w == 0) {
     int cnt = 0;
     {
@@ -746,16 +791,50 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       }
       cnt = __shfl(pre, 63);
     }
-    int ccnt = 0;
-    for (int c0 = 0; c0 < nctile; c0 += 64) {
-      const int tcv = c0 + lane;
-      bool need = false;
-      if (tcv < nctile)
-        for (int q = 0; q < QB; ++q)
-          for (int u = 0; u < CK / 32; ++u) need = need || (bits[q][tcv * (CK / 32) + u] != ~0u);
-      const unsigned long long m = __ballot(need);
-      if (need) s_clist[ccnt + __popcll(m & ((1ull << lane) - 1))] = (short)tcv;
-      ccnt += __popcll(m);
+    // stage 2 (approximate modes): the blocks that a live query block of the
+    // item leaves unselected, compacted in ascending order, so the sweep
+    // multiplies no column that every one of its rows masks; per query block,
+    // the positions it does not take (its exact blocks, the list's padding)
+    int ccnt = 0;                                        // stage-2 chunks
+    if (lane == 0) s_rag = -1;
+    if (approx) {
+      const int jr = (VL && Lv % BLK != 0) ? nne - 1 : -1;   // the ragged last block
+      unsigned live = 0u;
+#pragma unroll
+      for (int q = 0; q < QB; ++q)
+        if (i0 + q < nb && (!VL || block_count(Lv, i0 + q, BLK) > 0)) live |= 1u << q;
+      for (int e = lane; e < kBitWords; e += 64)
+#pragma unroll
+        for (int q = 0; q < QB; ++q) s_umask[q][e] = 0u;
+      wave_sync();
+      int n = 0;
+      for (int j0 = 0; j0 < nbp; j0 += 64) {
+        const int j = j0 + lane;
+        unsigned skip = 0u;                              // bit q: query block q does not take j
+        bool u = false;
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+          const bool ex = j >= nbp || !((live >> q) & 1u) || ((bits[q][j >> 5] >> (j & 31)) & 1u);
+          if (ex) skip |= 1u << q;
+          else u = true;
+        }
+        const unsigned long long m = __ballot(u);
+        if (u) {
+          const int pos = n + __popcll(m & ((1ull << lane) - 1));
+          s_ulist[pos] = (short)j;
+#pragma unroll
+          for (int q = 0; q < QB; ++q)
+            if ((skip >> q) & 1u) atomicOr(&s_umask[q][pos >> 5], 1u << (pos & 31));
+          if (j == jr) s_rag = pos;
+        }
+        n += __popcll(m);
+      }
+      ccnt = (n + CK - 1) / CK;
+      for (int pos = n + lane; pos < ccnt * CK; pos += 64) {
+        s_ulist[pos] = 0;                                // a valid row, masked for every query block
+#pragma unroll
+        for (int q = 0; q < QB; ++q) atomicOr(&s_umask[q][pos >> 5], 1u << (pos & 31));
+      }
     }
     int ucnt = 0;
     if (first) {
@@ -792,7 +871,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   const bool tail = !SP || part == 0;                  // this workgroup runs stages 2 and 3
   // mixed order with the bf16 pack: Hbar^T streams as HP ring chunks after stage 2
   const int nhb = (tail && packed && order == kOrderMixed) ? C::HP : 0;
-  const int nex = nexp, ncen = nex + (tail ? s_cnt[1] : 0), nhbe = ncen + nhb, ntot = nhbe + s_cnt[2] * C::HP;
+  const int nex = nexp, ncen = nex + (tail && packed ? s_cnt[1] : 0), nhbe = ncen + nhb, ntot = nhbe + s_cnt[2] * C::HP;
   const int ws = __builtin_amdgcn_readfirstlane(w);
   const unsigned lds_m0 = (unsigned)(uintptr_t)(lvoid*)lds;
   const char* Kb = reinterpret_cast<const char*>(Kh);
@@ -810,9 +889,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       const size_t off = ((size_t)j * BLK + (size_t)(u % SPB) * CK) * C::RB;
       dma_stage<C>(Kb + off, Vb + off, m0, ws, loff);
     } else if (t < ncen) {
-      const int tcv = __builtin_amdgcn_readfirstlane((int)s_clist[t - nex]);
-      const size_t off = (size_t)tcv * CK * C::RB;
-      dma_stage<C>(Cb + off, Sb + off, m0, ws, loff);
+      // stage-2 chunk t - nex: CK gathered rows of the compacted list
+      dma_rows<C>(Cb, Sb, s_ulist + (t - nex) * CK, m0, ws, loff);
     } else if (t < nhbe) {
       // rows part * RP .. of Hbar^T (same layout as the H_j^T parts below)
       const char* g = Hbt + (size_t)(t - ncen) * C::RP * C::RB;
@@ -861,13 +939,14 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   // stage 2: the ragged last block (if any) weighs its n_j tokens
   const int jrag = (VL && Lv % BLK != 0) ? nne - 1 : -1;
   const float wmiss = (float)(BLK - (Lv - jrag * BLK));
+  const int prag = VL ? s_rag : -1;         // its position in the stage-2 list (-1: absent)
   for (; t < ncen; ++t) {                   // stage 2: centroid / value-sum chunks
     wait_vm0();
     __syncthreads();
     if (t + 1 < ntot) issue(t + 1);
-    const int jbase = (int)s_clist[t - nex] * CK;
-    const int jp = (VL && jrag >= jbase && jrag < jbase + CK) ? jrag - jbase : -1;
-    if (alive) chunk<C, true>(st, qf, lds + (t & 1) * C::STB, off, c2, hh, bits[qb], jbase, CK, jp, wmiss);
+    const int pos0 = (t - nex) * CK;
+    const int jp = (VL && prag >= pos0 && prag < pos0 + CK) ? prag - pos0 : -1;
+    if (alive) chunk<C, true>(st, qf, lds + (t & 1) * C::STB, off, c2, hh, s_umask[qb], pos0, CK, jp, wmiss);
   }
   if (FO) {
     for (; t < ntot; ++t) {                 // per-block first order: H_j^T parts
@@ -886,12 +965,13 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       // ---- stage 2 from the fp32 statistics (converted while staging)
       const float* cen = p.centroid + (size_t)bh * nb * D;
       const float* vs = p.vsum + (size_t)bh * nb * D;
-      for (int j0 = 0; j0 < nbp; j0 += CK) {
+      const int nch = s_cnt[1];
+      for (int pos0 = 0; pos0 < nch * CK; pos0 += CK) {
         __syncthreads();
-        stage_centroids<C>(cen, vs, j0, nb, lds, tid);
+        stage_centroids<C>(cen, vs, s_ulist + pos0, nb, lds, tid);
         __syncthreads();
-        const int jp = (VL && jrag >= j0 && jrag < j0 + CK) ? jrag - j0 : -1;
-        if (alive) chunk<C, true>(st, qf, lds, off, c2, hh, bits[qb], j0, CK, jp, wmiss);
+        const int jp = (VL && prag >= pos0 && prag < pos0 + CK) ? prag - pos0 : -1;
+        if (alive) chunk<C, true>(st, qf, lds, off, c2, hh, s_umask[qb], pos0, CK, jp, wmiss);
       }
     }
   }
