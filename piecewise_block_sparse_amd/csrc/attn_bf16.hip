@@ -70,7 +70,7 @@ struct Cfg {
   static constexpr int RPD = 1024 / RB;          // rows per 1 KB copy
   // waves per SIMD the register budget is sized for: three (<= 168 VGPRs)
   // for d = 128 with 128 query rows per workgroup and 32-key chunks (three
-  // 4-wave groups per CU, 37 KB of LDS each); two otherwise
+  // 4-wave groups per CU, 41 KB of LDS each); two otherwise
   static constexpr int MINB = (D == 128 && QB * BLK == 128 && CK == 32) ? 3 : 2;
   static_assert(QB == 1 || (QB == 2 && BLK == 64), "query-block pairs are for 64-token blocks");
   static_assert(NDMA % NW == 0, "copies split evenly over waves");
@@ -114,31 +114,42 @@ __device__ __forceinline__ float row_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Per-lane LDS byte offsets, fixed for the whole kernel:
-//   koff[ks]       K row 32 kt + q32 (kt added as an immediate), columns 16 ks + 8 hh ..
-//   voff[mt][h]    transposing V read of 4 keys (slab base added as an immediate)
+// Per-lane LDS byte offsets, fixed for the whole kernel.  The swizzle is an
+// XOR on the 16-byte slot, so one lane's offsets differ only in XORed slot
+// bits, and each is one XOR away from a single base:
+//   K row 32 kt + q32 (kt added as an immediate), columns 16 ks + 8 hh ..:
+//     k0 ^ 32 ks (column 16 ks adds 2 ks to the slot, whose low bit is hh);
+//   transposing V read of tile mt: rows 0..7 of the slab at v0 ^ 64 mt,
+//     rows 8..15 at that ^ 32, plus 8 RB (swz(r + 8) = swz(r) ^ 2 for both
+//     head dims).
+// Holding two offsets instead of sixteen leaves the compiler registers to read
+// fragments further ahead of their MFMAs (measured 0.5-1.9% faster calls).
 template <class C>
 struct Offsets {
-  int koff[C::KS];
-  TrOff<C> tr;
+  int k0;
+  int v0;
 };
 
 template <class C>
 __device__ __forceinline__ Offsets<C> make_offsets(int lane) {
   Offsets<C> o;
   const int q32 = lane & 31, hh = lane >> 5;
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks)
-    o.koff[ks] = q32 * C::RB + (((2 * ks + hh) ^ swz<C::D>(q32)) << 4);
-  o.tr = tr_offsets<C>(lane);
+  o.k0 = q32 * C::RB + ((hh ^ swz<C::D>(q32)) << 4);
+  o.v0 = tr_lane_offset<C>(lane, 0, 0);
   return o;
+}
+
+template <class C>
+__device__ __forceinline__ int koff_of(const Offsets<C>& o, int ks) {
+  return o.k0 ^ (32 * ks);
 }
 
 // A operand of O^T += V^T P^T for 16-key slab sl and d-tile mt; its key order
 // within the slab is the one the lane's P registers hold.
 template <class C>
 __device__ __forceinline__ u32x4 v_frag(const char* vst, int sl, int mt, const Offsets<C>& off) {
-  return tr_frag<C>(vst, sl, mt, off.tr);
+  const int t0 = off.v0 ^ (64 * mt);
+  return tr_read<C>(vst + 8 * C::RB, sl, t0 - 8 * C::RB, t0 ^ 32);
 }
 
 // exp2 weights -> bf16 MFMA B operands, and the sum of the same bf16 weights.
@@ -174,13 +185,13 @@ __device__ __forceinline__ void s_tiles(f32x16 (&s)[C::NKT], const bf16x8 (&qf)[
     if constexpr (PRE) {
       u32x4 kf[C::KS];
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) kf[ks] = ld16(stage + kt * 32 * C::RB + off.koff[ks]);
+      for (int ks = 0; ks < C::KS; ++ks) kf[ks] = ld16(stage + kt * 32 * C::RB + koff_of<C>(off, ks));
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) s[kt] = mfma32(as_bf16x8(kf[ks]), qf[ks], s[kt]);
     } else {
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
-        s[kt] = mfma32(as_bf16x8(ld16(stage + kt * 32 * C::RB + off.koff[ks])), qf[ks], s[kt]);
+        s[kt] = mfma32(as_bf16x8(ld16(stage + kt * 32 * C::RB + koff_of<C>(off, ks))), qf[ks], s[kt]);
     }
   }
 }
@@ -339,7 +350,7 @@ __device__ __forceinline__ void first_order_part(RowState<C::D>& st, const bf16x
     hq[mtl] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
-      hq[mtl] = mfma32(as_bf16x8(ld16(stage + mtl * 32 * C::RB + off.koff[ks])), qf[ks], hq[mtl]);
+      hq[mtl] = mfma32(as_bf16x8(ld16(stage + mtl * 32 * C::RB + koff_of<C>(off, ks))), qf[ks], hq[mtl]);
   }
   // acc tile mt belongs to part mt / MTP; the other parts' tiles get a zero factor
 #pragma unroll
@@ -370,7 +381,7 @@ __device__ __forceinline__ void hbar_part(RowState<C::D>& st, const bf16x8 (&fq)
     if constexpr (PART * MTP + MTP <= C::MT) {
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
-        st.acc[PART * MTP + mtl] = mfma32(as_bf16x8(ld16(stage + mtl * 32 * C::RB + off.koff[ks])), fq[ks],
+        st.acc[PART * MTP + mtl] = mfma32(as_bf16x8(ld16(stage + mtl * 32 * C::RB + koff_of<C>(off, ks))), fq[ks],
                                           st.acc[PART * MTP + mtl]);
     }
   }
@@ -1007,7 +1018,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       for (int mt = 0; mt < C::MT; ++mt) {
         const char* base = (mt < C::MT / 2) ? lds + 32 * mt * C::RB : lds + C::STB + 32 * (mt - C::MT / 2) * C::RB;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) st.acc[mt] = mfma32(as_bf16x8(ld16(base + off.koff[ks])), qf[ks], st.acc[mt]);
+        for (int ks = 0; ks < C::KS; ++ks) st.acc[mt] = mfma32(as_bf16x8(ld16(base + koff_of<C>(off, ks))), qf[ks], st.acc[mt]);
       }
     }
   }

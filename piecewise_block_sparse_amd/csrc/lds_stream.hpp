@@ -137,26 +137,4 @@ __device__ __forceinline__ u32x4 tr_read(const char* base, int sl, int o0, int o
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
-// Offsets of every tile (index tiles with compile-time mt only: a run-time
-// index would put the table in scratch memory).
-template <class C>
-struct TrOff {
-  int v[C::D / 32][2];
-};
-
-template <class C>
-__device__ __forceinline__ TrOff<C> tr_offsets(int lane) {
-  TrOff<C> o;
-#pragma unroll
-  for (int mt = 0; mt < C::D / 32; ++mt)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) o.v[mt][h] = tr_lane_offset<C>(lane, mt, h);
-  return o;
-}
-
-template <class C>
-__device__ __forceinline__ u32x4 tr_frag(const char* base, int sl, int mt, const TrOff<C>& o) {
-  return tr_read<C>(base, sl, o.v[mt][0], o.v[mt][1]);
-}
-
 }  // namespace pisa

@@ -83,10 +83,10 @@ __global__ __launch_bounds__(256, 3) void probe_kernel(const char* src, float* o
   const char* win = src + (size_t)(blockIdx.x % kWindows) * kWindow;
   const unsigned m0 = (unsigned)(uintptr_t)(lvoid*)lds;
   const DmaOff<PC> loff = dma_lane_offsets<PC>(w, lane);
-  const TrOff<PC> tro = tr_offsets<PC>(lane);
-  int koff[PC::KS];
-#pragma unroll
-  for (int ks = 0; ks < PC::KS; ++ks) koff[ks] = q32 * PC::RB + (((2 * ks + hh) ^ swz<PC::D>(q32)) << 4);
+  // the attention kernel's two offset bases: every K and V fragment offset is
+  // one XOR (and an immediate) away from them
+  const int k0 = q32 * PC::RB + ((hh ^ swz<PC::D>(q32)) << 4);
+  const int v0 = tr_lane_offset<PC>(lane, 0, 0);
   bf16x8 qf[PC::KS];
 #pragma unroll
   for (int ks = 0; ks < PC::KS; ++ks) {
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256, 3) void probe_kernel(const char* src, float* o
     const char* stage = lds + (it & 1) * PC::STB;
     f32x16 s = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < PC::KS; ++ks) s = mfma32(as_bf16x8(ld16(stage + koff[ks])), qf[ks], s);
+    for (int ks = 0; ks < PC::KS; ++ks) s = mfma32(as_bf16x8(ld16(stage + (k0 ^ (32 * ks)))), qf[ks], s);
     u32x4 pf[2];
     if constexpr (MIX) {
       float sum = 0.f;
@@ -136,7 +136,9 @@ __global__ __launch_bounds__(256, 3) void probe_kernel(const char* src, float* o
     for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
       for (int mt = 0; mt < PC::MT; ++mt)
-        acc[mt] = mfma32(as_bf16x8(tr_frag<PC>(vst, sl, mt, tro)), as_bf16x8(pf[sl]), acc[mt]);
+        acc[mt] = mfma32(as_bf16x8(tr_read<PC>(vst + 8 * PC::RB, sl, (v0 ^ (64 * mt)) - 8 * PC::RB,
+                                               (v0 ^ (64 * mt)) ^ 32)),
+                         as_bf16x8(pf[sl]), acc[mt]);
   }
   float r = l;
 #pragma unroll
