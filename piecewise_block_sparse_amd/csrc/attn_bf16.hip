@@ -175,7 +175,7 @@ __device__ __forceinline__ float weights_bf16(const f32x16 (&s)[NKT], float c2, 
 
 // S^T of the chunk in `stage` (K rows) against this wave's queries.  PRE:
 // all K fragments of a tile are read before its MFMA chain (two-wave register
-// budget); otherwise each fragment is read next to its MFMA.
+// budget); otherwise through a window of three fragments.
 template <class C, bool PRE>
 __device__ __forceinline__ void s_tiles(f32x16 (&s)[C::NKT], const bf16x8 (&qf)[C::KS],
                                         const char* stage, const Offsets<C>& off) {
@@ -189,9 +189,19 @@ __device__ __forceinline__ void s_tiles(f32x16 (&s)[C::NKT], const bf16x8 (&qf)[
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) s[kt] = mfma32(as_bf16x8(kf[ks]), qf[ks], s[kt]);
     } else {
+      // a window of three fragments: each K read goes out three MFMAs ahead of
+      // its use, and the scheduling fences keep that order (the compiler alone
+      // placed them two ahead; three measured 0.5-3% faster calls, four the same)
+      constexpr int W = 3;
+      u32x4 kf[W];
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        s[kt] = mfma32(as_bf16x8(ld16(stage + kt * 32 * C::RB + koff_of<C>(off, ks))), qf[ks], s[kt]);
+      for (int ks = 0; ks < W; ++ks) kf[ks] = ld16(stage + kt * 32 * C::RB + koff_of<C>(off, ks));
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        s[kt] = mfma32(as_bf16x8(kf[ks % W]), qf[ks], s[kt]);
+        if (ks + W < C::KS) kf[ks % W] = ld16(stage + kt * 32 * C::RB + koff_of<C>(off, ks + W));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 }
@@ -290,7 +300,7 @@ __device__ __forceinline__ void pv_frags(RowState<C::D>& st, const u32x4 (&vf)[C
 // One CK-key chunk from a stage: S^T, softmax update, O^T += V^T P^T.
 // With the two-wave register budget and 32-key chunks (PRE) every LDS
 // fragment is read well before its MFMA; the three-wave budget (and 64-key
-// chunks) leave no room for that, and each fragment is read next to its MFMA.
+// chunks) leave room for a window of three fragments each for K and V.
 template <class C, bool STAGE2>
 __device__ __forceinline__ void chunk(RowState<C::D>& st, const bf16x8 (&qf)[C::KS],
                                       const char* stage, const Offsets<C>& off, float c2, int hh,
@@ -304,15 +314,27 @@ __device__ __forceinline__ void chunk(RowState<C::D>& st, const bf16x8 (&qf)[C::
   if constexpr (PRE) v_frags<C>(vf, vst, off);
   mask_keys<C, STAGE2>(s, hh, bits, jbase, kvalid);
   u32x4 pf[C::NSL];
+  // without PRE: the first VW V fragments are read before the softmax, so
+  // their latency hides under the exponentials, then each read goes out VW
+  // MFMAs ahead of its use (fenced like the K window; measured 0.7-1.3%
+  // faster calls, four fragments the same)
+  constexpr int VW = 3, NF = C::MT * C::NSL;
+  u32x4 vw[VW];
+  if constexpr (!PRE) {
+#pragma unroll
+    for (int f = 0; f < VW; ++f) vw[f] = v_frag<C>(vst, f % C::NSL, f / C::NSL, off);
+  }
   softmax_update<C, STAGE2>(st, s, c2, hh, pf, jpart, wmiss);
   if constexpr (PRE) {
     pv_frags<C>(st, vf, pf);
   } else {
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-      for (int sl = 0; sl < C::NSL; ++sl)
-        st.acc[mt] = mfma32(as_bf16x8(v_frag<C>(vst, sl, mt, off)), as_bf16x8(pf[sl]), st.acc[mt]);
+    for (int f = 0; f < NF; ++f) {
+      const int mt = f / C::NSL, sl = f % C::NSL;
+      st.acc[mt] = mfma32(as_bf16x8(vw[f % VW]), as_bf16x8(pf[sl]), st.acc[mt]);
+      if (f + VW < NF) vw[f % VW] = v_frag<C>(vst, (f + VW) % C::NSL, (f + VW) / C::NSL, off);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
