@@ -154,12 +154,13 @@ __device__ __forceinline__ u32x4 v_frag(const char* vst, int sl, int mt, const O
 
 // exp2 weights -> bf16 MFMA B operands, and the sum of the same bf16 weights.
 // Each pair is packed into its own 32-bit value and summed from that value
-// with v_dot2 against (1, 1).
+// with v_dot2 against (1, 1), alternating between two partial sums so that the
+// chain the rescale test waits for is half as long.
 template <int NKT>
 __device__ __forceinline__ float weights_bf16(const f32x16 (&s)[NKT], float c2, float nm,
                                               u32x4 (&pf)[2 * NKT]) {
   const bf16x2 one = {(bf16)1.f, (bf16)1.f};
-  float sum = 0.f;
+  float sum[2] = {0.f, 0.f};
 #pragma unroll
   for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
@@ -167,10 +168,10 @@ __device__ __forceinline__ float weights_bf16(const f32x16 (&s)[NKT], float c2, 
       const float p0 = fast_exp2(fmaf(s[kt][2 * q], c2, nm));
       const float p1 = fast_exp2(fmaf(s[kt][2 * q + 1], c2, nm));
       const bf16x2 pr = {(bf16)p0, (bf16)p1};
-      sum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, sum, false);
+      sum[q & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, sum[q & 1], false);
       pf[2 * kt + q / 4][q % 4] = __builtin_bit_cast(unsigned, pr);
     }
-  return sum;
+  return sum[0] + sum[1];
 }
 
 // S^T of the chunk in `stage` (K rows) against this wave's queries.  PRE:
@@ -323,6 +324,7 @@ __device__ __forceinline__ void chunk(RowState<C::D>& st, const bf16x8 (&qf)[C::
   if constexpr (!PRE) {
 #pragma unroll
     for (int f = 0; f < VW; ++f) vw[f] = v_frag<C>(vst, f % C::NSL, f / C::NSL, off);
+    __builtin_amdgcn_sched_barrier(0);   // issued in the wait for the last S^T MFMA
   }
   softmax_update<C, STAGE2>(st, s, c2, hh, pf, jpart, wmiss);
   if constexpr (PRE) {
