@@ -916,11 +916,15 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   const char* Hb = first ? reinterpret_cast<const char*>(p.ht + (size_t)bh * nb * D * D) : nullptr;
   const char* Hbt = nhb ? reinterpret_cast<const char*>(p.pk_hbart + (size_t)bh * D * D) : nullptr;
   // copy chunk t into stage t & 1
+  // copy chunk t into stage t & 1; returns an exact chunk's list entry (block id
+  // and pair membership bits, wave-uniform), 0 otherwise
   auto issue = [&](int t) {
     const unsigned m0 = lds_m0 + (unsigned)((t & 1) * C::STB);
+    int entry = 0;
     if (t < nex) {
       const int u = t + ex0;                              // exact chunk u of the item
-      const int j = __builtin_amdgcn_readfirstlane((int)s_list[u / SPB] & kIdMask);
+      entry = __builtin_amdgcn_readfirstlane((int)s_list[u / SPB]);
+      const int j = entry & kIdMask;
       const size_t off = ((size_t)j * BLK + (size_t)(u % SPB) * CK) * C::RB;
       dma_stage<C>(Kb + off, Vb + off, m0, ws, loff);
     } else if (t < ncen) {
@@ -937,8 +941,11 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       const char* g = Hb + ((size_t)j * D + (size_t)(hc % C::HP) * C::RP) * C::RB;
       dma_stage<C>(g, (2 * CK <= D) ? g + CK * C::RB : g, m0, ws, loff);
     }
+    return entry;
   };
-  if (ntot > 0) issue(0);
+  // the list entry of the next chunk to compute: read once, when its copy is
+  // issued, and carried to its step in a scalar register
+  int entry = ntot > 0 ? issue(0) : 0;
   // keys of exact chunk u inside the sequence (fewer only in a ragged last block)
   auto keys_of = [&](int u) {
     return VL ? min(max(block_count(Lv, (int)s_list[u / SPB] & kIdMask, BLK) - (u % SPB) * CK, 0), CK) : CK;
@@ -947,9 +954,10 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   // stream chunk t sits in stage t & 1, passed as `stage`; it is exact chunk
   // u = t + ex0 of the item
   auto exact_step = [&](int t, char* stage) {
+    const int cur = entry;
     wait_vm0();
     __syncthreads();
-    if (t + 1 < ntot) issue(t + 1);
+    if (t + 1 < ntot) entry = issue(t + 1);
     const int u = t + ex0;
     const int kv = keys_of(u);
     if (VL && kv < CK) {
@@ -960,8 +968,7 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
       __syncthreads();
     }
     // pairs: only the waves of a query block that routes this block compute it
-    const bool mine =
-        QB == 1 || (alive && ((__builtin_amdgcn_readfirstlane((int)s_list[u / SPB]) >> (12 + qb)) & 1));
+    const bool mine = QB == 1 || (alive && ((cur >> (12 + qb)) & 1));
     if (mine) chunk<C, false>(st, qf, stage, off, c2, hh, bits[qb], 0, kv);
   };
   // stage 1, two exact chunks per trip (t even), so each stage's offset is a
