@@ -918,12 +918,12 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   // copy chunk t into stage t & 1
   // copy chunk t into stage t & 1; returns an exact chunk's list entry (block id
   // and pair membership bits, wave-uniform), 0 otherwise
-  auto issue = [&](int t) {
+  auto issue = [&](int t, int raw = -1) {
     const unsigned m0 = lds_m0 + (unsigned)((t & 1) * C::STB);
     int entry = 0;
     if (t < nex) {
       const int u = t + ex0;                              // exact chunk u of the item
-      entry = __builtin_amdgcn_readfirstlane((int)s_list[u / SPB]);
+      entry = __builtin_amdgcn_readfirstlane(raw >= 0 ? raw : (int)s_list[u / SPB]);
       const int j = entry & kIdMask;
       const size_t off = ((size_t)j * BLK + (size_t)(u % SPB) * CK) * C::RB;
       dma_stage<C>(Kb + off, Vb + off, m0, ws, loff);
@@ -946,6 +946,9 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
   // the list entry of the next chunk to compute: read once, when its copy is
   // issued, and carried to its step in a scalar register
   int entry = ntot > 0 ? issue(0) : 0;
+  // the list entry of exact chunk 1, read ahead: step t reads chunk t + 2's entry
+  // after its barrier, for the copy that step t + 1 issues
+  int raw_next = (nex > 1) ? (int)(unsigned short)s_list[(1 + ex0) / SPB] : 0;
   // keys of exact chunk u inside the sequence (fewer only in a ragged last block)
   auto keys_of = [&](int u) {
     return VL ? min(max(block_count(Lv, (int)s_list[u / SPB] & kIdMask, BLK) - (u % SPB) * CK, 0), CK) : CK;
@@ -957,7 +960,8 @@ __global__ __launch_bounds__(C::NT, C::MINB) void attn_bf16_kernel(AttnPtrs p, i
     const int cur = entry;
     wait_vm0();
     __syncthreads();
-    if (t + 1 < ntot) entry = issue(t + 1);
+    if (t + 1 < ntot) entry = issue(t + 1, t + 1 < nex ? raw_next : -1);
+    if (t + 2 < nex) raw_next = (int)(unsigned short)s_list[(t + 2 + ex0) / SPB];
     const int u = t + ex0;
     const int kv = keys_of(u);
     if (VL && kv < CK) {
